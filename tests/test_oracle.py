@@ -1,0 +1,261 @@
+"""The CPU oracle against its pins (no GPU)."""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import workloads as W
+from oracle import attention as A
+from oracle.block_manager import BlockManagerModel, InvalidOp, OutOfBlocks
+from oracle.cache import PagedCacheModel
+
+import oracle_pins as P
+
+
+@pytest.mark.parametrize("check", P.ATTN_CHECKS, ids=lambda f: f.__name__)
+def test_attention_pins(check):
+    check(A.decode_attention)
+
+
+@pytest.mark.parametrize("check", P.ATTN_CHECKS, ids=lambda f: f.__name__)
+def test_split_attention_pins(check):
+    """The split-K form passes the same pins for several partition sizes."""
+    for part in (1, 3, 16, 512):
+        check(lambda q, K, V, s: A.decode_attention_split(q, K, V, s, part))
+
+
+def test_split_merge():
+    P.check_split_merge(A.split_k, A.lse_merge, A.decode_attention)
+
+
+def test_block_manager_golden():
+    P.check_bm_golden(BlockManagerModel, OutOfBlocks)
+
+
+def test_layout_golden():
+    P.check_layout_golden(PagedCacheModel)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_paged_equals_contiguous(dtype):
+    P.check_paged_equals_contiguous(PagedCacheModel, dtype)
+
+
+def test_copy_blocks():
+    P.check_copy_blocks(PagedCacheModel)
+
+
+# ------------------------------------------------------ block manager model
+def test_bm_errors_change_nothing():
+    bm = BlockManagerModel(4, 4)
+    bm.add_seq(1, 9)                       # 3 blocks
+    snap = (list(bm.free), list(bm.rc), {k: list(v) for k, v in bm.tables.items()}, dict(bm.lens))
+    with pytest.raises(OutOfBlocks):
+        bm.add_seq(2, 5)
+    with pytest.raises(InvalidOp):
+        bm.add_seq(1, 1)
+    with pytest.raises(InvalidOp):
+        bm.free_seq(7)
+    with pytest.raises(InvalidOp):
+        bm.fork(7, 8)
+    with pytest.raises(InvalidOp):
+        bm.append([1, 1])
+    bm.add_seq(3, 4)                       # last free block
+    bm.fork(3, 4)
+    snap = (list(bm.free), list(bm.rc), {k: list(v) for k, v in bm.tables.items()}, dict(bm.lens))
+    with pytest.raises(OutOfBlocks):       # seq 1 needs no block, seq 3 needs one
+        bm.append([1, 3])
+    assert snap == (list(bm.free), list(bm.rc), {k: list(v) for k, v in bm.tables.items()}, dict(bm.lens))
+
+
+def test_bm_interchangeable_blocks_after_churn():
+    """Every free block is interchangeable: after any churn an allocation of
+    k blocks succeeds exactly when k <= num_free."""
+    rng = np.random.default_rng(3)
+    bm = BlockManagerModel(64, 16, rng.permutation(64))
+    live = []
+    for i in range(2000):
+        if rng.random() < 0.55 and bm.num_free():
+            n = int(rng.integers(1, 16 * bm.num_free() + 1))
+            bm.add_seq(i, n)
+            live.append(i)
+        elif live:
+            bm.free_seq(live.pop(int(rng.integers(len(live)))))
+        P.bm_invariants(bm)
+    free = bm.num_free()
+    with pytest.raises(OutOfBlocks):
+        bm.add_seq(10**6, 16 * free + 1)
+    bm.add_seq(10**6, 16 * free)
+    assert bm.num_free() == 0
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.tuples(st.integers(0, 4), st.integers(0, 7), st.integers(0, 40)), max_size=60),
+       st.sampled_from([1, 4, 8]))
+def test_bm_random_ops_keep_invariants(ops, bs):
+    bm = BlockManagerModel(24, bs, list(reversed(range(24))))
+    for kind, seq, n in ops:
+        try:
+            if kind == 0:
+                bm.add_seq(seq, n % 20)
+            elif kind == 1:
+                bm.append([s for s in sorted(bm.tables) if (s + n) % 3 == 0])
+            elif kind == 2:
+                bm.fork(seq, (seq + n) % 8)
+            elif kind == 3:
+                bm.free_seq(seq)
+            else:
+                bm.append([seq])
+        except (OutOfBlocks, InvalidOp):
+            pass
+        P.bm_invariants(bm)
+
+
+# ----------------------------------------------------- scenario-level pins
+def _tiny(**kw):
+    return W.tiny(**kw)
+
+
+def test_scenario_paged_equals_contiguous_attention():
+    """Outputs over the pool equal attention over the workload's own
+    contiguous rows (the gather is exact)."""
+    w = _tiny(num_seqs=4, ctx=[1, 16, 17, 70], block_size=16, dtype="bf16", seed=1)
+    r = oracle.run_scenario(w)
+    d = r.decodes[-1]
+    for j, s in enumerate(d.seqs):
+        rows = w.row_of(s, np.arange(int(w.ctx[s])))
+        ref = A.decode_attention(w.q_sets[0][s], w.k_rows[rows], w.v_rows[rows], w.cfg.scale)
+        assert np.array_equal(d.out[j], ref)
+
+
+def test_scenario_permutation_invariance():
+    """Blocks may sit anywhere in any order: permuting physical blocks leaves
+    the outputs bit-identical and changes the tables."""
+    a = oracle.run_scenario(_tiny(ctx=[5, 40, 33], seed=2, permute=False))
+    b = oracle.run_scenario(_tiny(ctx=[5, 40, 33], seed=2, permute=True))
+    assert not np.array_equal(a.decodes[-1].tables, b.decodes[-1].tables)
+    assert np.array_equal(a.decodes[-1].out, b.decodes[-1].out)
+
+
+def _fork_workload(prefix, suffix, share: bool):
+    """Sequences with a common prefix, either forked (shared blocks) or added
+    as independent copies."""
+    base = _tiny(num_seqs=len(suffix), ctx=[prefix + s for s in suffix], block_size=8,
+                 num_kv_heads=2, num_q_heads=4, head_dim=64, seed=5)
+    B = len(suffix)
+    # every sequence reads the prefix rows of sequence 0
+    row_start = base.row_start.copy()
+    k, v = base.k_rows, base.v_rows
+    w = W.Workload(base.cfg, base.ctx, k, v, base.q_sets, [], 4 * int(base.num_blocks) + 64,
+                   row_start, 0)
+    pref_rows = np.arange(prefix)
+
+    def row_of(seq, positions):
+        positions = np.asarray(positions)
+        return np.where(positions < prefix, pref_rows[np.minimum(positions, prefix - 1)],
+                        row_start[seq] + positions)
+    w.row_of = row_of
+    ops = [("create", w.num_blocks, None)]
+    if share:
+        ops.append(("add_seq", 0, prefix, True))
+        ops += [("fork", 0, i) for i in range(1, B)]
+    else:
+        ops += [("add_seq", i, prefix, True) for i in range(B)]
+    done = [0] * B
+    while any(done[i] < suffix[i] for i in range(B)):
+        step = [i for i in range(B) if done[i] < suffix[i]]
+        ops.append(("append", step))
+        for i in step:
+            done[i] += 1
+    ops.append(("decode", list(range(B)), 0))
+    w.ops = ops
+    return w
+
+
+def test_scenario_shared_equals_unshared():
+    """Tables pointing at one physical prefix copy give the same outputs as
+    private copies, bit for bit; the shared run uses fewer blocks."""
+    for prefix in (16, 13):             # block-aligned prefix, and a partial shared block
+        suffix = [1, 3, 9, 20]
+        a = oracle.run_scenario(_fork_workload(prefix, suffix, share=True))
+        b = oracle.run_scenario(_fork_workload(prefix, suffix, share=False))
+        assert np.array_equal(a.decodes[-1].out, b.decodes[-1].out)
+        assert a.bm.num_free() > b.bm.num_free()
+        cows = sum(len(x["pairs"]) for x in a.appends)
+        assert cows == (len(suffix) - 1 if prefix % 8 else 0)
+
+
+def test_scenario_cow_isolation():
+    """Copy-on-write gives the writer its own copy: the block the others still
+    share is bit-identical before and after, and so are their outputs."""
+    w = _fork_workload(13, [0, 0, 0], share=True)
+    w.ops = w.ops[:4] + [("decode", [0, 1, 2], 0)]          # create, add, 2 forks, decode
+    r0 = oracle.run_scenario(w)
+    shared_last = r0.bm.table(0)[-1]
+    k_before = r0.cache.k[shared_last].copy()
+    v_before = r0.cache.v[shared_last].copy()
+    w.ops = w.ops[:4] + [("append", [1]), ("decode", [0, 2], 0)]
+    r1 = oracle.run_scenario(w)
+    assert r1.appends[0]["pairs"] == [(shared_last, r1.bm.table(1)[-1])]
+    assert np.array_equal(r1.cache.k[shared_last], k_before)
+    assert np.array_equal(r1.cache.v[shared_last], v_before)
+    assert np.array_equal(r1.decodes[-1].out, r0.decodes[-1].out[[0, 2]])
+    assert r1.bm.refcount(shared_last) == 2
+
+
+# ------------------------------------------------------ workload scripts
+def test_c1_construction():
+    w = W.build("c1_tiny_f32")
+    r = oracle.run_scenario(w)
+    assert r.bm.N - r.bm.num_free() == 29
+    d = r.decodes[-1]
+    assert d.ctx.tolist() == [17, 64, 100, 255]
+    order = w.ops[0][2]
+    # prefill takes order[0..27] by sequence then block; the decode step's
+    # block for sequence 0 (position 16 starts a block) is order[28]
+    assert d.tables[0, :2].tolist() == [order[0], order[28]]
+    assert d.tables[3, :16].tolist() == list(order[12:28])
+
+
+@pytest.mark.parametrize("name", ["c2_gqa_bf16_bs8", "c2_gqa_bf16", "c2_gqa_bf16_bs32", "c5_long_splitk"])
+def test_uniform_constructions(name):
+    w = W.build(name, values=False)
+    r = oracle.run_scenario(w, outputs=False, cache=False)
+    bs = w.cfg.block_size
+    need = int(np.sum(-(-w.ctx // bs)))
+    assert r.bm.N == int(np.ceil(1.2 * need)) and r.bm.N - r.bm.num_free() == need
+    assert r.decodes[-1].ctx.tolist() == w.ctx.tolist()
+    P.bm_invariants(r.bm)
+
+
+def test_c3_churn_construction():
+    w = W.build("c3_mha_f16_churn", values=False)
+    assert w.ctx.min() >= 1 and w.ctx.max() <= 4096
+    assert 380 < w.ctx.mean() < 650          # lognormal mean 512 before clipping
+    r = oracle.run_scenario(w, outputs=False, cache=False)
+    P.bm_invariants(r.bm)
+    need = int(np.sum(-(-w.ctx // 16)))
+    assert r.bm.N - r.bm.num_free() == need
+    # the churn scattered the batch: tables are far from the identity layout
+    t = r.decodes[-1].tables
+    first = t[:, 0]
+    assert np.mean(np.diff(first) == 1) < 0.5
+
+
+@pytest.mark.parametrize("name", ["c4a_prefix_share", "c4b_prefix_cow"])
+def test_c4_construction(name):
+    w = W.build(name, values=False)
+    r = oracle.run_scenario(w, outputs=False, cache=False)
+    P.bm_invariants(r.bm)
+    pairs = [p for a in r.appends for p in a["pairs"]]
+    tabs = r.decodes[-1].tables
+    if name == "c4a_prefix_share":
+        assert pairs == []
+        assert all(r.bm.refcount(int(b)) == 64 for b in tabs[0, :128])
+    else:
+        first = r.appends[0]
+        assert len(first["pairs"]) == 63 and len(pairs) == 63
+        src = {p[0] for p in first["pairs"]}
+        assert len(src) == 1 and tabs[63, 127] == next(iter(src))       # last sharer in place
+        assert all(r.bm.refcount(int(b)) == 64 for b in tabs[0, :127])
+    assert r.decodes[-1].ctx.tolist() == w.ctx.tolist()

@@ -1,0 +1,128 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each mutant is the oracle module's own source with one plausible slip
+(a dropped term, a wrong sign or index, a transposed operand, a different
+free-list order ...), loaded as a separate module on the CPU.  The pins of
+tests/oracle_pins.py run against it and at least one must fail; this shows
+the pins would catch that kind of mistake in the real oracle.
+"""
+import importlib.util
+import os
+import types
+
+import pytest
+
+import oracle_pins as P
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+
+def _mutant(module: str, old: str, new: str, count: int = 1) -> types.ModuleType:
+    with open(os.path.join(ORACLE_DIR, module + ".py")) as f:
+        src = f.read()
+    assert src.count(old) >= count, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new)
+    mod = types.ModuleType(f"oracle_mutant_{module}")
+    exec(compile(src, f"<mutant {module}>", "exec"), mod.__dict__)
+    return mod
+
+
+def _fails(checks) -> bool:
+    for c in checks:
+        try:
+            c()
+        except Exception:
+            return True
+    return False
+
+
+ATTN_MUTANTS = [
+    ("scale squared", "s[r] = (K[:, h, :] @ q[r]) * scale", "s[r] = (K[:, h, :] @ q[r]) * scale * scale"),
+    ("no scale", "s[r] = (K[:, h, :] @ q[r]) * scale", "s[r] = (K[:, h, :] @ q[r])"),
+    ("negated score", "s[r] = (K[:, h, :] @ q[r]) * scale", "s[r] = -(K[:, h, :] @ q[r]) * scale"),
+    ("interleaved head map in scores", "        h = r // g\n", "        h = r % Hkv\n"),
+    ("interleaved head map in values", "out[r] = (p @ V[:, r // g, :]) / p.sum()", "out[r] = (p @ V[:, r % Hkv, :]) / p.sum()"),
+    ("no max subtraction", "p = np.exp(s[r] - s[r].max())", "p = np.exp(s[r])"),
+    ("no normalisation", "out[r] = (p @ V[:, r // g, :]) / p.sum()", "out[r] = (p @ V[:, r // g, :])"),
+    ("drops last token", "    s = _scores(q, K, scale)\n    for r in range(Hq):\n        p = np.exp(s[r] - s[r].max())\n        out[r] = (p @ V[:, r // g, :]) / p.sum()",
+     "    s = _scores(q, K, scale)[:, : max(1, n - 1)]\n    for r in range(Hq):\n        p = np.exp(s[r] - s[r].max())\n        out[r] = (p @ V[: max(1, n - 1), r // g, :]) / p.sum()"),
+    ("uses K as V", "out[r] = (p @ V[:, r // g, :]) / p.sum()", "out[r] = (p @ K[:, r // g, :]) / p.sum()"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", ATTN_MUTANTS, ids=[m[0] for m in ATTN_MUTANTS])
+def test_attention_mutant_is_caught(name, old, new):
+    m = _mutant("attention", old, new)
+    assert _fails([lambda c=c: c(m.decode_attention) for c in P.ATTN_CHECKS]), name
+
+
+SPLIT_MUTANTS = [
+    ("merge forgets rescale of l", "L = (np.asarray(l) * w).sum(axis=0)", "L = np.asarray(l).sum(axis=0)"),
+    ("merge rescale sign", "w = np.exp(m - M[None, :])", "w = np.exp(M[None, :] - m)"),
+    ("partition drops a token", "lo, hi = p * part, min(n, (p + 1) * part)", "lo, hi = p * part, min(n, (p + 1) * part - 1)"),
+    ("partition max not subtracted", "e = np.exp(sp - m[p, r])", "e = np.exp(sp)"),
+    ("partial acc uses K", "acc[p, r] = e @ V[lo:hi, r // g, :]", "acc[p, r] = e @ K[lo:hi, r // g, :]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", SPLIT_MUTANTS, ids=[m[0] for m in SPLIT_MUTANTS])
+def test_split_mutant_is_caught(name, old, new):
+    m = _mutant("attention", old, new)
+    checks = [lambda: P.check_split_merge(m.split_k, m.lse_merge, m.decode_attention)]
+    checks += [lambda c=c: c(lambda q, K, V, s: m.decode_attention_split(q, K, V, s, 16))
+               for c in P.ATTN_CHECKS]
+    assert _fails(checks), name
+
+
+BM_MUTANTS = [
+    ("FIFO free list", "self.free: List[int] = list(reversed(order))", "self.free: List[int] = list(order)"),
+    ("copy even when unshared", "elif self.rc[t[-1]] > 1:", "elif self.rc[t[-1]] > 0:"),
+    ("never copy-on-write", "elif self.rc[t[-1]] > 1:", "elif False:"),
+    ("free in reverse order", "for b in self.tables.pop(seq):", "for b in reversed(self.tables.pop(seq)):"),
+    ("slot off by one", "return t[pos // self.BS] * self.BS + pos % self.BS", "return t[pos // self.BS] * self.BS + (pos + 1) % self.BS"),
+    ("block on full, not on first write", "            if pos % self.BS == 0:\n                t.append", "            if pos % self.BS == 1:\n                t.append"),
+    ("fork forgets refcount", "        for b in self.tables[child]:\n            self.rc[b] += 1", "        pass"),
+    ("no all-or-nothing", "        if need > len(self.free):\n            raise OutOfBlocks()\n        self.tables[seq]", "        self.tables[seq]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", BM_MUTANTS, ids=[m[0] for m in BM_MUTANTS])
+def test_block_manager_mutant_is_caught(name, old, new):
+    m = _mutant("block_manager", old, new)
+    assert _fails([lambda: P.check_bm_golden(m.BlockManagerModel, m.OutOfBlocks)]), name
+
+
+CACHE_MUTANTS = [
+    ("V stored token-major", "self.v[blk, :, :, off] = vb", "self.v.reshape(self.N, self.H, self.BS, self.D)[blk, :, off, :] = vb"),
+    ("K chunk transposed", "kx = kb.reshape(T, self.H, self.D // self.X, self.X)",
+     "kx = kb.reshape(T, self.H, self.X, self.D // self.X).transpose(0, 1, 3, 2)"),
+    ("copy skips V", "            self.v[dst] = self.v[src]\n", "            pass\n"),
+    ("negative slot not skipped", "keep = slots >= 0", "keep = slots >= -(1 << 60)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", CACHE_MUTANTS, ids=[m[0] for m in CACHE_MUTANTS])
+def test_cache_mutant_is_caught(name, old, new):
+    m = _mutant("cache", old, new)
+    checks = [lambda: P.check_layout_golden(m.PagedCacheModel),
+              lambda: P.check_copy_blocks(m.PagedCacheModel)]
+    checks += [lambda d=d: P.check_paged_equals_contiguous(m.PagedCacheModel, d) for d in ("bf16", "f32")]
+    assert _fails(checks), name
+
+
+@pytest.mark.parametrize("module", ["attention", "block_manager", "cache"])
+def test_unmutated_copy_passes_every_pin(module):
+    """The harness itself: the oracle's source loaded the same way, with no
+    mistake planted, passes every pin (so a caught mutant is the mistake)."""
+    m = _mutant(module, "import numpy as np", "import numpy as np")
+    if module == "attention":
+        for c in P.ATTN_CHECKS:
+            c(m.decode_attention)
+        P.check_split_merge(m.split_k, m.lse_merge, m.decode_attention)
+    elif module == "block_manager":
+        P.check_bm_golden(m.BlockManagerModel, m.OutOfBlocks)
+    else:
+        P.check_layout_golden(m.PagedCacheModel)
+        P.check_copy_blocks(m.PagedCacheModel)
+        for d in ("bf16", "f16", "f32"):
+            P.check_paged_equals_contiguous(m.PagedCacheModel, d)
