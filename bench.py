@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Paged-attention decode benchmark on one MI355X.
+
+A step is one decode step of one attention layer for the whole batch: the
+host block manager hands every sequence a slot for its new token (taking a
+block when the last one is full, copying a shared last block first), the
+bookkeeping goes to the device, then pa_copy_blocks, pa_write_kv and
+pa_decode (partition pass + log-sum-exp merge) run.  Inputs are the batch-64
+GQA bf16 configuration (64 sequences, 32 query / 8 KV heads, head_dim 128,
+block 16, contexts uniform in [128, 4096], pool 1.2x the blocks needed in a
+seeded random order), prefilled through the same kernels before timing.
+
+Prints one JSON line: whole-step KV read throughput (GB/s of K/V bytes the
+attention reads per step / step time), tokens/s, the decode kernel's
+roofline against MI355X HBM (8 TB/s), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode KV read GB/s (% of HBM peak) + tokens/s, batch 64 GQA bf16"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2_gqa_bf16")
+    ap.add_argument("--partition", type=int, default=None, help="tokens per split-K partition (0 = library)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kv_bytes(ctx: np.ndarray, hkv: int, d: int, esize: int) -> int:
+    """Algorithmic K+V bytes one decode reads: every context token's key and
+    value row of every kv head, once."""
+    return int(ctx.astype(np.int64).sum()) * hkv * d * 2 * esize
+
+
+def decode_bytes(ctx, cfg, esize, out_esize=4) -> int:
+    """Algorithmic bytes of one pa_decode call: K/V rows, the queries, the
+    outputs, the table entries and context lengths it reads."""
+    b = cfg.num_seqs
+    tables = int((-(-ctx.astype(np.int64) // cfg.block_size)).sum()) * 4
+    return (kv_bytes(ctx, cfg.num_kv_heads, cfg.head_dim, esize) + b * cfg.num_q_heads * cfg.head_dim * esize
+            + b * cfg.num_q_heads * cfg.head_dim * out_esize + tables + 4 * b)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it stands, on the host cores: replay of the script
+    (untimed), then gather + float64 attention of whole sequences of the
+    final decode step until about budget_s seconds have been spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    ref = oracle.run_scenario(w, outputs=False)
+    d = ref.decodes[-1]
+    cfg = w.cfg
+    q = w.q_sets[d.q_index]
+    done_bytes, seqs = 0, 0
+    t0 = time.perf_counter()
+    j = 0
+    while time.perf_counter() - t0 < budget_s:
+        i = j % len(d.seqs)
+        K, V = ref.cache.gather(d.tables[i], int(d.ctx[i]))
+        oracle.decode_attention(q[d.seqs[i]], K, V, cfg.scale)
+        done_bytes += kv_bytes(np.array([d.ctx[i]]), cfg.num_kv_heads, cfg.head_dim,
+                               W_ELEM[cfg.dtype])
+        seqs += 1
+        j += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{seqs} sequences of the final decode step ({done_bytes / 1e6:.0f} MB of K/V) "
+                      f"gathered through the table and attended in float64 in {el:.1f} s; "
+                      f"host has {os.cpu_count()} cpus, affinity {len(os.sched_getaffinity(0))}",
+            "tokens_per_s": round(seqs / el, 3)}
+
+
+W_ELEM = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout is a design "
+              "note, not a measured path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    from paged_kv_cache_332_amd.engine import PagedKVEngine
+
+    torch.cuda.init()
+    cfg = W.config(args.config)
+    part = cfg.partition_size if args.partition is None else args.partition
+    kernel = {"auto": pa.PA_KERNEL_AUTO, "valu": pa.PA_KERNEL_VALU, "mfma": pa.PA_KERNEL_MFMA}[args.kernel]
+    w = W.build(args.config)
+    dtype = runner.TORCH_DTYPE[cfg.dtype]
+    esize = W_ELEM[cfg.dtype]
+    print(f"[bench] {args.config}: {cfg.description}; replaying construction script", file=sys.stderr,
+          flush=True)
+
+    # replay the construction (prefill + first decode step) on an engine sized
+    # for the extra tokens the timed steps append
+    total_steps = args.warmup + args.steps
+    seqs = list(range(cfg.num_seqs))
+    dev = runner.run_script(w, partition_size=part, kernel=kernel, extra_context=total_steps)
+    eng: PagedKVEngine = dev.engine
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    k_new = torch.randn((cfg.num_seqs, cfg.num_kv_heads, cfg.head_dim), generator=g, device="cuda").to(dtype)
+    v_new = torch.randn((cfg.num_seqs, cfg.num_kv_heads, cfg.head_dim), generator=g, device="cuda").to(dtype)
+    q = dev.q_dev[-1][torch.tensor(seqs, device="cuda")].contiguous()
+    out = torch.empty((cfg.num_seqs, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    ctx0 = np.array([eng.bm.seq_len(s) for s in seqs], dtype=np.int64)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def one_step(i, timed):
+        eng.append(seqs, k_new, v_new, stream=stream)
+        if timed:
+            ev[i][0].record(stream)
+        eng.decode(seqs, q, out=out, partition_size=part, kernel=kernel, stream=stream)
+        if timed:
+            ev[i][1].record(stream)
+
+    for i in range(args.warmup):
+        one_step(i, False)
+    torch.cuda.synchronize()
+    ctx_start = ctx0 + args.warmup
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # each timed step appends one token per sequence before attending
+    step_ctx = [ctx_start + 1 + i for i in range(args.steps)]
+    kv_total = sum(kv_bytes(c, cfg.num_kv_heads, cfg.head_dim, esize) for c in step_ctx)
+    dec_bytes = [decode_bytes(c, cfg, esize) for c in step_ctx]
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    achieved = float(np.mean(dec_bytes) / (dec_ms.mean() * 1e-3) / 1e9)
+    value = kv_total / elapsed / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.config, "batch": cfg.num_seqs, "q_heads": cfg.num_q_heads,
+                   "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim, "block_size": cfg.block_size,
+                   "ctx_mean": round(float(np.mean(step_ctx[0])), 1), "partition": part or
+                   pa.pa_decode_default_partition(cfg.num_seqs, cfg.num_kv_heads, int(step_ctx[-1].max()),
+                                                  cfg.block_size),
+                   "kernel": args.kernel, "parallelism": "single GPU"},
+        "tokens_per_s": round(cfg.num_seqs * args.steps / elapsed, 1),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (partition pass + merge)", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(float(dec_ms.mean()) * 1e3, 2),
+                     "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                     "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
+                     "bytes_per_launch": int(np.mean(dec_bytes))},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,228 @@
+/*
+ * pa.h — paged-attention decode on AMD MI355X (gfx950): C ABI of libpa.so.
+ *
+ * The library keeps a transformer's key/value cache in fixed-size blocks of
+ * BS tokens that may sit anywhere in device memory, describes each sequence
+ * by a block table (an ordered list of physical block ids) and runs
+ * single-query decode attention that follows the table.  The idea and its
+ * parts are those of the pages:
+ *   [VM]  "Paged Attention: Virtual Memory for the KV Cache" (projectcozy.me)
+ *   [MM]  "Paged Attention as a Memory Manager" (diomgis.com)
+ *   [GL]  AI/ML term glossary, "Paged attention" (interviewkickstart.com)
+ *
+ * Conventions for every call
+ *   - Device pointers are caller-owned device memory (e.g. torch tensors),
+ *     contiguous, in the layouts stated below.  The library never allocates,
+ *     frees or synchronises device memory; work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and returns immediately.
+ *   - Host pointers are read or written before the call returns.
+ *   - Every call returns a pa_status.  No C++ exception crosses the ABI.  On a
+ *     non-OK status pa_last_error() returns a thread-local message.  Host
+ *     arguments (sizes, dtypes, supported shapes) are validated before any
+ *     launch; a failed launch maps to PA_ERR_HIP.
+ *   - Device *contents* (table entries, slots, context lengths, copy pairs)
+ *     are trusted like memcpy arguments: out-of-range ids or duplicate slots
+ *     are undefined behaviour.  pa_check_tables() validates host copies.
+ *   - Kernels are reentrant.  A block manager (pa_bm) is not thread-safe.
+ *
+ * Cache layout (one pool for K, one for V, per attention layer).  Both are
+ * head-major inside a block, so the tile of one (block, kv head) is one
+ * contiguous run of BS*D elements that a gather reads in full:
+ *   K pool  [num_blocks][num_kv_heads][D / X][BS][X]   X = 16 / element bytes
+ *           (8 for f16/bf16, 4 for f32): 16-byte chunks of a key, token-minor
+ *   V pool  [num_blocks][num_kv_heads][D][BS]           tokens innermost
+ * A slot s addresses token offset s % BS of block s / BS.
+ *
+ * Supported shapes: head_dim D in {64, 128}; block_size BS in {8, 16, 32};
+ * num_q_heads % num_kv_heads == 0 with group g = num_q_heads / num_kv_heads
+ * in {1, 2, 4, 8, 16}; num_blocks * BS < 2^31; element types below.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,      /* bad argument or unknown / duplicate sequence */
+  PA_ERR_OOM = 2,          /* not enough free blocks; nothing was changed */
+  PA_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
+  PA_ERR_UNSUPPORTED = 4   /* valid but unsupported shape or dtype */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Decode kernel selection (pa_decode_variant).  AUTO picks the matrix-core
+ * kernel for 16-bit caches with g >= 2 and the vector kernel otherwise. */
+typedef enum { PA_KERNEL_AUTO = 0, PA_KERNEL_VALU = 1, PA_KERNEL_MFMA = 2 } pa_kernel;
+
+const char* pa_last_error(void);
+const char* pa_version(void);
+
+/* ------------------------------------------------------------------------
+ * pa_write_kv — write the keys and values of num_tokens tokens into their
+ * slots.  A request fills the block it holds before it asks for another
+ * ([VM] §The fix borrowed from operating systems); the slots come from the
+ * block manager.
+ *   k_cache, v_cache   device pools in the layout above (written)
+ *   k_new, v_new       device [num_tokens][num_kv_heads][head_dim], dtype
+ *   slot_mapping       device int32 [num_tokens]; slot < 0 skips the token
+ *                      (lets callers pad a batch).  Slots of one call must be
+ *                      distinct and < num_blocks * block_size.
+ * Errors: PA_ERR_INVALID for negative sizes or a non-16-byte-multiple row;
+ * PA_ERR_UNSUPPORTED for shapes outside the supported set.  num_tokens = 0 is
+ * a no-op.
+ * ---------------------------------------------------------------------- */
+pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                      const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_copy_blocks — whole-block copies for copy-on-write: a sequence about to
+ * write into a block it shares gets its own copy first ([VM] §Sharing comes
+ * almost for free; [MM] §Virtual Memory as the Blueprint).  For each pair
+ * (src, dst) the K and V tiles of every kv head of block dst become a byte
+ * copy of block src (all BS slots, written or not).
+ *   pairs   device int32 [num_pairs][2] = (src, dst); destinations distinct
+ *           and never a source of the same call.
+ * Errors as pa_write_kv.  num_pairs = 0 is a no-op.  Issue it before the
+ * pa_write_kv of the same step on the same stream.
+ * ---------------------------------------------------------------------- */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, pa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_decode — one query token per sequence attends over its whole context
+ * through its block table: the kernel follows the table instead of assuming
+ * the sequence is laid out end to end ([VM] §The fix borrowed from operating
+ * systems; [GL] "What is Paged Attention?"), so the result is plain softmax
+ * attention over the logical sequence:
+ *     out[i][r] = sum_t softmax_t(scale * q[i][r] . K_i[t][r / g]) V_i[t][r / g]
+ * for t < context_lens[i]; query heads [h*g, (h+1)*g) share kv head h
+ * (grouped-query attention, [VM] §What it does not fix).  A zero context
+ * gives a zero row.  Softmax runs with a running maximum in fp32, products
+ * accumulate in fp32.
+ *   out            device [num_seqs][num_q_heads][head_dim], out_dtype = PA_F32
+ *                  or kv_dtype (then rounded to nearest even from fp32)
+ *   q              device [num_seqs][num_q_heads][head_dim], kv_dtype
+ *   block_tables   device int32 [num_seqs][table_stride]; entry j is the
+ *                  physical block of logical block j; entries past
+ *                  ceil(ctx/BS) are never read
+ *   context_lens   device int32 [num_seqs], 0 <= ctx <= max_context_len and
+ *                  ceil(ctx/BS) <= table_stride
+ *   max_context_len host-known upper bound of context_lens; it sizes the grid
+ *   partition_size  tokens per work item (split-K); a multiple of 64 and of
+ *                  4*BS, or 0 to let the library choose.  Sequences longer
+ *                  than one partition are reduced in two passes: per-
+ *                  partition partials (max, sum, unnormalised output) then a
+ *                  log-sum-exp merge.
+ *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
+ *                  bytes for the same num_seqs/num_q_heads/head_dim/
+ *                  max_context_len/partition_size (may be NULL when that is 0)
+ * Errors: PA_ERR_INVALID (bad sizes, workspace too small, out_dtype not F32
+ * or kv_dtype), PA_ERR_UNSUPPORTED (shape outside the supported set),
+ * PA_ERR_HIP (launch failure).
+ * ---------------------------------------------------------------------- */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/* The partition size pa_decode uses when passed 0 for these arguments. */
+int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t max_context_len, int32_t block_size);
+
+pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                    const void* v_cache, pa_dtype kv_dtype, const int32_t* block_tables,
+                    int32_t table_stride, const int32_t* context_lens, int32_t max_context_len,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_decode with an explicit kernel choice (for measurement): PA_KERNEL_VALU
+ * supports every shape above; PA_KERNEL_MFMA needs a 16-bit kv_dtype. */
+pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                            const void* v_cache, pa_dtype kv_dtype, const int32_t* block_tables,
+                            int32_t table_stride, const int32_t* context_lens,
+                            int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, float scale, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            pa_kernel kernel);
+
+/* ------------------------------------------------------------------------
+ * Host block manager: the shared pool of interchangeable blocks, per-block
+ * sharer counts and per-sequence block tables ([VM] §The fix borrowed from
+ * operating systems, §Sharing comes almost for free; [MM] §How the Kernel
+ * Executes Paged Attention; [GL] "What is Paged Attention?").
+ *
+ * Policy (the pages leave it open; it is fixed so results are unique):
+ *   - the free list is a LIFO stack; pa_bm_create stacks it so the first
+ *     allocation returns initial_order[0] (0,1,2,... when NULL);
+ *   - add_seq(n) takes ceil(n/BS) blocks in logical order;
+ *     slot(t) = table[t / BS] * BS + t % BS;
+ *   - an append at position pos takes a new block when pos % BS == 0;
+ *     otherwise, if the last block is shared (count > 1), it takes a new
+ *     block, lowers the old block's count, points the table at the new block
+ *     and reports the pair (old, new) for pa_copy_blocks; the last remaining
+ *     sharer writes in place.  A batch is applied in list order;
+ *   - fork copies the parent's table and raises each block's count;
+ *   - free_seq lowers counts in logical order and pushes each block whose
+ *     count reaches zero at once.
+ * Every call is all-or-nothing: PA_ERR_OOM and PA_ERR_INVALID leave the
+ * manager unchanged.  Sequence ids are arbitrary int64 keys.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_bm pa_bm;
+
+/* NULL on invalid arguments (see pa_last_error): num_blocks < 0, block_size
+ * <= 0, or initial_order not a permutation of 0..num_blocks-1. */
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_order);
+void pa_bm_destroy(pa_bm* bm);
+
+/* New sequence holding num_tokens tokens; slots_out (host, [num_tokens], may
+ * be NULL) receives their slots.  INVALID if seq exists or num_tokens < 0. */
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t num_tokens, int32_t* slots_out);
+
+/* One new token for each of seqs[0..n): slots_out[n] receives its slot,
+ * cow_pairs_out[n][2] the (src, dst) block copies to run first (host
+ * buffers), *num_cow_out their count.  INVALID for unknown or repeated ids. */
+pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* slots_out,
+                             int32_t* cow_pairs_out, int32_t* num_cow_out);
+
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq);
+
+/* tables_out host int32 [n][stride] padded with -1; ctx_lens_out host int32
+ * [n].  INVALID if a table is longer than stride or an id is unknown. */
+pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t stride,
+                       int32_t* tables_out, int32_t* ctx_lens_out);
+
+/* Free blocks: the headroom a server can admit against ([VM] §What it buys
+ * in practice). */
+int32_t pa_bm_num_free(const pa_bm* bm);
+int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);      /* -1 if out of range */
+int32_t pa_bm_seq_len(const pa_bm* bm, int64_t seq);         /* -1 if unknown */
+int32_t pa_bm_num_seqs(const pa_bm* bm);
+/* Free list, next allocation first; writes min(cap, num_free) ids, returns
+ * num_free. */
+int32_t pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap);
+/* out[5] = {free blocks, referenced blocks, shared blocks (count > 1),
+ *           copy-on-write pairs issued so far, slack tokens in last blocks} */
+pa_status pa_bm_stats(const pa_bm* bm, int64_t* out);
+
+/* Debug validator over HOST copies of the decode inputs: every table entry a
+ * sequence reads is in [0, num_blocks) and ceil(ctx/BS) <= stride.  Returns
+ * INVALID with the first offending (sequence, entry) in pa_last_error(). */
+pa_status pa_check_tables(const int32_t* tables, int32_t n, int32_t stride,
+                          const int32_t* ctx_lens, int32_t block_size, int32_t num_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

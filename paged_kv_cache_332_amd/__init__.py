@@ -1,0 +1,262 @@
+"""paged_kv_cache_332_amd — paged-attention decode on AMD MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libpa.so`` (declared in
+``include/pa.h``).  It only marshals arguments: every step of the decode path
+(block-table bookkeeping, KV append, copy-on-write copies, attention, split-K
+merge) runs in the library.  PyTorch supplies device memory and streams.
+
+The library must be built first (``python -m paged_kv_cache_332_amd.build``);
+importing this package without it raises ImportError — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "PAError", "lib", "LIB_PATH", "PA_F32", "PA_F16", "PA_BF16",
+    "PA_KERNEL_AUTO", "PA_KERNEL_VALU", "PA_KERNEL_MFMA",
+    "pa_write_kv", "pa_copy_blocks", "pa_decode", "pa_decode_variant",
+    "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
+    "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python -m paged_kv_cache_332_amd.build`")
+lib = ctypes.CDLL(LIB_PATH)
+
+PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_HIP, PA_ERR_UNSUPPORTED = range(5)
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
+_STATUS = {1: "invalid", 2: "out of blocks", 3: "hip", 4: "unsupported"}
+
+_i32, _i64, _vp, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+_pi32, _pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+
+
+def _sig(name, res, *args):
+    f = getattr(lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_sig("pa_last_error", ctypes.c_char_p)
+_sig("pa_version", ctypes.c_char_p)
+_sig("pa_write_kv", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
+_sig("pa_copy_blocks", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
+_sig("pa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32)
+_sig("pa_decode_default_partition", _i32, _i32, _i32, _i32, _i32)
+_DECODE_ARGS = [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                _i32, _f32, _i32, _vp, _sz, _vp]
+_sig("pa_decode", _i32, *_DECODE_ARGS)
+_sig("pa_decode_variant", _i32, *_DECODE_ARGS, _i32)
+_sig("pa_bm_create", _vp, _i32, _i32, _pi32)
+_sig("pa_bm_destroy", None, _vp)
+_sig("pa_bm_add_seq", _i32, _vp, _i64, _i32, _pi32)
+_sig("pa_bm_append_slots", _i32, _vp, _pi64, _i32, _pi32, _pi32, _pi32)
+_sig("pa_bm_fork", _i32, _vp, _i64, _i64)
+_sig("pa_bm_free_seq", _i32, _vp, _i64)
+_sig("pa_bm_export", _i32, _vp, _pi64, _i32, _i32, _pi32, _pi32)
+_sig("pa_bm_num_free", _i32, _vp)
+_sig("pa_bm_refcount", _i32, _vp, _i32)
+_sig("pa_bm_seq_len", _i32, _vp, _i64)
+_sig("pa_bm_num_seqs", _i32, _vp)
+_sig("pa_bm_free_list", _i32, _vp, _pi32, _i32)
+_sig("pa_bm_stats", _i32, _vp, _pi64)
+_sig("pa_check_tables", _i32, _pi32, _i32, _i32, _pi32, _i32, _i32)
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[{_STATUS.get(status, status)}] {msg}")
+        self.status = status
+
+
+class OutOfBlocks(PAError):
+    pass
+
+
+def _check(st: int):
+    if st != PA_OK:
+        msg = lib.pa_last_error().decode()
+        raise (OutOfBlocks if st == PA_ERR_OOM else PAError)(st, msg)
+
+
+def pa_version() -> str:
+    return lib.pa_version().decode()
+
+
+# ------------------------------------------------------------------ tensors
+def torch_dtype_code(dtype) -> int:
+    import torch
+    return {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}[dtype]
+
+
+def cache_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int, elem_bytes: int):
+    """Shapes of the K pool [N][Hkv][D/X][BS][X] and V pool [N][Hkv][D][BS]."""
+    x = 16 // elem_bytes
+    return ((num_blocks, num_kv_heads, head_dim // x, block_size, x),
+            (num_blocks, num_kv_heads, head_dim, block_size))
+
+
+def alloc_cache(num_blocks, num_kv_heads, head_dim, block_size, dtype, device="cuda", poison=True):
+    """Allocate a K and a V pool with torch; optionally fill with quiet NaN."""
+    import torch
+    ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, block_size, torch.empty((), dtype=dtype).element_size())
+    k = torch.empty(ks, dtype=dtype, device=device)
+    v = torch.empty(vs, dtype=dtype, device=device)
+    if poison:
+        k.fill_(float("nan"))
+        v.fill_(float("nan"))
+    return k, v
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _pool_dims(k_cache, v_cache):
+    n, hkv, dx, bs, x = k_cache.shape
+    d = dx * x
+    assert tuple(v_cache.shape) == (n, hkv, d, bs), "V pool shape does not match K pool"
+    assert k_cache.dtype == v_cache.dtype and k_cache.is_contiguous() and v_cache.is_contiguous()
+    return n, hkv, d, bs
+
+
+def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> None:
+    """k_new/v_new [T][Hkv][D], slot_mapping int32 [T] (device tensors)."""
+    n, hkv, d, bs = _pool_dims(k_cache, v_cache)
+    t = int(slot_mapping.numel())
+    assert k_new.is_contiguous() and v_new.is_contiguous() and slot_mapping.is_contiguous()
+    assert tuple(k_new.shape) == (t, hkv, d) and tuple(v_new.shape) == (t, hkv, d)
+    assert k_new.dtype == k_cache.dtype and str(slot_mapping.dtype) == "torch.int32"
+    _check(lib.pa_write_kv(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                           slot_mapping.data_ptr(), t, hkv, d, bs, n, torch_dtype_code(k_cache.dtype),
+                           _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """pairs int32 [P][2] = (src, dst) (device tensor)."""
+    n, hkv, d, bs = _pool_dims(k_cache, v_cache)
+    assert pairs.is_contiguous() and str(pairs.dtype) == "torch.int32"
+    _check(lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), pairs.data_ptr(), int(pairs.numel() // 2),
+                              hkv, d, bs, n, torch_dtype_code(k_cache.dtype), _stream(stream)))
+
+
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size=0) -> int:
+    return int(lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size))
+
+
+def pa_decode_default_partition(num_seqs, num_kv_heads, max_context_len, block_size) -> int:
+    return int(lib.pa_decode_default_partition(num_seqs, num_kv_heads, max_context_len, block_size))
+
+
+def pa_decode_variant(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                      scale: float, partition_size: int = 0, workspace=None, stream=None,
+                      kernel: int = PA_KERNEL_AUTO) -> None:
+    """q/out [B][Hq][D]; block_tables int32 [B][stride]; context_lens int32 [B]."""
+    n, hkv, d, bs = _pool_dims(k_cache, v_cache)
+    b, hq, dq = q.shape
+    assert dq == d and tuple(out.shape) == (b, hq, d) and q.is_contiguous() and out.is_contiguous()
+    assert block_tables.is_contiguous() and block_tables.dim() == 2 and block_tables.shape[0] == b
+    assert context_lens.is_contiguous() and context_lens.numel() == b
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(),
+                                                          workspace.numel() * workspace.element_size())
+    _check(lib.pa_decode_variant(out.data_ptr(), torch_dtype_code(out.dtype), q.data_ptr(), k_cache.data_ptr(),
+                                 v_cache.data_ptr(), torch_dtype_code(k_cache.dtype), block_tables.data_ptr(),
+                                 int(block_tables.shape[1]), context_lens.data_ptr(), int(max_context_len),
+                                 b, hq, hkv, d, bs, n, float(scale), int(partition_size), ws_ptr, ws_bytes,
+                                 _stream(stream), int(kernel)))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int, scale: float,
+              partition_size: int = 0, workspace=None, stream=None) -> None:
+    pa_decode_variant(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                      partition_size, workspace, stream, PA_KERNEL_AUTO)
+
+
+def pa_check_tables(tables: np.ndarray, ctx_lens: np.ndarray, block_size: int, num_blocks: int) -> None:
+    t = np.ascontiguousarray(tables, dtype=np.int32)
+    c = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    _check(lib.pa_check_tables(t.ctypes.data_as(_pi32), t.shape[0], t.shape[1], c.ctypes.data_as(_pi32),
+                               block_size, num_blocks))
+
+
+# ------------------------------------------------------------ block manager
+class BlockManager:
+    """Host block manager (pa_bm_*): free list, refcounts, tables, COW."""
+
+    def __init__(self, num_blocks: int, block_size: int, order: Optional[Sequence[int]] = None):
+        self.block_size = block_size
+        self.num_blocks = num_blocks
+        arr = None if order is None else np.ascontiguousarray(order, dtype=np.int32)
+        self._h = lib.pa_bm_create(num_blocks, block_size, None if arr is None else arr.ctypes.data_as(_pi32))
+        if not self._h:
+            raise PAError(PA_ERR_INVALID, lib.pa_last_error().decode())
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add_seq(self, seq: int, num_tokens: int) -> np.ndarray:
+        out = np.empty(max(num_tokens, 0), dtype=np.int32)
+        _check(lib.pa_bm_add_seq(self._h, int(seq), int(num_tokens), out.ctypes.data_as(_pi32)))
+        return out
+
+    def append_slots(self, seqs: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        slots = np.empty(len(s), dtype=np.int32)
+        pairs = np.empty((len(s), 2), dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(lib.pa_bm_append_slots(self._h, s.ctypes.data_as(_pi64), len(s), slots.ctypes.data_as(_pi32),
+                                      pairs.ctypes.data_as(_pi32), ctypes.byref(ncow)))
+        return slots, pairs[: ncow.value].copy()
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(lib.pa_bm_fork(self._h, int(parent), int(child)))
+
+    def free_seq(self, seq: int) -> None:
+        _check(lib.pa_bm_free_seq(self._h, int(seq)))
+
+    def export(self, seqs: Sequence[int], stride: int, tables_out=None, ctx_out=None):
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        tab = tables_out if tables_out is not None else np.empty((len(s), stride), dtype=np.int32)
+        ctx = ctx_out if ctx_out is not None else np.empty(len(s), dtype=np.int32)
+        _check(lib.pa_bm_export(self._h, s.ctypes.data_as(_pi64), len(s), int(stride), tab.ctypes.data_as(_pi32),
+                                ctx.ctypes.data_as(_pi32)))
+        return tab, ctx
+
+    def num_free(self) -> int:
+        return int(lib.pa_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(lib.pa_bm_refcount(self._h, int(block)))
+
+    def seq_len(self, seq: int) -> int:
+        return int(lib.pa_bm_seq_len(self._h, int(seq)))
+
+    def num_seqs(self) -> int:
+        return int(lib.pa_bm_num_seqs(self._h))
+
+    def free_list(self) -> np.ndarray:
+        n = int(lib.pa_bm_num_free(self._h))
+        out = np.empty(n, dtype=np.int32)
+        lib.pa_bm_free_list(self._h, out.ctypes.data_as(_pi32), n)
+        return out
+
+    def stats(self) -> Tuple[int, int, int, int, int]:
+        out = np.zeros(5, dtype=np.int64)
+        _check(lib.pa_bm_stats(self._h, out.ctypes.data_as(_pi64)))
+        return tuple(int(x) for x in out)

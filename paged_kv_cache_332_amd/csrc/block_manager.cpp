@@ -1,0 +1,253 @@
+// Host block manager: shared free list of interchangeable fixed-size blocks,
+// per-block sharer counts and per-sequence block tables.
+//
+// From the pages: blocks are handed out one at a time when the last one is
+// full and returned to a shared pool the moment a request finishes
+// ("Paged Attention: Virtual Memory for the KV Cache", §The fix borrowed from
+// operating systems; glossary "What is Paged Attention?"); prefill numbers
+// logical blocks in order and takes physical blocks from a free list
+// ("Paged Attention as a Memory Manager", §How the Kernel Executes Paged
+// Attention); tables of block references can share a block, and a sharer that
+// diverges copies the block it is about to write (§Sharing comes almost for
+// free).  The allocation policy the pages leave open is stated in pa.h.
+#include <algorithm>
+#include <unordered_map>
+#include <vector>
+
+#include "pa_internal.h"
+
+struct pa_bm {
+  struct Seq {
+    std::vector<int32_t> table;
+    int32_t len = 0;
+  };
+  int32_t num_blocks = 0;
+  int32_t block_size = 1;
+  std::vector<int32_t> free_stack;  // back() is the next block handed out
+  std::vector<int32_t> refcount;
+  std::unordered_map<int64_t, Seq> seqs;
+  int64_t cow_count = 0;
+
+  int32_t take() {
+    int32_t b = free_stack.back();
+    free_stack.pop_back();
+    refcount[b] = 1;
+    return b;
+  }
+  int32_t slot(const Seq& s, int32_t pos) const {
+    return s.table[pos / block_size] * block_size + pos % block_size;
+  }
+};
+
+extern "C" {
+
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_order) {
+  if (num_blocks < 0 || block_size <= 0 ||
+      static_cast<int64_t>(num_blocks) * block_size >= (int64_t(1) << 31)) {
+    pa::fail(PA_ERR_INVALID, "pa_bm_create: bad num_blocks %d / block_size %d", num_blocks,
+             block_size);
+    return nullptr;
+  }
+  auto* bm = new pa_bm;
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->refcount.assign(num_blocks, 0);
+  bm->free_stack.resize(num_blocks);
+  std::vector<char> seen(num_blocks, 0);
+  for (int32_t i = 0; i < num_blocks; ++i) {
+    int32_t b = initial_order ? initial_order[i] : i;
+    if (b < 0 || b >= num_blocks || seen[b]) {
+      delete bm;
+      pa::fail(PA_ERR_INVALID, "pa_bm_create: initial_order is not a permutation (entry %d)", i);
+      return nullptr;
+    }
+    seen[b] = 1;
+    bm->free_stack[num_blocks - 1 - i] = b;  // order[0] ends on top
+  }
+  return bm;
+}
+
+void pa_bm_destroy(pa_bm* bm) { delete bm; }
+
+pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t num_tokens, int32_t* slots_out) {
+  if (!bm || num_tokens < 0) return pa::fail(PA_ERR_INVALID, "pa_bm_add_seq: bad arguments");
+  if (bm->seqs.count(seq)) return pa::fail(PA_ERR_INVALID, "pa_bm_add_seq: sequence %lld exists", (long long)seq);
+  int64_t need = (static_cast<int64_t>(num_tokens) + bm->block_size - 1) / bm->block_size;
+  if (need > static_cast<int64_t>(bm->free_stack.size()))
+    return pa::fail(PA_ERR_OOM, "pa_bm_add_seq: need %lld blocks, %zu free", (long long)need,
+                    bm->free_stack.size());
+  pa_bm::Seq s;
+  s.table.reserve(need);
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(bm->take());
+  s.len = num_tokens;
+  if (slots_out)
+    for (int32_t t = 0; t < num_tokens; ++t) slots_out[t] = bm->slot(s, t);
+  bm->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* slots_out,
+                             int32_t* cow_pairs_out, int32_t* num_cow_out) {
+  if (!bm || n < 0 || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)) || !num_cow_out)
+    return pa::fail(PA_ERR_INVALID, "pa_bm_append_slots: bad arguments");
+  // Validate and count the fresh blocks first so the call is all-or-nothing.
+  std::vector<pa_bm::Seq*> ptr(n);
+  std::unordered_map<int32_t, int32_t> rc_after;  // counts of last blocks during the batch
+  std::unordered_map<int64_t, char> seen;
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end())
+      return pa::fail(PA_ERR_INVALID, "pa_bm_append_slots: unknown sequence %lld", (long long)seqs[i]);
+    if (!seen.emplace(seqs[i], 1).second)
+      return pa::fail(PA_ERR_INVALID, "pa_bm_append_slots: sequence %lld repeated", (long long)seqs[i]);
+    ptr[i] = &it->second;
+    const pa_bm::Seq& s = it->second;
+    if (s.len % bm->block_size == 0) {
+      ++need;
+    } else {
+      int32_t last = s.table.back();
+      auto f = rc_after.find(last);
+      int32_t c = f == rc_after.end() ? bm->refcount[last] : f->second;
+      if (c > 1) {
+        ++need;
+        rc_after[last] = c - 1;
+      }
+    }
+  }
+  if (need > static_cast<int64_t>(bm->free_stack.size()))
+    return pa::fail(PA_ERR_OOM, "pa_bm_append_slots: need %lld blocks, %zu free", (long long)need,
+                    bm->free_stack.size());
+  int32_t ncow = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    pa_bm::Seq& s = *ptr[i];
+    int32_t pos = s.len;
+    if (pos % bm->block_size == 0) {
+      s.table.push_back(bm->take());
+    } else if (bm->refcount[s.table.back()] > 1) {
+      int32_t old = s.table.back();
+      int32_t fresh = bm->take();
+      bm->refcount[old] -= 1;
+      s.table.back() = fresh;
+      cow_pairs_out[2 * ncow] = old;
+      cow_pairs_out[2 * ncow + 1] = fresh;
+      ++ncow;
+    }
+    slots_out[i] = bm->slot(s, pos);
+    s.len = pos + 1;
+  }
+  bm->cow_count += ncow;
+  *num_cow_out = ncow;
+  return PA_OK;
+}
+
+pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
+  if (!bm) return pa::fail(PA_ERR_INVALID, "pa_bm_fork: null manager");
+  auto it = bm->seqs.find(parent);
+  if (it == bm->seqs.end() || bm->seqs.count(child))
+    return pa::fail(PA_ERR_INVALID, "pa_bm_fork: unknown parent %lld or existing child %lld",
+                    (long long)parent, (long long)child);
+  pa_bm::Seq s = it->second;
+  for (int32_t b : s.table) bm->refcount[b] += 1;
+  bm->seqs.emplace(child, std::move(s));
+  return PA_OK;
+}
+
+pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq) {
+  if (!bm) return pa::fail(PA_ERR_INVALID, "pa_bm_free_seq: null manager");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end())
+    return pa::fail(PA_ERR_INVALID, "pa_bm_free_seq: unknown sequence %lld", (long long)seq);
+  for (int32_t b : it->second.table) {
+    if (bm->refcount[b] <= 0)
+      return pa::fail(PA_ERR_INVALID, "pa_bm_free_seq: refcount underflow on block %d", b);
+  }
+  for (int32_t b : it->second.table) {
+    if (--bm->refcount[b] == 0) bm->free_stack.push_back(b);
+  }
+  bm->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t stride,
+                       int32_t* tables_out, int32_t* ctx_lens_out) {
+  if (!bm || n < 0 || stride < 0 || (n > 0 && (!seqs || !tables_out || !ctx_lens_out)))
+    return pa::fail(PA_ERR_INVALID, "pa_bm_export: bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end())
+      return pa::fail(PA_ERR_INVALID, "pa_bm_export: unknown sequence %lld", (long long)seqs[i]);
+    if (static_cast<int64_t>(it->second.table.size()) > stride)
+      return pa::fail(PA_ERR_INVALID, "pa_bm_export: sequence %lld holds %zu blocks > stride %d",
+                      (long long)seqs[i], it->second.table.size(), stride);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const pa_bm::Seq& s = bm->seqs.find(seqs[i])->second;
+    int32_t* row = tables_out + static_cast<int64_t>(i) * stride;
+    std::copy(s.table.begin(), s.table.end(), row);
+    std::fill(row + s.table.size(), row + stride, -1);
+    ctx_lens_out[i] = s.len;
+  }
+  return PA_OK;
+}
+
+int32_t pa_bm_num_free(const pa_bm* bm) { return bm ? static_cast<int32_t>(bm->free_stack.size()) : -1; }
+
+int32_t pa_bm_refcount(const pa_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return -1;
+  return bm->refcount[block];
+}
+
+int32_t pa_bm_seq_len(const pa_bm* bm, int64_t seq) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? -1 : it->second.len;
+}
+
+int32_t pa_bm_num_seqs(const pa_bm* bm) { return bm ? static_cast<int32_t>(bm->seqs.size()) : -1; }
+
+int32_t pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap) {
+  if (!bm) return -1;
+  int32_t nf = static_cast<int32_t>(bm->free_stack.size());
+  for (int32_t i = 0; i < std::min(cap, nf); ++i) out[i] = bm->free_stack[nf - 1 - i];
+  return nf;
+}
+
+pa_status pa_bm_stats(const pa_bm* bm, int64_t* out) {
+  if (!bm || !out) return pa::fail(PA_ERR_INVALID, "pa_bm_stats: bad arguments");
+  int64_t used = 0, shared = 0, waste = 0;
+  for (int32_t c : bm->refcount) {
+    used += c > 0;
+    shared += c > 1;
+  }
+  for (const auto& kv : bm->seqs)
+    waste += static_cast<int64_t>(kv.second.table.size()) * bm->block_size - kv.second.len;
+  out[0] = static_cast<int64_t>(bm->free_stack.size());
+  out[1] = used;
+  out[2] = shared;
+  out[3] = bm->cow_count;
+  out[4] = waste;
+  return PA_OK;
+}
+
+pa_status pa_check_tables(const int32_t* tables, int32_t n, int32_t stride, const int32_t* ctx_lens,
+                          int32_t block_size, int32_t num_blocks) {
+  if (n < 0 || stride < 0 || block_size <= 0 || (n > 0 && (!tables || !ctx_lens)))
+    return pa::fail(PA_ERR_INVALID, "pa_check_tables: bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    if (ctx_lens[i] < 0) return pa::fail(PA_ERR_INVALID, "pa_check_tables: ctx[%d] = %d < 0", i, ctx_lens[i]);
+    int64_t nb = (static_cast<int64_t>(ctx_lens[i]) + block_size - 1) / block_size;
+    if (nb > stride)
+      return pa::fail(PA_ERR_INVALID, "pa_check_tables: sequence %d needs %lld entries > stride %d", i,
+                      (long long)nb, stride);
+    for (int64_t j = 0; j < nb; ++j) {
+      int32_t b = tables[static_cast<int64_t>(i) * stride + j];
+      if (b < 0 || b >= num_blocks)
+        return pa::fail(PA_ERR_INVALID, "pa_check_tables: sequence %d entry %lld = %d out of [0, %d)", i,
+                        (long long)j, b, num_blocks);
+    }
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

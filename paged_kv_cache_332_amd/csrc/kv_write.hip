@@ -1,0 +1,87 @@
+// KV append through a slot mapping and whole-block copies for copy-on-write.
+//
+// A request fills the block it holds and asks for another only when it is
+// full ("Paged Attention: Virtual Memory for the KV Cache", §The fix borrowed
+// from operating systems); a sharer that diverges gets its own copy of the
+// block it is about to write (§Sharing comes almost for free).  Both are
+// plain data movement, bound by HBM: the kernels read each source byte once
+// and write each destination byte once.
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+
+// One workgroup per token.  K: the token's row of each head is D/X 16-byte
+// chunks that land at stride BS*16 bytes (K tile [D/X][BS][X]).  V: each
+// element lands at stride BS elements (V tile [D][BS]).  Source reads are
+// fully coalesced; destination writes are the scatter the layout implies.
+template <typename Bits>
+__global__ __launch_bounds__(256) void write_kv_kernel(u32x4* __restrict__ kc,
+                                                       Bits* __restrict__ vc,
+                                                       const u32x4* __restrict__ kn,
+                                                       const Bits* __restrict__ vn,
+                                                       const int32_t* __restrict__ slots,
+                                                       int32_t hkv, int32_t d, int32_t bs) {
+  const int64_t t = blockIdx.x;
+  const int32_t s = slots[t];
+  if (s < 0) return;
+  const int64_t blk = s / bs;
+  const int32_t off = s % bs;
+  const int32_t x = 16 / static_cast<int32_t>(sizeof(Bits));
+  const int32_t cpr = d / x;                      // 16-byte chunks per head row
+  const int32_t nk = hkv * cpr;
+  for (int32_t i = threadIdx.x; i < nk; i += blockDim.x) {
+    const int32_t h = i / cpr, c = i % cpr;
+    kc[((blk * hkv + h) * cpr + c) * bs + off] = kn[t * nk + i];
+  }
+  const int32_t nv = hkv * d;
+  for (int32_t i = threadIdx.x; i < nv; i += blockDim.x) {
+    const int32_t h = i / d, e = i % d;
+    vc[((blk * hkv + h) * d + e) * bs + off] = vn[t * nv + i];
+  }
+}
+
+// grid (num_pairs, 2 * hkv): one workgroup copies one (K or V, head) tile of
+// a block, BS*D elements, in 16-byte units.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ kc,
+                                                          u32x4* __restrict__ vc,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int32_t hkv, int32_t tile_chunks) {
+  const int32_t p = blockIdx.x;
+  const int32_t kv = blockIdx.y / hkv, h = blockIdx.y % hkv;
+  const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+  u32x4* base = kv ? vc : kc;
+  const u32x4* from = base + (src * hkv + h) * tile_chunks;
+  u32x4* to = base + (dst * hkv + h) * tile_chunks;
+  for (int32_t i = threadIdx.x; i < tile_chunks; i += blockDim.x) to[i] = from[i];
+}
+
+hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int32_t* slots, int32_t num_tokens, int32_t hkv, int32_t d,
+                           int32_t bs, int32_t elem_bytes, hipStream_t stream) {
+  dim3 grid(num_tokens), block(256);
+  if (elem_bytes == 2) {
+    hipLaunchKernelGGL(write_kv_kernel<uint16_t>, grid, block, 0, stream,
+                       static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       static_cast<const u32x4*>(k_new), static_cast<const uint16_t*>(v_new), slots,
+                       hkv, d, bs);
+  } else {
+    hipLaunchKernelGGL(write_kv_kernel<uint32_t>, grid, block, 0, stream,
+                       static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache),
+                       static_cast<const u32x4*>(k_new), static_cast<const uint32_t*>(v_new), slots,
+                       hkv, d, bs);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                              int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,
+                              hipStream_t stream) {
+  const int32_t tile_chunks = d * bs * elem_bytes / 16;
+  dim3 grid(num_pairs, 2 * hkv), block(256);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, block, 0, stream, static_cast<u32x4*>(k_cache),
+                     static_cast<u32x4*>(v_cache), pairs, hkv, tile_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace pa

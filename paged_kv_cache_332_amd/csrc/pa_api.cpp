@@ -1,0 +1,219 @@
+// C ABI of libpa.so: argument validation, kernel selection and launches.
+// The operations and their citations are documented in include/pa.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "pa_internal.h"
+#include "pa_kernels.h"
+
+namespace pa {
+
+namespace {
+thread_local std::string g_error;
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
+bool valid_dtype(pa_dtype d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pa_status check_cache_shape(const char* fn, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, pa_dtype dtype) {
+  if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID, "%s: unknown dtype %d", fn, int(dtype));
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID, "%s: sizes must be positive (heads %d, dim %d, block %d, blocks %d)", fn,
+                num_kv_heads, head_dim, block_size, num_blocks);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d not in {8, 16, 32}", fn, block_size);
+  if (static_cast<int64_t>(num_blocks) * block_size >= (int64_t(1) << 31))
+    return fail(PA_ERR_INVALID, "%s: num_blocks * block_size must stay below 2^31", fn);
+  return PA_OK;
+}
+
+pa_status hip_status(const char* fn, hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+}
+
+int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a + b - 1) / b); }
+
+constexpr int32_t kMinAutoPartition = 256;
+
+}  // namespace
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+const char* pa_last_error(void) { return pa::g_error.c_str(); }
+
+const char* pa_version(void) { return "pa 0.1 gfx950"; }
+
+pa_status pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                      const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                      void* stream) {
+  if (pa_status st = pa::check_cache_shape("pa_write_kv", num_kv_heads, head_dim, block_size, num_blocks, dtype))
+    return st;
+  if (num_tokens < 0) return pa::fail(PA_ERR_INVALID, "pa_write_kv: num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+    return pa::fail(PA_ERR_INVALID, "pa_write_kv: null pointer");
+  if (!pa::aligned16(k_cache) || !pa::aligned16(k_new) || !pa::aligned16(v_cache) || !pa::aligned16(v_new))
+    return pa::fail(PA_ERR_INVALID, "pa_write_kv: caches and inputs must be 16-byte aligned");
+  return pa::hip_status("pa_write_kv",
+                        pa::launch_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens,
+                                            num_kv_heads, head_dim, block_size, pa::elem_bytes(dtype),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, pa_dtype dtype, void* stream) {
+  if (pa_status st = pa::check_cache_shape("pa_copy_blocks", num_kv_heads, head_dim, block_size, num_blocks, dtype))
+    return st;
+  if (num_pairs < 0) return pa::fail(PA_ERR_INVALID, "pa_copy_blocks: num_pairs %d < 0", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return pa::fail(PA_ERR_INVALID, "pa_copy_blocks: null pointer");
+  if (!pa::aligned16(k_cache) || !pa::aligned16(v_cache))
+    return pa::fail(PA_ERR_INVALID, "pa_copy_blocks: caches must be 16-byte aligned");
+  if (2 * num_kv_heads > 65535) return pa::fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: too many kv heads");
+  return pa::hip_status("pa_copy_blocks",
+                        pa::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, num_kv_heads, head_dim,
+                                               block_size, pa::elem_bytes(dtype),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                    int32_t block_size) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)max_context_len;
+  (void)block_size;
+  return 512;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || partition_size < 0)
+    return 0;
+  const int32_t part = partition_size ? partition_size : pa::kMinAutoPartition;
+  const int32_t pmax = pa::ceil_div(max_context_len, part);
+  if (pmax <= 1) return 0;
+  const size_t rows = size_t(num_seqs) * num_q_heads * pmax;
+  return 2 * pa::round_up(rows * sizeof(float)) + pa::round_up(rows * head_dim * sizeof(float));
+}
+
+pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                            const void* v_cache, pa_dtype kv_dtype, const int32_t* block_tables,
+                            int32_t table_stride, const int32_t* context_lens, int32_t max_context_len,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes, void* stream, pa_kernel kernel) {
+  const char* fn = "pa_decode";
+  if (pa_status st = pa::check_cache_shape(fn, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype))
+    return st;
+  if (out_dtype != PA_F32 && out_dtype != kv_dtype)
+    return pa::fail(PA_ERR_INVALID, "%s: out_dtype must be F32 or the kv dtype", fn);
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || table_stride < 0)
+    return pa::fail(PA_ERR_INVALID, "%s: bad sizes (seqs %d, q heads %d, max ctx %d, stride %d)", fn, num_seqs,
+                    num_q_heads, max_context_len, table_stride);
+  if (num_q_heads % num_kv_heads)
+    return pa::fail(PA_ERR_INVALID, "%s: %d query heads not a multiple of %d kv heads", fn, num_q_heads,
+                    num_kv_heads);
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: group size %d not in {1,2,4,8,16}", fn, group);
+  if (pa::ceil_div(max_context_len, block_size) > table_stride)
+    return pa::fail(PA_ERR_INVALID, "%s: table_stride %d < blocks of max_context_len %d", fn, table_stride,
+                    max_context_len);
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return pa::fail(PA_ERR_INVALID, "%s: null pointer", fn);
+  if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache))
+    return pa::fail(PA_ERR_INVALID, "%s: q and caches must be 16-byte aligned", fn);
+  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
+    return pa::fail(PA_ERR_INVALID, "%s: unknown kernel %d", fn, int(kernel));
+  if (kernel == PA_KERNEL_MFMA && kv_dtype == PA_F32)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: the matrix-core kernel needs a 16-bit cache", fn);
+  const int32_t part = partition_size ? partition_size
+                                      : pa_decode_default_partition(num_seqs, num_kv_heads, max_context_len,
+                                                                    block_size);
+  if (part <= 0 || part % 64 || part % (4 * block_size))
+    return pa::fail(PA_ERR_INVALID, "%s: partition_size %d must be a positive multiple of 64 and of 4*BS", fn,
+                    part);
+  const int32_t pmax = std::max(1, pa::ceil_div(max_context_len, part));
+  if (static_cast<int64_t>(num_kv_heads) * pmax * num_seqs * (group > 4 && kernel == PA_KERNEL_VALU ? group / 4 : 1) >=
+      (int64_t(1) << 31) - 8)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: too many work items", fn);
+  size_t need = 0;
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.tables = block_tables;
+  a.ctx = context_lens;
+  a.table_stride = table_stride;
+  a.max_ctx = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.pmax = pmax;
+  a.part = part;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_f32 = out_dtype == PA_F32;
+  if (pmax > 1) {
+    const size_t rows = size_t(num_seqs) * num_q_heads * pmax;
+    const size_t ml = pa::round_up(rows * sizeof(float));
+    need = 2 * ml + pa::round_up(rows * head_dim * sizeof(float));
+    if (!workspace || workspace_bytes < need)
+      return pa::fail(PA_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+    char* w = static_cast<char*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(w);
+    a.ws_l = reinterpret_cast<float*>(w + ml);
+    a.ws_acc = reinterpret_cast<float*>(w + 2 * ml);
+  }
+  const bool use_mfma =
+      kernel == PA_KERNEL_MFMA || (kernel == PA_KERNEL_AUTO && kv_dtype != PA_F32 && group >= 2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, kv_dtype, head_dim, block_size, group, s)
+                          : pa::launch_decode_valu(a, kv_dtype, head_dim, block_size, group, s);
+  if (e != hipSuccess) return pa::hip_status(fn, e);
+  if (pmax > 1) {
+    e = pa::launch_merge(a, kv_dtype, head_dim, s);
+    if (e != hipSuccess) return pa::hip_status(fn, e);
+  }
+  return PA_OK;
+}
+
+pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
+                    pa_dtype kv_dtype, const int32_t* block_tables, int32_t table_stride,
+                    const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, float scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return pa_decode_variant(out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, table_stride,
+                           context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                           block_size, num_blocks, scale, partition_size, workspace, workspace_bytes, stream,
+                           PA_KERNEL_AUTO);
+}
+
+}  // extern "C"

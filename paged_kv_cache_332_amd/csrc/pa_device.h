@@ -1,0 +1,154 @@
+// Device helpers for the gfx950 kernels: element types, conversions and
+// wave64 cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Storage element tags.  `bits` is the raw storage type.
+struct F32 {
+  using bits = uint32_t;
+  static constexpr int kBytes = 4;
+  __device__ static float to_f32(uint32_t b) { return __uint_as_float(b); }
+  __device__ static uint32_t from_f32(float x) { return __float_as_uint(x); }
+};
+struct F16 {
+  using bits = uint16_t;
+  static constexpr int kBytes = 2;
+  __device__ static float to_f32(uint32_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+  }
+  __device__ static uint32_t from_f32(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+  // two packed elements of a 32-bit word -> floats
+  __device__ static float lo(uint32_t w) { return to_f32(w & 0xFFFFu); }
+  __device__ static float hi(uint32_t w) { return to_f32(w >> 16); }
+  __device__ static float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                  false);
+  }
+};
+struct BF16 {
+  using bits = uint16_t;
+  static constexpr int kBytes = 2;
+  __device__ static float to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+  __device__ static uint32_t from_f32(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+  }
+  __device__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+  __device__ static float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+  }
+};
+
+// ---------------------------------------------------------------- lanes
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// DPP controls (all stay inside a 16-lane row)
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowRor8 = 0x128;     // lane i <- lane (i+8) mod 16 == i ^ 8
+
+struct OpSum {
+  __device__ static float op(float a, float b) { return a + b; }
+};
+struct OpMax {
+  __device__ static float op(float a, float b) { return fmaxf(a, b); }
+};
+
+// Combine with the lane whose id differs in bit 4 (xor 16) or bit 5 (xor 32).
+// The gfx950 permlane swaps exchange 16-lane rows / 32-lane halves between
+// two registers; combining the two results is symmetric, so every lane ends
+// with op(x[l], x[l ^ 16]) (resp. x[l ^ 32]).
+template <class Op>
+__device__ __forceinline__ float xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return Op::op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <class Op>
+__device__ __forceinline__ float xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return Op::op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// All-reduce over the lanes that differ only in bits [0, NBITS) of the lane
+// id (groups of 2^NBITS consecutive lanes).  The mirror patterns pair whole
+// already-reduced sub-groups, so bits are taken in increasing order.
+template <class Op, int NBITS>
+__device__ __forceinline__ float reduce_low_bits(float x) {
+  if constexpr (NBITS > 0) x = Op::op(x, dpp<kQuadXor1>(x));
+  if constexpr (NBITS > 1) x = Op::op(x, dpp<kQuadXor2>(x));
+  if constexpr (NBITS > 2) x = Op::op(x, dpp<kRowHalfMirror>(x));
+  if constexpr (NBITS > 3) x = Op::op(x, dpp<kRowMirror>(x));
+  if constexpr (NBITS > 4) x = xor16<Op>(x);
+  if constexpr (NBITS > 5) x = xor32<Op>(x);
+  return x;
+}
+
+// All-reduce over lane-id bits [LO, 6) with LO >= 3 (the other bits are
+// left as they are): exact xor partners for bits 3, 4, 5.
+template <class Op, int LO>
+__device__ __forceinline__ float reduce_high_bits(float x) {
+  static_assert(LO >= 3, "only bits 3..5 have exact xor partners here");
+  if constexpr (LO <= 3) x = Op::op(x, dpp<kRowRor8>(x));
+  if constexpr (LO <= 4) x = xor16<Op>(x);
+  if constexpr (LO <= 5) x = xor32<Op>(x);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int N>
+struct ilog2 {
+  static constexpr int value = 1 + ilog2<N / 2>::value;
+};
+template <>
+struct ilog2<1> {
+  static constexpr int value = 0;
+};
+
+// Keeps the compiler from moving LDS accesses of one wave across this point
+// (the LDS unit itself executes one wave's operations in order).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Work-item order: items are ranked (kv head, partition, sequence) with the
+// sequence fastest, and consecutive ranks are kept on one XCD (workgroups
+// are dealt round-robin over the 8 XCDs by id), so the 64 sharers of one
+// prefix block read it through the same L2.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int64_t xcd_rank(int64_t total) {
+  int64_t per = (total + kNumXcd - 1) / kNumXcd;
+  int64_t bid = blockIdx.x;
+  return (bid % kNumXcd) * per + bid / kNumXcd;
+}
+inline int64_t xcd_grid(int64_t total) { return ((total + kNumXcd - 1) / kNumXcd) * kNumXcd; }
+
+}  // namespace pa

@@ -1,0 +1,48 @@
+// Launchers of the gfx950 kernels (host-callable, defined in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pa {
+
+// Arguments of the decode partition pass and the merge pass.
+struct DecodeArgs {
+  void* out;                     // [B][Hq][D], fp32 or the kv dtype
+  const void* q;                 // [B][Hq][D], kv dtype
+  const void* k;                 // K pool
+  const void* v;                 // V pool
+  const int32_t* tables;         // [B][table_stride]
+  const int32_t* ctx;            // [B]
+  float* ws_m;                   // [B][Hq][pmax]  running max (log2 domain)
+  float* ws_l;                   // [B][Hq][pmax]  sum of exp2(s - m)
+  float* ws_acc;                 // [B][Hq][pmax][D] unnormalised output
+  int32_t table_stride;
+  int32_t max_ctx;               // host bound; device lengths are clamped to [0, max_ctx]
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t pmax;                  // partitions of the longest context
+  int32_t part;                  // tokens per partition
+  float scale_log2;              // scale * log2(e)
+  int32_t out_f32;               // 1: fp32 output, 0: kv dtype output
+};
+
+hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                           const int32_t* slots, int32_t num_tokens, int32_t hkv, int32_t d,
+                           int32_t bs, int32_t elem_bytes, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                              int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,
+                              hipStream_t stream);
+
+// dtype: 0 f32, 1 f16, 2 bf16 (pa_dtype values).  Return hipErrorInvalidValue
+// for a shape they were not instantiated for.
+hipError_t launch_decode_valu(const DecodeArgs& a, int32_t dtype, int32_t d, int32_t bs,
+                              int32_t group, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int32_t dtype, int32_t d, int32_t bs,
+                              int32_t group, hipStream_t stream);
+hipError_t launch_merge(const DecodeArgs& a, int32_t dtype, int32_t d, hipStream_t stream);
+
+}  // namespace pa

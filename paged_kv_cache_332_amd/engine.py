@@ -1,0 +1,141 @@
+"""Host runtime around libpa: one layer's K/V pools, the block manager and the
+device copies of its bookkeeping, driven one decode step at a time.
+
+A decode step is: the block manager hands each sequence a slot for its new
+token (taking a block when the last is full, or copying a shared last block
+first); the copy pairs, slots, tables and context lengths go to the device
+through pinned staging buffers on the compute stream; then pa_copy_blocks,
+pa_write_kv and pa_decode (partition pass + log-sum-exp merge) run on that
+stream.  Staging buffers rotate through a small ring guarded by events so the
+host can prepare step k+1 while the device still reads step k's copy.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (PA_KERNEL_AUTO, BlockManager, alloc_cache, pa_copy_blocks, pa_decode_variant,
+               pa_decode_workspace_bytes, pa_write_kv)
+
+__all__ = ["PagedKVEngine"]
+
+
+class _Staging:
+    """Pinned host buffers + device mirrors for one step's bookkeeping."""
+
+    def __init__(self, max_seqs: int, stride: int, device):
+        self.stride = stride
+        pin = dict(dtype=torch.int32, pin_memory=True)
+        self.h_tables = torch.empty((max_seqs, stride), **pin)
+        self.h_ctx = torch.empty(max_seqs, **pin)
+        self.h_slots = torch.empty(max_seqs, **pin)
+        self.h_pairs = torch.empty((max_seqs, 2), **pin)
+        dev = dict(dtype=torch.int32, device=device)
+        self.d_tables = torch.empty((max_seqs, stride), **dev)
+        self.d_ctx = torch.empty(max_seqs, **dev)
+        self.d_slots = torch.empty(max_seqs, **dev)
+        self.d_pairs = torch.empty((max_seqs, 2), **dev)
+        self.event: Optional[torch.cuda.Event] = None
+
+    def wait(self):
+        if self.event is not None:
+            self.event.synchronize()
+
+
+class PagedKVEngine:
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int, dtype,
+                 order: Optional[Sequence[int]] = None, device: str = "cuda", poison: bool = True,
+                 max_seqs: int = 256, max_context: int = 4096, ring: int = 3):
+        self.N, self.H, self.D, self.BS, self.dtype = num_blocks, num_kv_heads, head_dim, block_size, dtype
+        self.device = torch.device(device)
+        self.bm = BlockManager(num_blocks, block_size, order)
+        self.k_cache, self.v_cache = alloc_cache(num_blocks, num_kv_heads, head_dim, block_size, dtype,
+                                                 device=self.device, poison=poison)
+        self.max_seqs = max_seqs
+        self.stride = -(-max_context // block_size)
+        self._ring = [_Staging(max_seqs, self.stride, self.device) for _ in range(ring)]
+        self._ri = 0
+        self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
+
+    # ------------------------------------------------------------- helpers
+    def _next(self) -> _Staging:
+        st = self._ring[self._ri]
+        self._ri = (self._ri + 1) % len(self._ring)
+        st.wait()
+        return st
+
+    def _record(self, st: _Staging, stream):
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        st.event = ev
+
+    def workspace(self, num_seqs: int, num_q_heads: int, max_ctx: int, partition_size: int = 0):
+        need = pa_decode_workspace_bytes(num_seqs, num_q_heads, self.D, max_ctx, partition_size)
+        if need > self._ws.numel():
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    # ----------------------------------------------------------- sequences
+    def add_seq(self, seq: int, k_rows: Optional[torch.Tensor], v_rows: Optional[torch.Tensor], n: int,
+                stream=None) -> np.ndarray:
+        """New sequence of n tokens; writes their K/V rows ([n][Hkv][D], device) if given."""
+        slots = self.bm.add_seq(seq, n)
+        if k_rows is not None and n:
+            d_slots = torch.from_numpy(slots).to(self.device, non_blocking=False)
+            pa_write_kv(self.k_cache, self.v_cache, k_rows, v_rows, d_slots, stream=stream)
+        return slots
+
+    def fork(self, parent: int, child: int) -> None:
+        self.bm.fork(parent, child)
+
+    def free_seq(self, seq: int) -> None:
+        self.bm.free_seq(seq)
+
+    def append(self, seqs: Sequence[int], k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
+        """One token per sequence: copy-on-write copies, then the K/V write."""
+        stream = stream or torch.cuda.current_stream()
+        n = len(seqs)
+        st = self._next()
+        slots, pairs = self.bm.append_slots(seqs)
+        st.h_slots[:n].numpy()[:] = slots
+        st.d_slots[:n].copy_(st.h_slots[:n], non_blocking=True)
+        if len(pairs):
+            st.h_pairs[: len(pairs)].numpy()[:] = pairs
+            st.d_pairs[: len(pairs)].copy_(st.h_pairs[: len(pairs)], non_blocking=True)
+            pa_copy_blocks(self.k_cache, self.v_cache, st.d_pairs[: len(pairs)], stream=stream)
+        pa_write_kv(self.k_cache, self.v_cache, k_new, v_new, st.d_slots[:n], stream=stream)
+        self._record(st, stream)
+        return slots, pairs
+
+    def export(self, seqs: Sequence[int]):
+        st = self._next()
+        n = len(seqs)
+        tab, ctx = self.bm.export(seqs, self.stride, st.h_tables[:n].numpy(), st.h_ctx[:n].numpy())
+        return st, tab, ctx
+
+    def decode(self, seqs: Sequence[int], q: torch.Tensor, out: Optional[torch.Tensor] = None,
+               out_dtype=torch.float32, partition_size: int = 0, kernel: int = PA_KERNEL_AUTO,
+               stream=None) -> torch.Tensor:
+        """Attention of q [n][Hq][D] over each listed sequence's whole context."""
+        stream = stream or torch.cuda.current_stream()
+        n = len(seqs)
+        st, tab, ctx = self.export(seqs)
+        self.last_tables, self.last_ctx = tab, ctx      # views of the pinned staging buffers
+        max_ctx = int(ctx.max()) if n else 0
+        st.d_tables[:n].copy_(st.h_tables[:n], non_blocking=True)
+        st.d_ctx[:n].copy_(st.h_ctx[:n], non_blocking=True)
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=self.device)
+        ws = self.workspace(n, q.shape[1], max_ctx, partition_size)
+        pa_decode_variant(out, q, self.k_cache, self.v_cache, st.d_tables[:n], st.d_ctx[:n], max_ctx,
+                          1.0 / float(self.D) ** 0.5, partition_size, ws if ws.numel() else None,
+                          stream=stream, kernel=kernel)
+        self._record(st, stream)
+        return out
+
+    def step(self, seqs, k_new, v_new, q, out=None, **kw):
+        """One decode step: append the new token of every sequence, then attend."""
+        self.append(seqs, k_new, v_new, stream=kw.get("stream"))
+        return self.decode(seqs, q, out=out, **kw)

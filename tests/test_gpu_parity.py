@@ -1,0 +1,266 @@
+"""HIP path against the CPU oracle on an MI355X.
+
+Integer results (slots, copy pairs, tables, context lengths, the K/V pool
+bytes) must be bit-identical; decode outputs (fp32) must be within 2e-3 of the
+float64 oracle for 16-bit caches and 1e-5 for fp32 caches.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+
+
+def _pa():
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    return pa, runner
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def pool_bits(t: torch.Tensor) -> np.ndarray:
+    if t.element_size() == 2:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+def check_run(w, dev, ref, tol=None, pools=True, label=""):
+    """Compare a device replay with the oracle's replay of the same script."""
+    tol = TOL[w.cfg.dtype] if tol is None else tol
+    assert len(dev.appends) == len(ref.appends)
+    for a, b in zip(dev.appends, ref.appends):
+        assert list(a["slots"]) == list(b["slots"]), label
+        assert a["pairs"] == [tuple(p) for p in b["pairs"]], label
+    assert len(dev.decodes) == len(ref.decodes)
+    errs = []
+    for d, r in zip(dev.decodes, ref.decodes):
+        assert np.array_equal(d.tables, r.tables) and np.array_equal(d.ctx, r.ctx), label
+        out = d.out.float().cpu().numpy().astype(np.float64)
+        rows = r.computed
+        assert np.all(np.isfinite(out[rows])), label
+        err = float(np.max(np.abs(out[rows] - r.out[rows]))) if rows else 0.0
+        errs.append(err)
+        assert err <= tol, f"{label}: max abs error {err:.3e} > {tol}"
+    if pools:
+        kb, vb = ref.cache.pool_bits()
+        assert np.array_equal(pool_bits(dev.engine.k_cache), kb), f"{label}: K pool bytes differ"
+        assert np.array_equal(pool_bits(dev.engine.v_cache), vb), f"{label}: V pool bytes differ"
+    return errs
+
+
+# ------------------------------------------------------------ small cases
+SMALL = []
+for dtype in ("f32", "f16", "bf16"):
+    for d in (64, 128):
+        for bs in (8, 16, 32):
+            for g in (1, 4, 8):
+                kernels = ["valu"] + (["mfma"] if dtype != "f32" and g > 1 else [])
+                for kern in kernels:
+                    SMALL.append((dtype, d, bs, g, kern))
+
+
+@pytest.mark.parametrize("dtype,d,bs,g,kern", SMALL, ids=lambda *a: None)
+def test_small_shapes(dtype, d, bs, g, kern):
+    """Ragged contexts (one token, a block minus one, exact blocks, several
+    partitions with a ragged tail) with split-K at a small partition size."""
+    pa, runner = _pa()
+    hkv = 2
+    ctx = [1, bs - 1, bs, bs + 1, 3 * bs, 700, 129]
+    w = W.tiny(num_seqs=len(ctx), num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=d, block_size=bs,
+               dtype=dtype, ctx=ctx, seed=bs + d + g)
+    part = max(128, 4 * bs)
+    say("small", dtype, d, bs, g, kern, "part", part)
+    ref = oracle.run_scenario(w)
+    kernel = pa.PA_KERNEL_MFMA if kern == "mfma" else pa.PA_KERNEL_VALU
+    dev = runner.run_script(w, partition_size=part, kernel=kernel)
+    check_run(w, dev, ref, label=f"{dtype}/D{d}/BS{bs}/g{g}/{kern}")
+
+
+@pytest.mark.parametrize("part", [64, 128, 256, 512, 1024, 0])
+@pytest.mark.parametrize("kern", ["valu", "mfma"])
+def test_partition_sizes(part, kern):
+    """Every partition size gives the oracle's result (one partition, many,
+    and the merge of ragged ones)."""
+    pa, runner = _pa()
+    if part and part % (4 * 16):
+        pytest.skip("partition must hold 4 blocks")
+    w = W.tiny(num_seqs=5, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
+               ctx=[1, 63, 64, 1000, 2049], seed=3)
+    say("partition", part, kern)
+    ref = oracle.run_scenario(w)
+    dev = runner.run_script(w, partition_size=part,
+                            kernel=pa.PA_KERNEL_MFMA if kern == "mfma" else pa.PA_KERNEL_VALU)
+    check_run(w, dev, ref, label=f"part{part}/{kern}")
+
+
+# --------------------------------------------------------- full configs
+@functools.lru_cache(maxsize=1)
+def _config(name):
+    say("generating", name)
+    w = W.build(name)
+    say("oracle", name)
+    ref = oracle.run_scenario(w)
+    return w, ref
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["c1_tiny_f32", "c2_gqa_bf16", "c2_gqa_bf16_bs8", "c2_gqa_bf16_bs32",
+                                  "c4a_prefix_share", "c4b_prefix_cow", "c3_mha_f16_churn", "c5_long_splitk"])
+def test_config_parity(name):
+    """The five configurations at full size, in the launch configuration the
+    benchmark times (library-chosen partition size, or 512 tokens for the
+    long-context split-K configuration): every output row and every pool byte."""
+    pa, runner = _pa()
+    w, ref = _config(name)
+    say("device replay", name)
+    dev = runner.run_script(w, partition_size=w.cfg.partition_size)
+    errs = check_run(w, dev, ref, label=name)
+    say(name, "max abs errors", errs)
+    if name == "c4a_prefix_share":
+        assert all(len(a["pairs"]) == 0 for a in dev.appends)
+    if name == "c4b_prefix_cow":
+        assert len(dev.appends[0]["pairs"]) == 63
+    del dev
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_half_precision_output_is_rounded_fp32():
+    """The bf16 output is the fp32 output rounded to nearest even (torch's
+    conversion), bit for bit, on the batch-64 GQA configuration."""
+    pa, runner = _pa()
+    w, ref = _config("c2_gqa_bf16")
+    say("bf16 output")
+    dev = runner.run_script(w, out_dtype=torch.bfloat16)
+    eng = dev.engine
+    q = dev.q_dev[0]
+    seqs = list(range(w.cfg.num_seqs))
+    out32 = eng.decode(seqs, q, out_dtype=torch.float32)
+    out16 = dev.decodes[-1].out
+    torch.cuda.synchronize()
+    assert torch.equal(out32.to(torch.bfloat16).view(torch.int16), out16.view(torch.int16))
+    err = float((out16.double().cpu() - torch.from_numpy(ref.decodes[-1].out)).abs().max())
+    say("bf16 output max abs error", err)
+
+
+# ------------------------------------------------ invariants on the device
+def test_permutation_invariance_bitwise():
+    """Blocks may sit anywhere in any order: outputs are bit-identical when the
+    physical blocks are permuted (the reduction order follows logical
+    position only)."""
+    pa, runner = _pa()
+    outs = []
+    for permute in (False, True):
+        w = W.tiny(num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
+                   ctx=[5, 300, 77, 1030], seed=9, permute=permute)
+        for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA):
+            say("permutation", permute, kern)
+            dev = runner.run_script(w, partition_size=256, kernel=kern)
+            outs.append((permute, kern, dev.decodes[-1].out.cpu(), dev.decodes[-1].tables))
+    for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA):
+        a = [o for o in outs if o[1] == kern and not o[0]][0]
+        b = [o for o in outs if o[1] == kern and o[0]][0]
+        assert not np.array_equal(a[3], b[3])
+        assert torch.equal(a[2], b[2])
+
+
+def test_shared_equals_unshared_bitwise():
+    """Sequences whose tables point at one physical prefix give the same
+    outputs, bit for bit, as sequences holding private copies."""
+    pa, runner = _pa()
+    from scenarios import fork_workload
+    for prefix in (16, 13):
+        res = []
+        for share in (True, False):
+            w = fork_workload(prefix, [1, 3, 9, 20], share, block_size=8, num_kv_heads=2, num_q_heads=8,
+                              head_dim=128)
+            say("sharing", prefix, share)
+            dev = runner.run_script(w, partition_size=128)
+            res.append(dev.decodes[-1].out.cpu())
+            if share:
+                ref = oracle.run_scenario(w)
+                check_run(w, dev, ref, label=f"shared prefix {prefix}")
+        assert torch.equal(res[0], res[1])
+
+
+def test_cow_isolation():
+    """After a sharer copies the partial block it writes, the block the others
+    still share keeps its bytes and their outputs are unchanged, bit for bit."""
+    pa, runner = _pa()
+    from scenarios import fork_workload
+    w = fork_workload(13, [0, 0, 0], True, block_size=8, num_kv_heads=2, num_q_heads=8, head_dim=128)
+    w.ops = w.ops[:4] + [("decode", [0, 1, 2], 0)]
+    say("cow isolation: before")
+    d0 = runner.run_script(w, partition_size=128)
+    last = d0.engine.bm.export([0], 2)[0][0][1]
+    kb0 = pool_bits(d0.engine.k_cache)[last].copy()
+    vb0 = pool_bits(d0.engine.v_cache)[last].copy()
+    w.ops = w.ops[:4] + [("append", [1]), ("decode", [0, 2], 0)]
+    say("cow isolation: after")
+    d1 = runner.run_script(w, partition_size=128)
+    assert d1.appends[0]["pairs"] == [(int(last), int(d1.engine.bm.export([1], 2)[0][0][1]))]
+    assert np.array_equal(pool_bits(d1.engine.k_cache)[last], kb0)
+    assert np.array_equal(pool_bits(d1.engine.v_cache)[last], vb0)
+    assert torch.equal(d1.decodes[-1].out.cpu(), d0.decodes[-1].out.cpu()[[0, 2]])
+    ref = oracle.run_scenario(w)
+    check_run(w, d1, ref, label="cow")
+
+
+def test_zero_context_gives_zero_rows():
+    pa, runner = _pa()
+    from paged_kv_cache_332_amd.engine import PagedKVEngine
+    say("zero context")
+    eng = PagedKVEngine(16, 2, 128, 16, torch.bfloat16, max_seqs=3, max_context=64)
+    rows = torch.randn(40, 2, 128, device="cuda").to(torch.bfloat16)
+    eng.add_seq(0, None, None, 0)
+    eng.add_seq(1, rows, rows, 40)
+    eng.add_seq(2, None, None, 0)
+    q = torch.randn(3, 8, 128, device="cuda").to(torch.bfloat16)
+    for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA):
+        out = eng.decode([0, 1, 2], q, kernel=kern)
+        torch.cuda.synchronize()
+        assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+        assert torch.all(torch.isfinite(out[1])) and torch.any(out[1] != 0)
+
+
+def test_write_kv_skips_negative_slots():
+    pa, runner = _pa()
+    say("negative slots")
+    k, v = pa.alloc_cache(4, 2, 64, 8, torch.float16)
+    before_k, before_v = pool_bits(k), pool_bits(v)
+    x = torch.randn(3, 2, 64, device="cuda").to(torch.float16)
+    slots = torch.tensor([-1, 9, -5], dtype=torch.int32, device="cuda")
+    pa.pa_write_kv(k, v, x, x, slots)
+    torch.cuda.synchronize()
+    after_k, after_v = pool_bits(k), pool_bits(v)
+    changed = np.argwhere(after_k != before_k)
+    assert set(changed[:, 0].tolist()) == {1} and set(changed[:, 3].tolist()) == {1}
+    cm = oracle.PagedCacheModel(4, 2, 64, 8, "f16")
+    cm.write([-1, 9, -5], x.float().cpu().numpy(), x.float().cpu().numpy())
+    assert np.array_equal(after_k, cm.k) and np.array_equal(after_v, cm.v)
+
+
+def test_large_logits_stay_finite():
+    """Scores far apart (query x 64): the running-maximum softmax neither
+    overflows nor loses the dominant token."""
+    pa, runner = _pa()
+    w = W.tiny(num_seqs=3, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
+               ctx=[40, 600, 1500], seed=4)
+    w.q_sets = [W.round_to_dtype(w.q_sets[0] * 64.0, "bf16")]
+    ref = oracle.run_scenario(w)
+    for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA):
+        say("large logits", kern)
+        dev = runner.run_script(w, partition_size=256, kernel=kern)
+        check_run(w, dev, ref, label=f"large logits {kern}")

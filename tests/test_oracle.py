@@ -10,6 +10,7 @@ from oracle.block_manager import BlockManagerModel, InvalidOp, OutOfBlocks
 from oracle.cache import PagedCacheModel
 
 import oracle_pins as P
+from scenarios import fork_workload
 
 
 @pytest.mark.parametrize("check", P.ATTN_CHECKS, ids=lambda f: f.__name__)
@@ -138,38 +139,7 @@ def test_scenario_permutation_invariance():
 
 
 def _fork_workload(prefix, suffix, share: bool):
-    """Sequences with a common prefix, either forked (shared blocks) or added
-    as independent copies."""
-    base = _tiny(num_seqs=len(suffix), ctx=[prefix + s for s in suffix], block_size=8,
-                 num_kv_heads=2, num_q_heads=4, head_dim=64, seed=5)
-    B = len(suffix)
-    # every sequence reads the prefix rows of sequence 0
-    row_start = base.row_start.copy()
-    k, v = base.k_rows, base.v_rows
-    w = W.Workload(base.cfg, base.ctx, k, v, base.q_sets, [], 4 * int(base.num_blocks) + 64,
-                   row_start, 0)
-    pref_rows = np.arange(prefix)
-
-    def row_of(seq, positions):
-        positions = np.asarray(positions)
-        return np.where(positions < prefix, pref_rows[np.minimum(positions, prefix - 1)],
-                        row_start[seq] + positions)
-    w.row_of = row_of
-    ops = [("create", w.num_blocks, None)]
-    if share:
-        ops.append(("add_seq", 0, prefix, True))
-        ops += [("fork", 0, i) for i in range(1, B)]
-    else:
-        ops += [("add_seq", i, prefix, True) for i in range(B)]
-    done = [0] * B
-    while any(done[i] < suffix[i] for i in range(B)):
-        step = [i for i in range(B) if done[i] < suffix[i]]
-        ops.append(("append", step))
-        for i in step:
-            done[i] += 1
-    ops.append(("decode", list(range(B)), 0))
-    w.ops = ops
-    return w
+    return fork_workload(prefix, suffix, share)
 
 
 def test_scenario_shared_equals_unshared():

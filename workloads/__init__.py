@@ -147,7 +147,20 @@ def _ceil_div(a, b):
     return -(-np.asarray(a) // b)
 
 
+_KV_MEMO: dict = {}
+
+
 def _draw_kv(cfg: Config, rows: int, k_scale: float = 1.0):
+    # the block-size sweep shares its draws: keep the last one
+    key = (cfg.index, rows, cfg.num_kv_heads, cfg.head_dim, cfg.dtype, k_scale)
+    if key in _KV_MEMO:
+        return _KV_MEMO[key]
+    _KV_MEMO.clear()
+    _KV_MEMO[key] = _draw_kv_uncached(cfg, rows, k_scale)
+    return _KV_MEMO[key]
+
+
+def _draw_kv_uncached(cfg: Config, rows: int, k_scale: float = 1.0):
     shape = (rows, cfg.num_kv_heads, cfg.head_dim)
     k = _rng(cfg.index, 2).standard_normal(shape, dtype=np.float32)
     if k_scale != 1.0:
