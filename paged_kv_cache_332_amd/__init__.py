@@ -5,7 +5,7 @@ A thin Python binding over the C ABI of ``libpa.so`` (declared in
 (block-table bookkeeping, KV append, copy-on-write copies, attention, split-K
 merge) runs in the library.  PyTorch supplies device memory and streams.
 
-The library must be built first (``python -m paged_kv_cache_332_amd.build``);
+The library must be built first (``python paged_kv_cache_332_amd/build.py``);
 importing this package without it raises ImportError — there is no fallback.
 """
 from __future__ import annotations
@@ -26,7 +26,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built: run `python -m paged_kv_cache_332_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built: run `python paged_kv_cache_332_amd/build.py`")
 lib = ctypes.CDLL(LIB_PATH)
 
 PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_HIP, PA_ERR_UNSUPPORTED = range(5)

@@ -1,4 +1,4 @@
-"""Build libpa.so (HIP for gfx950) in place: ``python -m paged_kv_cache_332_amd.build``.
+"""Build libpa.so (HIP for gfx950) in place: ``python paged_kv_cache_332_amd/build.py``.
 
 Each translation unit is compiled by hipcc in parallel into ``_build/`` and
 linked into ``paged_kv_cache_332_amd/libpa.so``.  Packed-FP32 instruction
