@@ -39,7 +39,22 @@ def parse():
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (scales byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain device-to-device copy of known size: what FETCH_SIZE and
+    WRITE_SIZE read for it gives the factor from counter units to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "calls": 5}), flush=True)
 
 
 def kv_bytes(ctx: np.ndarray, hkv: int, d: int, esize: int) -> int:
@@ -100,6 +115,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU layout is a design "
               "note, not a measured path", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     import workloads as W
     import paged_kv_cache_332_amd as pa
