@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2_gqa_bf16")
     ap.add_argument("--partition", type=int, default=None, help="tokens per split-K partition (0 = library)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma", "stream"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -127,7 +127,8 @@ def main():
     torch.cuda.init()
     cfg = W.config(args.config)
     part = cfg.partition_size if args.partition is None else args.partition
-    kernel = {"auto": pa.PA_KERNEL_AUTO, "valu": pa.PA_KERNEL_VALU, "mfma": pa.PA_KERNEL_MFMA}[args.kernel]
+    kernel = {"auto": pa.PA_KERNEL_AUTO, "valu": pa.PA_KERNEL_VALU, "mfma": pa.PA_KERNEL_MFMA,
+              "stream": pa.PA_KERNEL_STREAM}[args.kernel]
     w = W.build(args.config)
     dtype = runner.TORCH_DTYPE[cfg.dtype]
     esize = W_ELEM[cfg.dtype]

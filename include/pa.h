@@ -57,9 +57,20 @@ typedef enum {
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 
-/* Decode kernel selection (pa_decode_variant).  AUTO picks the matrix-core
- * kernel for 16-bit caches with g >= 2 and the vector kernel otherwise. */
-typedef enum { PA_KERNEL_AUTO = 0, PA_KERNEL_VALU = 1, PA_KERNEL_MFMA = 2 } pa_kernel;
+/* Decode kernel selection (pa_decode_variant).
+ *   STREAM  matrix cores, every wave takes an equal share of all (sequence,
+ *           kv head) tiles, direct global->LDS tile loads; 16-bit caches
+ *   MFMA    matrix cores, one workgroup per (sequence, kv head, partition);
+ *           16-bit caches
+ *   VALU    vector ALU, one workgroup per (sequence, kv head, head group,
+ *           partition); every dtype
+ * AUTO picks STREAM for 16-bit caches and VALU for fp32. */
+typedef enum {
+  PA_KERNEL_AUTO = 0,
+  PA_KERNEL_VALU = 1,
+  PA_KERNEL_MFMA = 2,
+  PA_KERNEL_STREAM = 3
+} pa_kernel;
 
 const char* pa_last_error(void);
 const char* pa_version(void);
@@ -124,14 +135,16 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
  *                  partition partials (max, sum, unnormalised output) then a
  *                  log-sum-exp merge.
  *   workspace      device scratch of at least pa_decode_workspace_bytes(...)
- *                  bytes for the same num_seqs/num_q_heads/head_dim/
- *                  max_context_len/partition_size (may be NULL when that is 0)
+ *                  bytes for the same num_seqs/num_q_heads/num_kv_heads/
+ *                  head_dim/max_context_len/partition_size (any contents;
+ *                  256-byte aligned).  Calls that share one workspace must
+ *                  be ordered (one stream).
  * Errors: PA_ERR_INVALID (bad sizes, workspace too small, out_dtype not F32
  * or kv_dtype), PA_ERR_UNSUPPORTED (shape outside the supported set),
  * PA_ERR_HIP (launch failure).
  * ---------------------------------------------------------------------- */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t partition_size);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len, int32_t partition_size);
 
 /* The partition size pa_decode uses when passed 0 for these arguments. */
 int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
@@ -145,7 +158,8 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* pa_decode with an explicit kernel choice (for measurement): PA_KERNEL_VALU
- * supports every shape above; PA_KERNEL_MFMA needs a 16-bit kv_dtype. */
+ * supports every shape above; PA_KERNEL_MFMA and PA_KERNEL_STREAM need a
+ * 16-bit kv_dtype (STREAM ignores partition_size). */
 pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
                             const void* v_cache, pa_dtype kv_dtype, const int32_t* block_tables,
                             int32_t table_stride, const int32_t* context_lens,

@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = [
     "PAError", "lib", "LIB_PATH", "PA_F32", "PA_F16", "PA_BF16",
-    "PA_KERNEL_AUTO", "PA_KERNEL_VALU", "PA_KERNEL_MFMA",
+    "PA_KERNEL_AUTO", "PA_KERNEL_VALU", "PA_KERNEL_MFMA", "PA_KERNEL_STREAM",
     "pa_write_kv", "pa_copy_blocks", "pa_decode", "pa_decode_variant",
     "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
     "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version",
@@ -31,7 +31,7 @@ lib = ctypes.CDLL(LIB_PATH)
 
 PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_HIP, PA_ERR_UNSUPPORTED = range(5)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
-PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
+PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA, PA_KERNEL_STREAM = 0, 1, 2, 3
 _STATUS = {1: "invalid", 2: "out of blocks", 3: "hip", 4: "unsupported"}
 
 _i32, _i64, _vp, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
@@ -49,7 +49,7 @@ _sig("pa_last_error", ctypes.c_char_p)
 _sig("pa_version", ctypes.c_char_p)
 _sig("pa_write_kv", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
 _sig("pa_copy_blocks", _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
-_sig("pa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32)
+_sig("pa_decode_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32)
 _sig("pa_decode_default_partition", _i32, _i32, _i32, _i32, _i32)
 _DECODE_ARGS = [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                 _i32, _f32, _i32, _vp, _sz, _vp]
@@ -151,8 +151,11 @@ def pa_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
                               hkv, d, bs, n, torch_dtype_code(k_cache.dtype), _stream(stream)))
 
 
-def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size=0) -> int:
-    return int(lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size))
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                              partition_size=0) -> int:
+    """Bytes of decode workspace (256-byte aligned device memory, any contents)."""
+    return int(lib.pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                             partition_size))
 
 
 def pa_decode_default_partition(num_seqs, num_kv_heads, max_context_len, block_size) -> int:

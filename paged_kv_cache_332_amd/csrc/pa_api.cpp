@@ -104,21 +104,77 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
 int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                     int32_t block_size) {
   (void)num_seqs;
-  (void)num_kv_heads;
   (void)max_context_len;
   (void)block_size;
   return 512;
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || partition_size < 0)
-    return 0;
-  const int32_t part = partition_size ? partition_size : pa::kMinAutoPartition;
-  const int32_t pmax = pa::ceil_div(max_context_len, part);
+}  // extern "C"
+
+namespace pa {
+namespace {
+
+// Stream-kernel plan for a shape: slots per wave, LDS bytes, grid size.
+struct StreamPlan {
+  int gmax = 0, nslot = 0, grid = 0;
+  size_t lds = 0;
+  size_t ml_bytes = 0, acc_bytes = 0;
+  bool ok = false;
+};
+
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+StreamPlan stream_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t head_dim) {
+  StreamPlan p;
+  p.gmax = group <= 4 ? 4 : group <= 8 ? 8 : 16;
+  if (num_seqs > kStreamMaxSeqs) return p;
+  for (int ns = 4; ns >= 2; --ns) {
+    const size_t lds = stream_lds_bytes(head_dim, p.gmax, ns);
+    if (lds + kStreamStaticLds <= kStreamLdsPerCu) {
+      p.nslot = ns;
+      p.lds = lds;
+      break;
+    }
+  }
+  if (!p.nslot) return p;
+  const int per_cu = static_cast<int>(kStreamLdsPerCu / (p.lds + kStreamStaticLds));
+  p.grid = device_cus() * std::max(1, per_cu);
+  const size_t workers = size_t(p.grid) * 4;
+  p.ml_bytes = round_up(workers * 2 * p.gmax * 2 * sizeof(float));
+  p.acc_bytes = round_up(workers * 2 * p.gmax * size_t(head_dim) * sizeof(float));
+  p.ok = true;
+  return p;
+}
+
+size_t partition_ws_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t pmax) {
   if (pmax <= 1) return 0;
   const size_t rows = size_t(num_seqs) * num_q_heads * pmax;
-  return 2 * pa::round_up(rows * sizeof(float)) + pa::round_up(rows * head_dim * sizeof(float));
+  return 2 * round_up(rows * sizeof(float)) + round_up(rows * head_dim * sizeof(float));
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0 ||
+      max_context_len < 0 || partition_size < 0)
+    return 0;
+  const int32_t part = partition_size ? partition_size : pa::kMinAutoPartition;
+  const int32_t pmax = std::max(1, pa::ceil_div(max_context_len, part));
+  size_t need = pa::partition_ws_bytes(num_seqs, num_q_heads, head_dim, pmax);
+  const pa::StreamPlan sp = pa::stream_plan(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim);
+  if (sp.ok) need = std::max(need, sp.ml_bytes + sp.acc_bytes);
+  return need;
 }
 
 pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
@@ -149,10 +205,46 @@ pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const 
     return pa::fail(PA_ERR_INVALID, "%s: null pointer", fn);
   if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache))
     return pa::fail(PA_ERR_INVALID, "%s: q and caches must be 16-byte aligned", fn);
-  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA)
+  if (kernel != PA_KERNEL_AUTO && kernel != PA_KERNEL_VALU && kernel != PA_KERNEL_MFMA &&
+      kernel != PA_KERNEL_STREAM)
     return pa::fail(PA_ERR_INVALID, "%s: unknown kernel %d", fn, int(kernel));
-  if (kernel == PA_KERNEL_MFMA && kv_dtype == PA_F32)
-    return pa::fail(PA_ERR_UNSUPPORTED, "%s: the matrix-core kernel needs a 16-bit cache", fn);
+  if ((kernel == PA_KERNEL_MFMA || kernel == PA_KERNEL_STREAM) && kv_dtype == PA_F32)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: the matrix-core kernels need a 16-bit cache", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kernel == PA_KERNEL_STREAM || (kernel == PA_KERNEL_AUTO && kv_dtype != PA_F32)) {
+    const pa::StreamPlan sp = pa::stream_plan(num_seqs, num_kv_heads, group, head_dim);
+    if (sp.ok) {
+      const size_t need = sp.ml_bytes + sp.acc_bytes;
+      if (!workspace || workspace_bytes < need)
+        return pa::fail(PA_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                        workspace_bytes);
+      if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return pa::fail(PA_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+      pa::StreamArgs sa{};
+      sa.d.out = out;
+      sa.d.q = q;
+      sa.d.k = k_cache;
+      sa.d.v = v_cache;
+      sa.d.tables = block_tables;
+      sa.d.ctx = context_lens;
+      sa.d.table_stride = table_stride;
+      sa.d.max_ctx = max_context_len;
+      sa.d.num_seqs = num_seqs;
+      sa.d.num_q_heads = num_q_heads;
+      sa.d.num_kv_heads = num_kv_heads;
+      sa.d.pmax = 1;
+      sa.d.part = 0;
+      sa.d.scale_log2 = scale * 1.4426950408889634f;
+      sa.d.out_f32 = out_dtype == PA_F32;
+      char* w = static_cast<char*>(workspace);
+      sa.rec_ml = reinterpret_cast<float*>(w);
+      sa.rec_acc = reinterpret_cast<float*>(w + sp.ml_bytes);
+      return pa::hip_status(fn, pa::launch_decode_stream(sa, kv_dtype, head_dim, block_size, sp.gmax, sp.nslot,
+                                                          sp.lds, sp.grid, s));
+    }
+    if (kernel == PA_KERNEL_STREAM)
+      return pa::fail(PA_ERR_UNSUPPORTED, "%s: %d sequences do not fit the stream kernel's LDS", fn, num_seqs);
+  }
   const int32_t part = partition_size ? partition_size
                                       : pa_decode_default_partition(num_seqs, num_kv_heads, max_context_len,
                                                                     block_size);
@@ -191,9 +283,7 @@ pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const 
     a.ws_l = reinterpret_cast<float*>(w + ml);
     a.ws_acc = reinterpret_cast<float*>(w + 2 * ml);
   }
-  const bool use_mfma =
-      kernel == PA_KERNEL_MFMA || (kernel == PA_KERNEL_AUTO && kv_dtype != PA_F32 && group >= 2);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool use_mfma = kernel == PA_KERNEL_MFMA || (kernel == PA_KERNEL_AUTO && kv_dtype != PA_F32);
   hipError_t e = use_mfma ? pa::launch_decode_mfma(a, kv_dtype, head_dim, block_size, group, s)
                           : pa::launch_decode_valu(a, kv_dtype, head_dim, block_size, group, s);
   if (e != hipSuccess) return pa::hip_status(fn, e);

@@ -29,6 +29,27 @@ struct DecodeArgs {
   int32_t out_f32;               // 1: fp32 output, 0: kv dtype output
 };
 
+// Arguments of the stream kernel: the decode arguments plus its workspace.
+struct StreamArgs {
+  DecodeArgs d;
+  float* rec_ml;                 // [workers][2][gmax][2]  (max, sum) of partial states
+  float* rec_acc;                // [workers][2][gmax][D]  unnormalised partial outputs
+};
+
+// Stream kernel limits: tiles whose block ids a wave stages per pass, the
+// largest batch, and its static LDS (block ids, lengths, prefix sums).
+constexpr int kStreamTcap = 224;
+constexpr int kStreamMaxSeqs = 1024;
+// (16 KiB bounds the arrays with the compiler's alignment padding)
+constexpr size_t kStreamStaticLds = 16 * 1024;
+static_assert(4 * kStreamTcap * 8 + (2 * kStreamMaxSeqs + 1) * 4 + 64 <= kStreamStaticLds, "static LDS");
+constexpr size_t kStreamLdsPerCu = 160 * 1024;
+
+// Dynamic LDS bytes (the tile rings) of one stream workgroup.
+size_t stream_lds_bytes(int d, int gmax, int nslot);
+hipError_t launch_decode_stream(const StreamArgs& sa, int32_t dtype, int32_t d, int32_t bs, int32_t gmax,
+                                int32_t nslot, size_t lds, int32_t grid, hipStream_t stream);
+
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int32_t* slots, int32_t num_tokens, int32_t hkv, int32_t d,
                            int32_t bs, int32_t elem_bytes, hipStream_t stream);

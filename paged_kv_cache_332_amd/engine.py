@@ -72,9 +72,10 @@ class PagedKVEngine:
         st.event = ev
 
     def workspace(self, num_seqs: int, num_q_heads: int, max_ctx: int, partition_size: int = 0):
-        need = pa_decode_workspace_bytes(num_seqs, num_q_heads, self.D, max_ctx, partition_size)
+        """Decode workspace, grown on demand and reused across calls."""
+        need = pa_decode_workspace_bytes(num_seqs, num_q_heads, self.H, self.D, max_ctx, partition_size)
         if need > self._ws.numel():
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
         return self._ws
 
     # ----------------------------------------------------------- sequences

@@ -238,10 +238,17 @@ def test_write_and_copy_reject_bad_arguments():
 
 
 def test_workspace_bytes():
-    # one partition: no workspace; several: m, l and acc sections, 256-byte aligned
-    assert pa.pa_decode_workspace_bytes(64, 32, 128, 512, 512) == 0
+    def r(x):
+        return -(-x // 256) * 256
+    # stream kernel: two partial records per worker; 256 compute units x one
+    # 144 KiB workgroup of 4 waves
+    workers = 256 * 4
+    stream = r(workers * 2 * 4 * 2 * 4) + r(workers * 2 * 4 * 128 * 4)
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 512, 512) == stream
+    # partition kernels: m, l and acc sections per (sequence, q head, partition)
     rows = 64 * 32 * 8
-    expect = 2 * (-(-rows * 4 // 256) * 256) + -(-rows * 128 * 4 // 256) * 256
-    assert pa.pa_decode_workspace_bytes(64, 32, 128, 4096, 512) == expect
+    part = 2 * r(rows * 4) + r(rows * 128 * 4)
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 512) == max(stream, part)
     # auto partition sizes never need more than the 256-token bound
-    assert pa.pa_decode_workspace_bytes(64, 32, 128, 4096, 0) >= expect
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 0) >= max(stream, part)
+    assert pa.pa_decode_workspace_bytes(64, 32, 7, 128, 4096, 0) == 0   # heads not a multiple

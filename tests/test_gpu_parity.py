@@ -60,13 +60,29 @@ def check_run(w, dev, ref, tol=None, pools=True, label=""):
     return errs
 
 
+def _kernels():
+    import paged_kv_cache_332_amd as pa
+    return {"valu": pa.PA_KERNEL_VALU, "mfma": pa.PA_KERNEL_MFMA, "stream": pa.PA_KERNEL_STREAM,
+            "auto": pa.PA_KERNEL_AUTO}
+
+
+class _Lazy(dict):
+    def __missing__(self, k):
+        self.update(_kernels())
+        return dict.__getitem__(self, k)
+
+
+KERNELS = _Lazy()
+
+
 # ------------------------------------------------------------ small cases
 SMALL = []
 for dtype in ("f32", "f16", "bf16"):
     for d in (64, 128):
         for bs in (8, 16, 32):
             for g in (1, 4, 8):
-                kernels = ["valu"] + (["mfma"] if dtype != "f32" and g > 1 else [])
+                kernels = ["valu"] + (["mfma"] if dtype != "f32" and g > 1 else []) + \
+                    (["stream"] if dtype != "f32" else [])
                 for kern in kernels:
                     SMALL.append((dtype, d, bs, g, kern))
 
@@ -83,13 +99,12 @@ def test_small_shapes(dtype, d, bs, g, kern):
     part = max(128, 4 * bs)
     say("small", dtype, d, bs, g, kern, "part", part)
     ref = oracle.run_scenario(w)
-    kernel = pa.PA_KERNEL_MFMA if kern == "mfma" else pa.PA_KERNEL_VALU
-    dev = runner.run_script(w, partition_size=part, kernel=kernel)
+    dev = runner.run_script(w, partition_size=part, kernel=KERNELS[kern])
     check_run(w, dev, ref, label=f"{dtype}/D{d}/BS{bs}/g{g}/{kern}")
 
 
 @pytest.mark.parametrize("part", [64, 128, 256, 512, 1024, 0])
-@pytest.mark.parametrize("kern", ["valu", "mfma"])
+@pytest.mark.parametrize("kern", ["valu", "mfma", "stream"])
 def test_partition_sizes(part, kern):
     """Every partition size gives the oracle's result (one partition, many,
     and the merge of ragged ones)."""
@@ -100,8 +115,7 @@ def test_partition_sizes(part, kern):
                ctx=[1, 63, 64, 1000, 2049], seed=3)
     say("partition", part, kern)
     ref = oracle.run_scenario(w)
-    dev = runner.run_script(w, partition_size=part,
-                            kernel=pa.PA_KERNEL_MFMA if kern == "mfma" else pa.PA_KERNEL_VALU)
+    dev = runner.run_script(w, partition_size=part, kernel=KERNELS[kern])
     check_run(w, dev, ref, label=f"part{part}/{kern}")
 
 
@@ -165,11 +179,11 @@ def test_permutation_invariance_bitwise():
     for permute in (False, True):
         w = W.tiny(num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, dtype="bf16",
                    ctx=[5, 300, 77, 1030], seed=9, permute=permute)
-        for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA):
+        for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA, pa.PA_KERNEL_STREAM):
             say("permutation", permute, kern)
             dev = runner.run_script(w, partition_size=256, kernel=kern)
             outs.append((permute, kern, dev.decodes[-1].out.cpu(), dev.decodes[-1].tables))
-    for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA):
+    for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA, pa.PA_KERNEL_STREAM):
         a = [o for o in outs if o[1] == kern and not o[0]][0]
         b = [o for o in outs if o[1] == kern and o[0]][0]
         assert not np.array_equal(a[3], b[3])
@@ -228,7 +242,7 @@ def test_zero_context_gives_zero_rows():
     eng.add_seq(1, rows, rows, 40)
     eng.add_seq(2, None, None, 0)
     q = torch.randn(3, 8, 128, device="cuda").to(torch.bfloat16)
-    for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA):
+    for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA, pa.PA_KERNEL_STREAM):
         out = eng.decode([0, 1, 2], q, kernel=kern)
         torch.cuda.synchronize()
         assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
@@ -260,7 +274,42 @@ def test_large_logits_stay_finite():
                ctx=[40, 600, 1500], seed=4)
     w.q_sets = [W.round_to_dtype(w.q_sets[0] * 64.0, "bf16")]
     ref = oracle.run_scenario(w)
-    for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA):
+    for kern in (pa.PA_KERNEL_VALU, pa.PA_KERNEL_MFMA, pa.PA_KERNEL_STREAM):
         say("large logits", kern)
         dev = runner.run_script(w, partition_size=256, kernel=kern)
         check_run(w, dev, ref, label=f"large logits {kern}")
+
+
+@pytest.mark.parametrize("case", ["tiny_ctx", "many_seqs", "one_seq", "mixed_zero"])
+def test_stream_work_split(case):
+    """The stream kernel splits the tile list of all (sequence, kv head)
+    items evenly over its waves: fewer tiles than waves, many one-token
+    sequences, one long sequence cut over many waves, empty sequences mixed
+    in.  Every output row matches the oracle; a second call on the same
+    workspace (counters left at zero) gives bit-identical results."""
+    pa, runner = _pa()
+    if case == "tiny_ctx":
+        kw = dict(ctx=[1, 2, 3, 5, 8, 13, 21], num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16)
+    elif case == "many_seqs":
+        kw = dict(ctx=list(np.random.default_rng(11).integers(1, 40, size=300)), num_q_heads=4, num_kv_heads=4,
+                  head_dim=64, block_size=8)
+    elif case == "one_seq":
+        kw = dict(ctx=[70000], num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=32)
+    else:
+        kw = dict(ctx=[0, 600, 0, 0, 33, 4000, 0], num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16)
+    w = W.tiny(num_seqs=len(kw["ctx"]), dtype="bf16", seed=21, **kw)
+    if case == "mixed_zero":
+        # empty sequences are added with no tokens, skip the append and are decoded
+        ctx = [int(x) for x in kw["ctx"]]
+        w.ops = [w.ops[0]] + [("add_seq", i, max(n - 1, 0), True) for i, n in enumerate(ctx)] + \
+            [("append", [i for i, n in enumerate(ctx) if n > 0]), ("decode", list(range(len(ctx))), 0)]
+    say("stream split", case)
+    ref = oracle.run_scenario(w)
+    dev = runner.run_script(w, kernel=pa.PA_KERNEL_STREAM)
+    check_run(w, dev, ref, label=f"stream {case}")
+    eng = dev.engine
+    seqs = dev.decodes[-1].seqs
+    q = dev.q_dev[dev.decodes[-1].q_index][torch.tensor(seqs, device="cuda")].contiguous()
+    again = eng.decode(seqs, q, kernel=pa.PA_KERNEL_STREAM)
+    torch.cuda.synchronize()
+    assert torch.equal(again, dev.decodes[-1].out)
