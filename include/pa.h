@@ -169,6 +169,22 @@ pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const 
                             void* workspace, size_t workspace_bytes, void* stream,
                             pa_kernel kernel);
 
+/* pa_decode in its two phases, for callers that time or schedule them apart:
+ * phase 1 is the pass over the K/V tiles (it writes every output row that one
+ * work item covers and the partial (max, sum, unnormalised output) of the
+ * others), phase 2 the log-sum-exp merge of those partials; phase 3 runs both
+ * (= pa_decode_variant).  Phase 2 must follow phase 1 of the same arguments
+ * and workspace on the same stream. */
+typedef enum { PA_PHASE_PASS = 1, PA_PHASE_MERGE = 2, PA_PHASE_ALL = 3 } pa_phase;
+
+pa_status pa_decode_phase(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                          const void* v_cache, pa_dtype kv_dtype, const int32_t* block_tables,
+                          int32_t table_stride, const int32_t* context_lens, int32_t max_context_len,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
+                          void* workspace, size_t workspace_bytes, void* stream, pa_kernel kernel,
+                          int32_t phase);
+
 /* ------------------------------------------------------------------------
  * Host block manager: the shared pool of interchangeable blocks, per-block
  * sharer counts and per-sequence block tables ([VM] §The fix borrowed from
@@ -228,6 +244,38 @@ int32_t pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap);
 /* out[5] = {free blocks, referenced blocks, shared blocks (count > 1),
  *           copy-on-write pairs issued so far, slack tokens in last blocks} */
 pa_status pa_bm_stats(const pa_bm* bm, int64_t* out);
+
+/* ------------------------------------------------------------------------
+ * pa_step — one decode step of a batch, host and device parts in one call:
+ *   1. pa_bm_append_slots: the new token of each of seqs[0..n) gets a slot
+ *      (a fresh block when the last one is full; a copy of a shared last
+ *      block first, [VM] §Sharing comes almost for free);
+ *   2. pa_bm_export of the grown tables and context lengths;
+ *   3. the step record, laid out in int32 words as
+ *      [slots n | copy pairs 2n | context lengths n | tables n * table_stride]
+ *      (rounded up to a multiple of 4 words), goes from stage_host (pinned
+ *      host memory, 16-byte aligned) to stage_dev (device memory): when the
+ *      runtime maps stage_host into the device's address space, a kernel on
+ *      the stream copies it and writes the new tokens in the same launch,
+ *      otherwise a host-to-device copy precedes pa_write_kv;
+ *   4. pa_copy_blocks of the copy pairs and the KV write of k_new/v_new
+ *      ([n][num_kv_heads][head_dim], device) into the new slots;
+ *   5. pa_decode_phase PASS then MERGE of q ([n][num_q_heads][head_dim])
+ *      into out over the exported tables; pass_begin / pass_end (hipEvent_t
+ *      or NULL) are recorded on the stream around the pass.
+ * Everything is enqueued on `stream`.  stage_host must not be rewritten until
+ * this call's kernels have read it (keep a ring of records guarded by
+ * events); both stage buffers hold the rounded record.
+ * *max_ctx_out (may be NULL) receives the longest context.  Errors from the
+ * manager leave it unchanged and launch nothing; a sequence whose next token
+ * would not fit table_stride blocks is rejected before any change.
+ * ---------------------------------------------------------------------- */
+pa_status pa_step(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* stage_host, int32_t* stage_dev,
+                  int32_t table_stride, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                  const void* q, void* out, pa_dtype out_dtype, pa_dtype kv_dtype, int32_t num_q_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                  int32_t partition_size, void* workspace, size_t workspace_bytes, pa_kernel kernel,
+                  void* stream, void* pass_begin, void* pass_end, int32_t* max_ctx_out);
 
 /* Debug validator over HOST copies of the decode inputs: every table entry a
  * sequence reads is in [0, num_blocks) and ceil(ctx/BS) <= stride.  Returns

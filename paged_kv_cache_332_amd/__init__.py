@@ -19,9 +19,10 @@ import numpy as np
 __all__ = [
     "PAError", "lib", "LIB_PATH", "PA_F32", "PA_F16", "PA_BF16",
     "PA_KERNEL_AUTO", "PA_KERNEL_VALU", "PA_KERNEL_MFMA", "PA_KERNEL_STREAM",
-    "pa_write_kv", "pa_copy_blocks", "pa_decode", "pa_decode_variant",
+    "pa_write_kv", "pa_copy_blocks", "pa_decode", "pa_decode_variant", "pa_decode_phase",
+    "PA_PHASE_PASS", "PA_PHASE_MERGE", "PA_PHASE_ALL",
     "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
-    "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version",
+    "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version", "pa_step",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -32,6 +33,7 @@ lib = ctypes.CDLL(LIB_PATH)
 PA_OK, PA_ERR_INVALID, PA_ERR_OOM, PA_ERR_HIP, PA_ERR_UNSUPPORTED = range(5)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA, PA_KERNEL_STREAM = 0, 1, 2, 3
+PA_PHASE_PASS, PA_PHASE_MERGE, PA_PHASE_ALL = 1, 2, 3
 _STATUS = {1: "invalid", 2: "out of blocks", 3: "hip", 4: "unsupported"}
 
 _i32, _i64, _vp, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
@@ -55,6 +57,7 @@ _DECODE_ARGS = [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32
                 _i32, _f32, _i32, _vp, _sz, _vp]
 _sig("pa_decode", _i32, *_DECODE_ARGS)
 _sig("pa_decode_variant", _i32, *_DECODE_ARGS, _i32)
+_sig("pa_decode_phase", _i32, *_DECODE_ARGS, _i32, _i32)
 _sig("pa_bm_create", _vp, _i32, _i32, _pi32)
 _sig("pa_bm_destroy", None, _vp)
 _sig("pa_bm_add_seq", _i32, _vp, _i64, _i32, _pi32)
@@ -69,6 +72,8 @@ _sig("pa_bm_num_seqs", _i32, _vp)
 _sig("pa_bm_free_list", _i32, _vp, _pi32, _i32)
 _sig("pa_bm_stats", _i32, _vp, _pi64)
 _sig("pa_check_tables", _i32, _pi32, _i32, _i32, _pi32, _i32, _i32)
+_sig("pa_step", _i32, _vp, _pi64, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+     _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp, _vp, _pi32)
 
 
 class PAError(RuntimeError):
@@ -164,7 +169,7 @@ def pa_decode_default_partition(num_seqs, num_kv_heads, max_context_len, block_s
 
 def pa_decode_variant(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
                       scale: float, partition_size: int = 0, workspace=None, stream=None,
-                      kernel: int = PA_KERNEL_AUTO) -> None:
+                      kernel: int = PA_KERNEL_AUTO, phase: int = PA_PHASE_ALL) -> None:
     """q/out [B][Hq][D]; block_tables int32 [B][stride]; context_lens int32 [B]."""
     n, hkv, d, bs = _pool_dims(k_cache, v_cache)
     b, hq, dq = q.shape
@@ -173,17 +178,40 @@ def pa_decode_variant(out, q, k_cache, v_cache, block_tables, context_lens, max_
     assert context_lens.is_contiguous() and context_lens.numel() == b
     ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(),
                                                           workspace.numel() * workspace.element_size())
-    _check(lib.pa_decode_variant(out.data_ptr(), torch_dtype_code(out.dtype), q.data_ptr(), k_cache.data_ptr(),
-                                 v_cache.data_ptr(), torch_dtype_code(k_cache.dtype), block_tables.data_ptr(),
-                                 int(block_tables.shape[1]), context_lens.data_ptr(), int(max_context_len),
-                                 b, hq, hkv, d, bs, n, float(scale), int(partition_size), ws_ptr, ws_bytes,
-                                 _stream(stream), int(kernel)))
+    _check(lib.pa_decode_phase(out.data_ptr(), torch_dtype_code(out.dtype), q.data_ptr(), k_cache.data_ptr(),
+                               v_cache.data_ptr(), torch_dtype_code(k_cache.dtype), block_tables.data_ptr(),
+                               int(block_tables.shape[1]), context_lens.data_ptr(), int(max_context_len),
+                               b, hq, hkv, d, bs, n, float(scale), int(partition_size), ws_ptr, ws_bytes,
+                               _stream(stream), int(kernel), int(phase)))
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int, scale: float,
               partition_size: int = 0, workspace=None, stream=None) -> None:
     pa_decode_variant(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                       partition_size, workspace, stream, PA_KERNEL_AUTO)
+
+
+def pa_step(bm: "BlockManager", seqs_i64: np.ndarray, stage_host, stage_dev, table_stride: int, k_cache, v_cache,
+            k_new, v_new, q, out, scale: float, partition_size: int = 0, workspace=None, kernel: int = PA_KERNEL_AUTO,
+            stream=None, pass_events=None) -> int:
+    """One decode step (see pa_step in pa.h); returns the longest context.
+    ``seqs_i64`` is a contiguous int64 array; stage_host/stage_dev are int32
+    tensors (pinned / device) of at least n * (4 + table_stride) words;
+    ``pass_events`` = (begin, end) torch CUDA events already created (recorded
+    once), recorded around the decode pass."""
+    n_, hkv, d, bs = _pool_dims(k_cache, v_cache)
+    n = int(seqs_i64.shape[0])
+    hq = int(q.shape[1])
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(),
+                                                          workspace.numel() * workspace.element_size())
+    ev0, ev1 = (None, None) if pass_events is None else (pass_events[0].cuda_event, pass_events[1].cuda_event)
+    max_ctx = ctypes.c_int32(0)
+    _check(lib.pa_step(bm._h, seqs_i64.ctypes.data_as(_pi64), n, stage_host.data_ptr(), stage_dev.data_ptr(),
+                       int(table_stride), k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                       q.data_ptr(), out.data_ptr(), torch_dtype_code(out.dtype), torch_dtype_code(k_cache.dtype),
+                       hq, hkv, d, bs, n_, float(scale), int(partition_size), ws_ptr, ws_bytes, int(kernel),
+                       _stream(stream), ev0, ev1, ctypes.byref(max_ctx)))
+    return int(max_ctx.value)
 
 
 def pa_check_tables(tables: np.ndarray, ctx_lens: np.ndarray, block_size: int, num_blocks: int) -> None:

@@ -566,7 +566,7 @@ size_t stream_lds_bytes(int d, int gmax, int nslot) {
 }
 
 template <class T, int D, int BS, int GMAX, int NSLOT>
-static hipError_t launch_s(const StreamArgs& sa, size_t lds, int grid, hipStream_t stream) {
+static hipError_t launch_s(const StreamArgs& sa, size_t lds, int grid, int phases, hipStream_t stream) {
   auto kern = decode_stream_kernel<T, D, BS, GMAX, NSLOT>;
   // the dynamic size of an instantiation depends only on its template
   // arguments; allow it once
@@ -577,9 +577,12 @@ static hipError_t launch_s(const StreamArgs& sa, size_t lds, int grid, hipStream
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, sa);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (phases & 1) {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, sa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(phases & 2)) return hipSuccess;
   const int64_t items = int64_t(sa.d.num_seqs) * sa.d.num_kv_heads;
   hipLaunchKernelGGL((stream_merge_kernel<T, D, GMAX>), dim3(static_cast<uint32_t>(items)), dim3(64), 0, stream, sa,
                      grid * 4);
@@ -587,51 +590,52 @@ static hipError_t launch_s(const StreamArgs& sa, size_t lds, int grid, hipStream
 }
 
 template <class T, int D, int BS, int GMAX>
-static hipError_t launch_n(const StreamArgs& sa, int nslot, size_t lds, int grid, hipStream_t stream) {
+static hipError_t launch_n(const StreamArgs& sa, int nslot, size_t lds, int grid, int phases, hipStream_t stream) {
   switch (nslot) {
-    case 2: return launch_s<T, D, BS, GMAX, 2>(sa, lds, grid, stream);
-    case 3: return launch_s<T, D, BS, GMAX, 3>(sa, lds, grid, stream);
-    case 4: return launch_s<T, D, BS, GMAX, 4>(sa, lds, grid, stream);
+    case 2: return launch_s<T, D, BS, GMAX, 2>(sa, lds, grid, phases, stream);
+    case 3: return launch_s<T, D, BS, GMAX, 3>(sa, lds, grid, phases, stream);
+    case 4: return launch_s<T, D, BS, GMAX, 4>(sa, lds, grid, phases, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <class T, int D, int BS>
-static hipError_t launch_g(const StreamArgs& sa, int gmax, int nslot, size_t lds, int grid, hipStream_t stream) {
+static hipError_t launch_g(const StreamArgs& sa, int gmax, int nslot, size_t lds, int grid, int phases,
+                           hipStream_t stream) {
   switch (gmax) {
-    case 4: return launch_n<T, D, BS, 4>(sa, nslot, lds, grid, stream);
-    case 8: return launch_n<T, D, BS, 8>(sa, nslot, lds, grid, stream);
-    case 16: return launch_n<T, D, BS, 16>(sa, nslot, lds, grid, stream);
+    case 4: return launch_n<T, D, BS, 4>(sa, nslot, lds, grid, phases, stream);
+    case 8: return launch_n<T, D, BS, 8>(sa, nslot, lds, grid, phases, stream);
+    case 16: return launch_n<T, D, BS, 16>(sa, nslot, lds, grid, phases, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <class T, int D>
-static hipError_t launch_b(const StreamArgs& sa, int bs, int gmax, int nslot, size_t lds, int grid,
+static hipError_t launch_b(const StreamArgs& sa, int bs, int gmax, int nslot, size_t lds, int grid, int phases,
                            hipStream_t stream) {
   switch (bs) {
-    case 8: return launch_g<T, D, 8>(sa, gmax, nslot, lds, grid, stream);
-    case 16: return launch_g<T, D, 16>(sa, gmax, nslot, lds, grid, stream);
-    case 32: return launch_g<T, D, 32>(sa, gmax, nslot, lds, grid, stream);
+    case 8: return launch_g<T, D, 8>(sa, gmax, nslot, lds, grid, phases, stream);
+    case 16: return launch_g<T, D, 16>(sa, gmax, nslot, lds, grid, phases, stream);
+    case 32: return launch_g<T, D, 32>(sa, gmax, nslot, lds, grid, phases, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <class T>
 static hipError_t launch_d(const StreamArgs& sa, int d, int bs, int gmax, int nslot, size_t lds, int grid,
-                           hipStream_t stream) {
+                           int phases, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_b<T, 64>(sa, bs, gmax, nslot, lds, grid, stream);
-    case 128: return launch_b<T, 128>(sa, bs, gmax, nslot, lds, grid, stream);
+    case 64: return launch_b<T, 64>(sa, bs, gmax, nslot, lds, grid, phases, stream);
+    case 128: return launch_b<T, 128>(sa, bs, gmax, nslot, lds, grid, phases, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode_stream(const StreamArgs& sa, int32_t dtype, int32_t d, int32_t bs, int32_t gmax,
-                                int32_t nslot, size_t lds, int32_t grid, hipStream_t stream) {
+                                int32_t nslot, size_t lds, int32_t grid, int32_t phases, hipStream_t stream) {
   switch (dtype) {
-    case 1: return launch_d<F16>(sa, d, bs, gmax, nslot, lds, grid, stream);
-    case 2: return launch_d<BF16>(sa, d, bs, gmax, nslot, lds, grid, stream);
+    case 1: return launch_d<F16>(sa, d, bs, gmax, nslot, lds, grid, phases, stream);
+    case 2: return launch_d<BF16>(sa, d, bs, gmax, nslot, lds, grid, phases, stream);
     default: return hipErrorInvalidValue;
   }
 }

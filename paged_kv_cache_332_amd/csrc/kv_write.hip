@@ -6,6 +6,8 @@
 // block it is about to write (§Sharing comes almost for free).  Both are
 // plain data movement, bound by HBM: the kernels read each source byte once
 // and write each destination byte once.
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -54,6 +56,64 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* __restrict__ kc
   const u32x4* from = base + (src * hkv + h) * tile_chunks;
   u32x4* to = base + (dst * hkv + h) * tile_chunks;
   for (int32_t i = threadIdx.x; i < tile_chunks; i += blockDim.x) to[i] = from[i];
+}
+
+// One decode step's record and KV write in one launch, on the compute queue
+// (no copy engine, so the kernels that follow wait for no cross-engine
+// signal).  Workgroups [0, n) write token blockIdx.x like write_kv_kernel,
+// taking its slot from the record in pinned host memory; the other
+// workgroups copy the record (`words` int32) from host to device memory in
+// 16-byte units.
+template <typename Bits>
+__global__ __launch_bounds__(256) void step_stage_kernel(const int32_t* __restrict__ rec_host,
+                                                         int32_t* __restrict__ rec_dev, int64_t words, int32_t n,
+                                                         u32x4* __restrict__ kc, Bits* __restrict__ vc,
+                                                         const u32x4* __restrict__ kn, const Bits* __restrict__ vn,
+                                                         int32_t hkv, int32_t d, int32_t bs) {
+  if (blockIdx.x >= n) {
+    const int64_t units = words / 4;                  // words is a multiple of 4
+    const u32x4* src = reinterpret_cast<const u32x4*>(rec_host);
+    u32x4* dst = reinterpret_cast<u32x4*>(rec_dev);
+    for (int64_t i = int64_t(blockIdx.x - n) * blockDim.x + threadIdx.x; i < units;
+         i += int64_t(gridDim.x - n) * blockDim.x)
+      dst[i] = src[i];
+    return;
+  }
+  const int64_t t = blockIdx.x;
+  const int32_t s = rec_host[t];
+  if (s < 0) return;
+  const int64_t blk = s / bs;
+  const int32_t off = s % bs;
+  const int32_t x = 16 / static_cast<int32_t>(sizeof(Bits));
+  const int32_t cpr = d / x;
+  const int32_t nk = hkv * cpr;
+  for (int32_t i = threadIdx.x; i < nk; i += blockDim.x) {
+    const int32_t h = i / cpr, c = i % cpr;
+    kc[((blk * hkv + h) * cpr + c) * bs + off] = kn[t * nk + i];
+  }
+  const int32_t nv = hkv * d;
+  for (int32_t i = threadIdx.x; i < nv; i += blockDim.x) {
+    const int32_t h = i / d, e = i % d;
+    vc[((blk * hkv + h) * d + e) * bs + off] = vn[t * nv + i];
+  }
+}
+
+hipError_t launch_step_stage(const int32_t* rec_host, int32_t* rec_dev, int64_t words, int32_t n, void* k_cache,
+                             void* v_cache, const void* k_new, const void* v_new, int32_t hkv, int32_t d,
+                             int32_t bs, int32_t elem_bytes, hipStream_t stream) {
+  const int64_t units = words / 4;
+  const int32_t copiers = static_cast<int32_t>(std::min<int64_t>(64, std::max<int64_t>(1, (units + 255) / 256)));
+  dim3 grid(n + copiers), block(256);
+  if (elem_bytes == 2) {
+    hipLaunchKernelGGL(step_stage_kernel<uint16_t>, grid, block, 0, stream, rec_host, rec_dev, words, n,
+                       static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       static_cast<const u32x4*>(k_new), static_cast<const uint16_t*>(v_new), hkv, d, bs);
+  } else {
+    hipLaunchKernelGGL(step_stage_kernel<uint32_t>, grid, block, 0, stream, rec_host, rec_dev, words, n,
+                       static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache),
+                       static_cast<const u32x4*>(k_new), static_cast<const uint32_t*>(v_new), hkv, d, bs);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,

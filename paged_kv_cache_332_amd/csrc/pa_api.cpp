@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -123,11 +124,18 @@ struct StreamPlan {
 };
 
 
+// Compute units of the current device, looked up once per device.
 int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return 256;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    if (const int c = cache[dev].load(std::memory_order_relaxed)) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  if (dev < kMaxDevices) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
@@ -177,13 +185,21 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return need;
 }
 
-pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
-                            const void* v_cache, pa_dtype kv_dtype, const int32_t* block_tables,
-                            int32_t table_stride, const int32_t* context_lens, int32_t max_context_len,
-                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                            int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
-                            void* workspace, size_t workspace_bytes, void* stream, pa_kernel kernel) {
+}  // extern "C"
+
+namespace pa {
+namespace {
+
+// Validates, picks the kernel and launches the phases asked for (bit 0: the
+// pass over the K/V tiles, bit 1: the merge of split items).
+pa_status decode_impl(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
+                      pa_dtype kv_dtype, const int32_t* block_tables, int32_t table_stride,
+                      const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream,
+                      pa_kernel kernel, int phases) {
   const char* fn = "pa_decode";
+  if (phases < 1 || phases > 3) return pa::fail(PA_ERR_INVALID, "%s: phases %d not in 1..3", fn, phases);
   if (pa_status st = pa::check_cache_shape(fn, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype))
     return st;
   if (out_dtype != PA_F32 && out_dtype != kv_dtype)
@@ -240,7 +256,7 @@ pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const 
       sa.rec_ml = reinterpret_cast<float*>(w);
       sa.rec_acc = reinterpret_cast<float*>(w + sp.ml_bytes);
       return pa::hip_status(fn, pa::launch_decode_stream(sa, kv_dtype, head_dim, block_size, sp.gmax, sp.nslot,
-                                                          sp.lds, sp.grid, s));
+                                                          sp.lds, sp.grid, phases, s));
     }
     if (kernel == PA_KERNEL_STREAM)
       return pa::fail(PA_ERR_UNSUPPORTED, "%s: %d sequences do not fit the stream kernel's LDS", fn, num_seqs);
@@ -284,14 +300,43 @@ pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const 
     a.ws_acc = reinterpret_cast<float*>(w + 2 * ml);
   }
   const bool use_mfma = kernel == PA_KERNEL_MFMA || (kernel == PA_KERNEL_AUTO && kv_dtype != PA_F32);
-  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, kv_dtype, head_dim, block_size, group, s)
-                          : pa::launch_decode_valu(a, kv_dtype, head_dim, block_size, group, s);
-  if (e != hipSuccess) return pa::hip_status(fn, e);
-  if (pmax > 1) {
-    e = pa::launch_merge(a, kv_dtype, head_dim, s);
+  if (phases & 1) {
+    hipError_t e = use_mfma ? pa::launch_decode_mfma(a, kv_dtype, head_dim, block_size, group, s)
+                            : pa::launch_decode_valu(a, kv_dtype, head_dim, block_size, group, s);
+    if (e != hipSuccess) return pa::hip_status(fn, e);
+  }
+  if ((phases & 2) && pmax > 1) {
+    hipError_t e = pa::launch_merge(a, kv_dtype, head_dim, s);
     if (e != hipSuccess) return pa::hip_status(fn, e);
   }
   return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                            const void* v_cache, pa_dtype kv_dtype, const int32_t* block_tables,
+                            int32_t table_stride, const int32_t* context_lens, int32_t max_context_len,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes, void* stream, pa_kernel kernel) {
+  return pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, table_stride, context_lens,
+                         max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                         scale, partition_size, workspace, workspace_bytes, stream, kernel, 3);
+}
+
+pa_status pa_decode_phase(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
+                          pa_dtype kv_dtype, const int32_t* block_tables, int32_t table_stride,
+                          const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, float scale, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, void* stream, pa_kernel kernel, int32_t phase) {
+  return pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, table_stride, context_lens,
+                         max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                         scale, partition_size, workspace, workspace_bytes, stream, kernel, phase);
 }
 
 pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,

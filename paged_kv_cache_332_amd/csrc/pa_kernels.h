@@ -47,12 +47,19 @@ constexpr size_t kStreamLdsPerCu = 160 * 1024;
 
 // Dynamic LDS bytes (the tile rings) of one stream workgroup.
 size_t stream_lds_bytes(int d, int gmax, int nslot);
+// phases: bit 0 the stream pass, bit 1 the merge of cut items
 hipError_t launch_decode_stream(const StreamArgs& sa, int32_t dtype, int32_t d, int32_t bs, int32_t gmax,
-                                int32_t nslot, size_t lds, int32_t grid, hipStream_t stream);
+                                int32_t nslot, size_t lds, int32_t grid, int32_t phases, hipStream_t stream);
 
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int32_t* slots, int32_t num_tokens, int32_t hkv, int32_t d,
                            int32_t bs, int32_t elem_bytes, hipStream_t stream);
+
+// Step record copy (pinned host -> device, `words` a multiple of 4) fused with
+// the KV write of its n tokens (slots = the record's first n words).
+hipError_t launch_step_stage(const int32_t* rec_host, int32_t* rec_dev, int64_t words, int32_t n, void* k_cache,
+                             void* v_cache, const void* k_new, const void* v_new, int32_t hkv, int32_t d,
+                             int32_t bs, int32_t elem_bytes, hipStream_t stream);
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                               int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,

@@ -17,27 +17,36 @@ import numpy as np
 import torch
 
 from . import (PA_KERNEL_AUTO, BlockManager, alloc_cache, pa_copy_blocks, pa_decode_variant,
-               pa_decode_workspace_bytes, pa_write_kv)
+               pa_decode_workspace_bytes, pa_step, pa_write_kv)
 
 __all__ = ["PagedKVEngine"]
 
 
 class _Staging:
-    """Pinned host buffers + device mirrors for one step's bookkeeping."""
+    """One step's bookkeeping in a single pinned host buffer and its device
+    mirror, laid out [slots B | copy pairs 2B | context lengths B | tables
+    B x stride], so a whole step needs one host-to-device copy."""
 
     def __init__(self, max_seqs: int, stride: int, device):
         self.stride = stride
-        pin = dict(dtype=torch.int32, pin_memory=True)
-        self.h_tables = torch.empty((max_seqs, stride), **pin)
-        self.h_ctx = torch.empty(max_seqs, **pin)
-        self.h_slots = torch.empty(max_seqs, **pin)
-        self.h_pairs = torch.empty((max_seqs, 2), **pin)
-        dev = dict(dtype=torch.int32, device=device)
-        self.d_tables = torch.empty((max_seqs, stride), **dev)
-        self.d_ctx = torch.empty(max_seqs, **dev)
-        self.d_slots = torch.empty(max_seqs, **dev)
-        self.d_pairs = torch.empty((max_seqs, 2), **dev)
+        self.max_seqs = max_seqs
+        words = max_seqs * (4 + stride) + 4      # the record is rounded up to 16 bytes
+        self.h = torch.empty(words, dtype=torch.int32, pin_memory=True)
+        self.d = torch.empty(words, dtype=torch.int32, device=device)
+        self.h_slots, self.h_pairs, self.h_ctx, self.h_tables = self._views(self.h, max_seqs)
+        self.d_slots, self.d_pairs, self.d_ctx, self.d_tables = self._views(self.d, max_seqs)
         self.event: Optional[torch.cuda.Event] = None
+
+    def _views(self, t, b):
+        s = self.stride
+        return (t[:b], t[b:3 * b].view(b, 2), t[3 * b:4 * b], t[4 * b:4 * b + b * s].view(b, s))
+
+    def packed(self, n):
+        """Views of an n-sequence step, packed at the front of both buffers:
+        (host, device) x (slots, pairs, ctx, tables)."""
+        h = self._views(self.h, n)
+        d = self._views(self.d, n)
+        return h, d, 4 * n + n * self.stride
 
     def wait(self):
         if self.event is not None:
@@ -67,15 +76,18 @@ class PagedKVEngine:
         return st
 
     def _record(self, st: _Staging, stream):
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        st.event = ev
+        if st.event is None:
+            st.event = torch.cuda.Event()
+        st.event.record(stream)
 
     def workspace(self, num_seqs: int, num_q_heads: int, max_ctx: int, partition_size: int = 0):
         """Decode workspace, grown on demand and reused across calls."""
-        need = pa_decode_workspace_bytes(num_seqs, num_q_heads, self.H, self.D, max_ctx, partition_size)
-        if need > self._ws.numel():
-            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        key = (num_seqs, num_q_heads, max_ctx, partition_size)
+        if getattr(self, "_ws_key", None) != key:
+            need = pa_decode_workspace_bytes(num_seqs, num_q_heads, self.H, self.D, max_ctx, partition_size)
+            if need > self._ws.numel():
+                self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            self._ws_key = key
         return self._ws
 
     # ----------------------------------------------------------- sequences
@@ -136,7 +148,29 @@ class PagedKVEngine:
         self._record(st, stream)
         return out
 
-    def step(self, seqs, k_new, v_new, q, out=None, **kw):
-        """One decode step: append the new token of every sequence, then attend."""
-        self.append(seqs, k_new, v_new, stream=kw.get("stream"))
-        return self.decode(seqs, q, out=out, **kw)
+    def step(self, seqs, k_new, v_new, q, out=None, out_dtype=torch.float32, partition_size: int = 0,
+             kernel: int = PA_KERNEL_AUTO, stream=None, pass_events=None) -> torch.Tensor:
+        """One decode step for the listed sequences, in one native call
+        (pa_step): the block manager gives each its new token's slot
+        (copy-on-write pairs first), the slots, pairs, context lengths and
+        block tables go to the device in one copy, then pa_copy_blocks,
+        pa_write_kv and the decode pass and merge run on the stream.
+        ``pass_events`` = (start, end) CUDA events (already created) recorded
+        around the decode pass."""
+        stream = stream or torch.cuda.current_stream()
+        n = len(seqs)
+        st = self._next()
+        key = tuple(seqs)
+        if getattr(self, "_seq_key", None) != key:
+            self._seq_key, self._seq_arr = key, np.ascontiguousarray(seqs, dtype=np.int64)
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=self.device)
+        # the workspace is sized for the longest context the tables can hold
+        ws = self.workspace(n, q.shape[1], self.stride * self.BS, partition_size)
+        max_ctx = pa_step(self.bm, self._seq_arr, st.h, st.d, self.stride, self.k_cache, self.v_cache, k_new, v_new,
+                          q, out, 1.0 / float(self.D) ** 0.5, partition_size, ws if ws.numel() else None, kernel,
+                          stream, pass_events)
+        (hs, hp, hc, ht), _, _ = st.packed(n)
+        self.last_tables, self.last_ctx, self.last_max_ctx = ht.numpy(), hc.numpy(), max_ctx
+        self._record(st, stream)
+        return out

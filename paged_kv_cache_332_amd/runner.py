@@ -53,9 +53,11 @@ class DeviceRun:
 
 def run_script(w, device="cuda", partition_size: int = 0, kernel: int = PA_KERNEL_AUTO,
                out_dtype=torch.float32, poison: bool = True, decode: bool = True,
-               extra_context: int = 0) -> DeviceRun:
+               extra_context: int = 0, use_step: bool = False) -> DeviceRun:
     """Replay ``w.ops``; ``extra_context`` widens the table stride for tokens
-    appended after the script."""
+    appended after the script.  With ``use_step`` an append directly followed
+    by a decode of the same sequences runs as one engine step (one host to
+    device copy), the way the benchmark drives it."""
     cfg = w.cfg
     dtype = TORCH_DTYPE[cfg.dtype]
     dev = torch.device(device)
@@ -64,8 +66,31 @@ def run_script(w, device="cuda", partition_size: int = 0, kernel: int = PA_KERNE
     q_dev = [upload_rows(q, dtype, dev) for q in w.q_sets]
     run: Optional[DeviceRun] = None
     max_ctx = int(np.max(w.ctx)) + extra_context
-    for op in w.ops:
+    ops = list(w.ops)
+    i = 0
+    while i < len(ops):
+        op = ops[i]
+        i += 1
         kind = op[0]
+        if (use_step and decode and kind == "append" and i < len(ops) and ops[i][0] == "decode"
+                and list(ops[i][1]) == list(op[1])):
+            seqs, qi = op[1], ops[i][2]
+            i += 1
+            pos = np.array([run.engine.bm.seq_len(s) for s in seqs], dtype=np.int64)
+            rows = np.array([w.row_of(s, np.array([p]))[0] for s, p in zip(seqs, pos)], dtype=np.int64)
+            idx = torch.from_numpy(rows).to(dev)
+            q = q_dev[qi][torch.tensor(seqs, device=dev)].contiguous()
+            before = run.engine.bm.stats()[3]
+            out = run.engine.step(seqs, k_dev[idx], v_dev[idx], q, out_dtype=out_dtype,
+                                  partition_size=partition_size, kernel=kernel)
+            ncow = run.engine.bm.stats()[3] - before
+            st = run.engine._ring[(run.engine._ri - 1) % len(run.engine._ring)]
+            (hs, hp, _, _), _, _ = st.packed(len(seqs))
+            run.appends.append({"seqs": list(seqs), "pos": pos, "slots": hs.numpy().copy(),
+                                "pairs": [tuple(int(x) for x in p) for p in hp.numpy()[:ncow]]})
+            run.decodes.append(DeviceDecode(list(seqs), qi, run.engine.last_tables.copy(),
+                                            run.engine.last_ctx.copy(), out))
+            continue
         if kind == "create":
             eng = PagedKVEngine(op[1], cfg.num_kv_heads, cfg.head_dim, cfg.block_size, dtype, op[2],
                                 device=dev, poison=poison, max_seqs=cfg.num_seqs, max_context=max_ctx)

@@ -134,12 +134,13 @@ def _config(name):
                                   "c4a_prefix_share", "c4b_prefix_cow", "c3_mha_f16_churn", "c5_long_splitk"])
 def test_config_parity(name):
     """The five configurations at full size, in the launch configuration the
-    benchmark times (library-chosen partition size, or 512 tokens for the
-    long-context split-K configuration): every output row and every pool byte."""
+    benchmark times (engine steps: one packed host-to-device copy, copy-on-
+    write copies, KV write, decode pass and merge): every output row and every
+    pool byte."""
     pa, runner = _pa()
     w, ref = _config(name)
     say("device replay", name)
-    dev = runner.run_script(w, partition_size=w.cfg.partition_size)
+    dev = runner.run_script(w, partition_size=w.cfg.partition_size, use_step=True)
     errs = check_run(w, dev, ref, label=name)
     say(name, "max abs errors", errs)
     if name == "c4a_prefix_share":
