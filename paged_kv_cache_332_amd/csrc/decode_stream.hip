@@ -484,7 +484,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
 // from the context lengths, and if the item spans workers wlo < whi it
 // combines their partial states
 //     M = max_w m_w,  out = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w
-// in worker order (so the result does not depend on timing).
+// in worker order (so the result does not depend on timing), a batch of
+// workers at a time with the running maximum carried between batches.
 template <class T, int D, int GMAX>
 __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa, int32_t workers) {
   using bits = typename T::bits;
@@ -519,31 +520,77 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa, int32_t
   if (wlo == whi) return;  // written whole by its worker
   const int r0 = stream_start(wlo, ntot, nw) < gs ? 1 : 0;
   const int64_t row0 = int64_t(seq) * Hq + int64_t(kvh) * G;
-  for (int idx = lane; idx < G * (D / 4); idx += 64) {
-    const int j = idx / (D / 4), d4 = idx % (D / 4);
-    float M = kNegInf;
-    for (int64_t wi = wlo; wi <= whi; ++wi) {
-      const int64_t rj = (wi * 2 + (wi == wlo ? r0 : 0)) * GMAX + j;
-      M = fmaxf(M, sa.rec_ml[rj * 2]);
-    }
-    float L = 0.f;
-    f32x4 O = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t wi = wlo; wi <= whi; ++wi) {
-      const int64_t rj = (wi * 2 + (wi == wlo ? r0 : 0)) * GMAX + j;
-      const float2 ml = *reinterpret_cast<const float2*>(sa.rec_ml + rj * 2);
-      const float e = fast_exp2(ml.x - M);
-      L = __builtin_fmaf(e, ml.y, L);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(sa.rec_acc + rj * D + 4 * d4);
+  // each lane merges units idx = lane + 64 u (4 output columns each) of the
+  // G x D item; the records are read in batches of R so that a batch's
+  // loads are in flight together (two round trips per batch: maxima, then
+  // sums and partial outputs)
+  constexpr int NU = (GMAX * D / 4 + 63) / 64;
+  constexpr int R = 4;
+  const int units = G * (D / 4);
+  float M[NU], L[NU];
+  f32x4 O[NU];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) O[i] = __builtin_fmaf(e, v[i], O[i]);
+  for (int u = 0; u < NU; ++u) {
+    M[u] = kNegInf;
+    L[u] = 0.f;
+    O[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto rec_of = [&](int64_t wi, int j) { return (wi * 2 + (wi == wlo ? r0 : 0)) * GMAX + j; };
+  for (int64_t base = wlo; base <= whi; base += R) {
+    float m[R][NU];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int idx = lane + 64 * u;
+        const int64_t wi = min(base + r, whi);
+        m[r][u] = idx < units ? sa.rec_ml[rec_of(wi, idx / (D / 4)) * 2] : 0.f;
+      }
+    float2 ml[R][NU];
+    f32x4 v[R][NU];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int idx = lane + 64 * u;
+        const int64_t wi = min(base + r, whi);
+        const int64_t rj = rec_of(wi, idx < units ? idx / (D / 4) : 0);
+        ml[r][u] = *reinterpret_cast<const float2*>(sa.rec_ml + rj * 2);
+        v[r][u] = *reinterpret_cast<const f32x4*>(sa.rec_acc + rj * D + 4 * (idx < units ? idx % (D / 4) : 0));
+      }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      float mb = M[u];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (base + r <= whi) mb = fmaxf(mb, m[r][u]);
+      const float c0 = M[u] == kNegInf ? 0.f : fast_exp2(M[u] - mb);
+      L[u] *= c0;
+      O[u] *= c0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (base + r <= whi) {
+          const float e = fast_exp2(ml[r][u].x - mb);
+          L[u] = __builtin_fmaf(e, ml[r][u].y, L[u]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[u][i] = __builtin_fmaf(e, v[r][u][i], O[u][i]);
+        }
+      }
+      M[u] = mb;
     }
-    const float inv = 1.f / L;
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int idx = lane + 64 * u;
+    if (idx >= units) continue;
+    const int j = idx / (D / 4), d4 = idx % (D / 4);
+    const float inv = 1.f / L[u];
     const int64_t o = (row0 + j) * D + 4 * d4;
     if (a.out_f32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = O * inv;
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = O[u] * inv;
     } else {
-      const uint32_t lo = T::from_f32(O[0] * inv) | (T::from_f32(O[1] * inv) << 16);
-      const uint32_t hi = T::from_f32(O[2] * inv) | (T::from_f32(O[3] * inv) << 16);
+      const uint32_t lo = T::from_f32(O[u][0] * inv) | (T::from_f32(O[u][1] * inv) << 16);
+      const uint32_t hi = T::from_f32(O[u][2] * inv) | (T::from_f32(O[u][3] * inv) << 16);
       *reinterpret_cast<u32x2*>(static_cast<bits*>(a.out) + o) = u32x2{lo, hi};
     }
   }

@@ -56,7 +56,7 @@ class _Staging:
 class PagedKVEngine:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int, dtype,
                  order: Optional[Sequence[int]] = None, device: str = "cuda", poison: bool = True,
-                 max_seqs: int = 256, max_context: int = 4096, ring: int = 3):
+                 max_seqs: int = 256, max_context: int = 4096, ring: int = 8, guard_every: int = 4):
         self.N, self.H, self.D, self.BS, self.dtype = num_blocks, num_kv_heads, head_dim, block_size, dtype
         self.device = torch.device(device)
         self.bm = BlockManager(num_blocks, block_size, order)
@@ -66,19 +66,38 @@ class PagedKVEngine:
         self.stride = -(-max_context // block_size)
         self._ring = [_Staging(max_seqs, self.stride, self.device) for _ in range(ring)]
         self._ri = 0
+        # an event packet between kernels costs the stream ~4 us, so only every
+        # guard_every-th record is guarded; a slot is reused ring records later,
+        # so the host waits on the newest guard at least ring - guard_every back
+        assert 1 <= guard_every <= ring // 2
+        self._guard_every = guard_every
+        self._uses = 0
+        self._pending = []
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
 
     # ------------------------------------------------------------- helpers
     def _next(self) -> _Staging:
+        """The next staging record; returns once no queued work reads it."""
         st = self._ring[self._ri]
         self._ri = (self._ri + 1) % len(self._ring)
+        # the guard recorded after this slot's last use, or after a later one
+        # of the previous lap, has completed before the slot is rewritten
         st.wait()
         return st
 
     def _record(self, st: _Staging, stream):
-        if st.event is None:
-            st.event = torch.cuda.Event()
-        st.event.record(stream)
+        """Guard the records used so far: every guard_every-th use records an
+        event on the stream and hands it to the slots of the last
+        guard_every uses (they are reused only after it completes)."""
+        self._uses += 1
+        self._pending.append(st)
+        if self._uses % self._guard_every:
+            return      # the slot keeps its previous guard until the next one is recorded
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        for p in self._pending:
+            p.event = ev
+        self._pending = []
 
     def workspace(self, num_seqs: int, num_q_heads: int, max_ctx: int, partition_size: int = 0):
         """Decode workspace, grown on demand and reused across calls."""

@@ -53,9 +53,11 @@ class DeviceRun:
 
 def run_script(w, device="cuda", partition_size: int = 0, kernel: int = PA_KERNEL_AUTO,
                out_dtype=torch.float32, poison: bool = True, decode: bool = True,
-               extra_context: int = 0, use_step: bool = False) -> DeviceRun:
+               extra_context: int = 0, use_step: bool = False, extra_blocks: int = 0) -> DeviceRun:
     """Replay ``w.ops``; ``extra_context`` widens the table stride for tokens
-    appended after the script.  With ``use_step`` an append directly followed
+    appended after the script and ``extra_blocks`` adds spare blocks at the
+    bottom of the free list (the script's allocations are unchanged; tokens
+    appended after it use them).  With ``use_step`` an append directly followed
     by a decode of the same sequences runs as one engine step (one host to
     device copy), the way the benchmark drives it."""
     cfg = w.cfg
@@ -92,7 +94,12 @@ def run_script(w, device="cuda", partition_size: int = 0, kernel: int = PA_KERNE
                                             run.engine.last_ctx.copy(), out))
             continue
         if kind == "create":
-            eng = PagedKVEngine(op[1], cfg.num_kv_heads, cfg.head_dim, cfg.block_size, dtype, op[2],
+            nb, order = op[1], op[2]
+            if extra_blocks:
+                base = np.arange(nb) if order is None else np.asarray(order)
+                order = np.concatenate([base, np.arange(nb, nb + extra_blocks)])
+                nb += extra_blocks
+            eng = PagedKVEngine(nb, cfg.num_kv_heads, cfg.head_dim, cfg.block_size, dtype, order,
                                 device=dev, poison=poison, max_seqs=cfg.num_seqs, max_context=max_ctx)
             run = DeviceRun(eng, k_dev=k_dev, v_dev=v_dev, q_dev=q_dev)
         elif kind == "add_seq":
