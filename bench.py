@@ -39,7 +39,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=64,
+                    help="untimed steps (they also settle the stream kernel's workgroup shares)")
     ap.add_argument("--config", default="c2_gqa_bf16")
     ap.add_argument("--partition", type=int, default=None, help="tokens per split-K partition (0 = library)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma", "stream"])
@@ -48,6 +49,8 @@ def parse():
                     help="time the decode pass with HIP events on every k-th timed step (an event packet "
                          "between kernels costs the stream ~4 us, so sparse timing keeps the step intact)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-balance", action="store_true",
+                    help="equal workgroup shares in the stream kernel (no feedback from wave times)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (scales byte counters)")
     return ap.parse_args()
@@ -168,6 +171,7 @@ def main():
     dev = runner.run_script(w, partition_size=part, kernel=kernel, extra_context=total_steps,
                             extra_blocks=extra_blocks)
     eng: PagedKVEngine = dev.engine
+    eng.balance = not args.no_balance
     g = torch.Generator(device="cuda").manual_seed(1234)
     k_new = torch.randn((cfg.num_seqs, cfg.num_kv_heads, cfg.head_dim), generator=g, device="cuda").to(dtype)
     v_new = torch.randn((cfg.num_seqs, cfg.num_kv_heads, cfg.head_dim), generator=g, device="cuda").to(dtype)
@@ -198,6 +202,9 @@ def main():
         host_s.append(time.perf_counter() - h0)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    wts = eng.weights(cfg.num_seqs, cfg.num_q_heads)
+    if wts is not None:
+        print(f"[bench] workgroup weights by die: {wts[:8].tolist()}", file=sys.stderr, flush=True)
 
     # each timed step appends one token per sequence before attending
     step_ctx = [ctx_start + 1 + i for i in range(args.steps)]
@@ -226,7 +233,7 @@ def main():
                    "ctx_mean": round(float(np.mean(step_ctx[0])), 1), "partition": part or
                    pa.pa_decode_default_partition(cfg.num_seqs, cfg.num_kv_heads, int(step_ctx[-1].max()),
                                                   cfg.block_size),
-                   "kernel": args.kernel, "parallelism": "single GPU"},
+                   "kernel": args.kernel, "balance": eng.balance, "parallelism": "single GPU"},
         "tokens_per_s": round(cfg.num_seqs * args.steps / elapsed, 1),
         "host_us_per_step": round(float(np.median(host_s)) * 1e6, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),

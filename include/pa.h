@@ -252,12 +252,17 @@ pa_status pa_bm_stats(const pa_bm* bm, int64_t* out);
  *      block first, [VM] §Sharing comes almost for free);
  *   2. pa_bm_export of the grown tables and context lengths;
  *   3. the step record, laid out in int32 words as
- *      [slots n | copy pairs 2n | context lengths n | tables n * table_stride]
+ *      [slots n | copy pairs 2n | context lengths n | tables n * table_stride
+ *       | tile prefix sums n + 1 | stream plan]
  *      (rounded up to a multiple of 4 words), goes from stage_host (pinned
  *      host memory, 16-byte aligned) to stage_dev (device memory): when the
  *      runtime maps stage_host into the device's address space, a kernel on
  *      the stream copies it and writes the new tokens in the same launch,
- *      otherwise a host-to-device copy precedes pa_write_kv;
+ *      otherwise a host-to-device copy precedes pa_write_kv.  The stream
+ *      plan (16-bit caches, stream kernel selected) is the host's split of
+ *      the (sequence, kv head, 16-token tile) list over the kernel's waves:
+ *      each wave's first tile, then the items cut between waves with the
+ *      waves holding them, so that the merge runs over cut items only;
  *   4. pa_copy_blocks of the copy pairs and the KV write of k_new/v_new
  *      ([n][num_kv_heads][head_dim], device) into the new slots;
  *   5. pa_decode_phase PASS then MERGE of q ([n][num_q_heads][head_dim])
@@ -265,17 +270,48 @@ pa_status pa_bm_stats(const pa_bm* bm, int64_t* out);
  *      or NULL) are recorded on the stream around the pass.
  * Everything is enqueued on `stream`.  stage_host must not be rewritten until
  * this call's kernels have read it (keep a ring of records guarded by
- * events); both stage buffers hold the rounded record.
- * *max_ctx_out (may be NULL) receives the longest context.  Errors from the
- * manager leave it unchanged and launch nothing; a sequence whose next token
- * would not fit table_stride blocks is rejected before any change.
+ * events); both stage buffers hold stage_words >= pa_step_record_words(n,
+ * table_stride, num_kv_heads) int32 words.
+ * *max_ctx_out (may be NULL) receives the longest context.  Errors leave the
+ * manager unchanged and launch nothing: the decode arguments, the record
+ * size and the stride (a sequence whose next token would not fit
+ * table_stride blocks) are checked before any change.
+ * Stream kernel only: wg_weights (host, num_weights =
+ * pa_decode_stream_grid(...) entries, or NULL for equal shares) sets each
+ * workgroup's share of the tiles (clamped to 1..65536; results do not depend
+ * on it), and wave_times (pinned host or device memory, 8 * grid int32, or
+ * NULL) receives, for the 4 waves of each workgroup in order, the start and
+ * end of the wave as the low 32 bits of the GPU's 100 MHz real-time counter
+ * (compare stamps by signed difference), from which a caller can give slow
+ * compute units smaller shares on later steps (written only when the stream
+ * kernel runs).
  * ---------------------------------------------------------------------- */
 pa_status pa_step(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* stage_host, int32_t* stage_dev,
-                  int32_t table_stride, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
-                  const void* q, void* out, pa_dtype out_dtype, pa_dtype kv_dtype, int32_t num_q_heads,
-                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                  int32_t partition_size, void* workspace, size_t workspace_bytes, pa_kernel kernel,
-                  void* stream, void* pass_begin, void* pass_end, int32_t* max_ctx_out);
+                  size_t stage_words, int32_t table_stride, void* k_cache, void* v_cache, const void* k_new,
+                  const void* v_new, const void* q, void* out, pa_dtype out_dtype, pa_dtype kv_dtype,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t num_blocks, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                  pa_kernel kernel, void* stream, void* pass_begin, void* pass_end, int32_t* max_ctx_out,
+                  const int32_t* wg_weights, int32_t num_weights, int32_t* wave_times);
+
+/* Int32 words of a pa_step record for up to max_seqs sequences (0 for bad
+ * sizes). */
+size_t pa_step_record_words(int32_t max_seqs, int32_t table_stride, int32_t num_kv_heads);
+
+/* The stream plan pa_step writes into its record, computed on the host for
+ * inspection: tile_prefix[n + 1] (tiles of 16 tokens of the sequences before
+ * each one; non-decreasing from 0), `grid` workgroups (1..1024) with weights
+ * (NULL = equal).  Writes into out (out_words >= 4 grid + 1 + 2 n
+ * num_kv_heads + 1 + 8 grid): the first tile of each of the 4 grid waves and
+ * the end, the cut items (2 * (seq * num_kv_heads + kvh) + 1 when the item's
+ * first wave starts before it), their num_cut + 1 offsets and the waves of
+ * each.  Returns the words written, or -1 for bad arguments. */
+int64_t pa_stream_plan(const int32_t* tile_prefix, int32_t n, int32_t num_kv_heads, int32_t grid,
+                       const int32_t* weights, int32_t* out, size_t out_words, int32_t* num_cut);
+
+/* Workgroups of the stream kernel for this shape (0 when pa_decode would not
+ * use it): the length of pa_step's wg_weights. */
+int32_t pa_decode_stream_grid(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
 
 /* Debug validator over HOST copies of the decode inputs: every table entry a
  * sequence reads is in [0, num_blocks) and ceil(ctx/BS) <= stride.  Returns

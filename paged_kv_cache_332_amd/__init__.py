@@ -23,6 +23,7 @@ __all__ = [
     "PA_PHASE_PASS", "PA_PHASE_MERGE", "PA_PHASE_ALL",
     "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
     "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version", "pa_step",
+    "pa_decode_stream_grid", "step_record_words", "pa_stream_plan",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -72,8 +73,11 @@ _sig("pa_bm_num_seqs", _i32, _vp)
 _sig("pa_bm_free_list", _i32, _vp, _pi32, _i32)
 _sig("pa_bm_stats", _i32, _vp, _pi64)
 _sig("pa_check_tables", _i32, _pi32, _i32, _i32, _pi32, _i32, _i32)
-_sig("pa_step", _i32, _vp, _pi64, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-     _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp, _vp, _pi32)
+_sig("pa_step", _i32, _vp, _pi64, _i32, _vp, _vp, _sz, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+     _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp, _vp, _pi32, _pi32, _i32, _vp)
+_sig("pa_decode_stream_grid", _i32, _i32, _i32, _i32, _i32)
+_sig("pa_step_record_words", _sz, _i32, _i32, _i32)
+_sig("pa_stream_plan", _i64, _pi32, _i32, _i32, _i32, _pi32, _pi32, _sz, _pi32)
 
 
 class PAError(RuntimeError):
@@ -193,12 +197,16 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
 
 def pa_step(bm: "BlockManager", seqs_i64: np.ndarray, stage_host, stage_dev, table_stride: int, k_cache, v_cache,
             k_new, v_new, q, out, scale: float, partition_size: int = 0, workspace=None, kernel: int = PA_KERNEL_AUTO,
-            stream=None, pass_events=None) -> int:
+            stream=None, pass_events=None, wg_weights: Optional[np.ndarray] = None, wave_times=None) -> int:
     """One decode step (see pa_step in pa.h); returns the longest context.
     ``seqs_i64`` is a contiguous int64 array; stage_host/stage_dev are int32
-    tensors (pinned / device) of at least n * (4 + table_stride) words;
+    tensors (pinned / device) of at least step_record_words(n, table_stride,
+    Hkv) words;
     ``pass_events`` = (begin, end) torch CUDA events already created (recorded
-    once), recorded around the decode pass."""
+    once), recorded around the decode pass; ``wg_weights`` (contiguous int32,
+    pa_decode_stream_grid entries) sets the stream kernel's workgroup shares
+    and ``wave_times`` (int32 tensor, pinned or device, 8 x grid) receives its
+    wave start/end stamps."""
     n_, hkv, d, bs = _pool_dims(k_cache, v_cache)
     n = int(seqs_i64.shape[0])
     hq = int(q.shape[1])
@@ -206,12 +214,48 @@ def pa_step(bm: "BlockManager", seqs_i64: np.ndarray, stage_host, stage_dev, tab
                                                           workspace.numel() * workspace.element_size())
     ev0, ev1 = (None, None) if pass_events is None else (pass_events[0].cuda_event, pass_events[1].cuda_event)
     max_ctx = ctypes.c_int32(0)
+    words = min(stage_host.numel(), stage_dev.numel())
     _check(lib.pa_step(bm._h, seqs_i64.ctypes.data_as(_pi64), n, stage_host.data_ptr(), stage_dev.data_ptr(),
-                       int(table_stride), k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                       words, int(table_stride), k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
                        q.data_ptr(), out.data_ptr(), torch_dtype_code(out.dtype), torch_dtype_code(k_cache.dtype),
                        hq, hkv, d, bs, n_, float(scale), int(partition_size), ws_ptr, ws_bytes, int(kernel),
-                       _stream(stream), ev0, ev1, ctypes.byref(max_ctx)))
+                       _stream(stream), ev0, ev1, ctypes.byref(max_ctx),
+                       None if wg_weights is None else wg_weights.ctypes.data_as(_pi32),
+                       0 if wg_weights is None else int(wg_weights.shape[0]),
+                       None if wave_times is None else wave_times.data_ptr()))
     return int(max_ctx.value)
+
+
+def pa_decode_stream_grid(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    """Workgroups of the stream kernel for this shape (0 when not used)."""
+    return int(lib.pa_decode_stream_grid(num_seqs, num_q_heads, num_kv_heads, head_dim))
+
+
+def pa_stream_plan(tile_prefix: np.ndarray, num_kv_heads: int, grid: int, weights: Optional[np.ndarray] = None):
+    """The stream plan of pa_step for these tile counts: (wave starts [4 grid
+    + 1], cut item codes, offsets, waves)."""
+    pre = np.ascontiguousarray(tile_prefix, dtype=np.int32)
+    n = pre.shape[0] - 1
+    cap = 4 * grid + 1 + 2 * n * num_kv_heads + 1 + 8 * grid
+    out = np.zeros(cap, dtype=np.int32)
+    ncut = ctypes.c_int32(0)
+    w = None if weights is None else np.ascontiguousarray(weights, dtype=np.int32)
+    words = lib.pa_stream_plan(pre.ctypes.data_as(_pi32), n, num_kv_heads, grid,
+                               None if w is None else w.ctypes.data_as(_pi32), out.ctypes.data_as(_pi32), cap,
+                               ctypes.byref(ncut))
+    if words < 0:
+        raise PAError(1, "pa_stream_plan: bad arguments")
+    nw, k = 4 * grid, int(ncut.value)
+    starts = out[: nw + 1]
+    items = out[nw + 1: nw + 1 + k]
+    offs = out[nw + 1 + k: nw + 2 + 2 * k]
+    waves = out[nw + 2 + 2 * k: int(words)]
+    return starts, items, offs, waves
+
+
+def step_record_words(max_seqs: int, table_stride: int, num_kv_heads: int) -> int:
+    """Int32 words of a pa_step record for up to max_seqs sequences."""
+    return int(lib.pa_step_record_words(max_seqs, table_stride, num_kv_heads))
 
 
 def pa_check_tables(tables: np.ndarray, ctx_lens: np.ndarray, block_size: int, num_blocks: int) -> None:

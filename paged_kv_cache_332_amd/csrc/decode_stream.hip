@@ -9,11 +9,13 @@
 //
 // Work decomposition.  An item is one (sequence, kv head) pair; its tiles are
 // the 16-token slices of the sequence.  All tiles of all items are laid end to
-// end (sequence-major, then kv head, then tile) and every wave of the grid --
-// one workgroup per compute unit, four waves each -- takes an equal,
-// contiguous share of that list.  Each wave therefore reads the same number
-// of K/V bytes whatever the length mix, and streams across item boundaries
-// without draining.  An item cut between waves leaves a partial state
+// end (sequence-major, then kv head, then tile) and every workgroup of the
+// grid -- one per compute unit, four waves each -- takes a contiguous share of
+// that list, split evenly over its waves.  Shares are equal, or proportional
+// to per-workgroup weights the caller derives from the busy times the kernel
+// reports (compute units do not all stream at the same rate, and an even
+// split leaves the fast ones idle at the end).  A wave streams across item
+// boundaries without draining.  An item cut between waves leaves a partial state
 // (running max, sum, unnormalised output) per wave in the workspace, written
 // with plain stores; a second, small kernel merges the partial states of each
 // cut item by log-sum-exp in worker order.  The kernel boundary orders the
@@ -113,12 +115,17 @@ struct Cursor {
 
 }  // namespace
 
-// Worker owning global tile g when T tiles are split over nw workers as
-// [floor(w T / nw), floor((w + 1) T / nw)).
-__device__ __forceinline__ int64_t stream_owner(int64_t g, int64_t T, int64_t nw) {
-  return ((g + 1) * nw + T - 1) / T - 1;
+// Weights are clamped to [1, 2^16]; a zero, negative or garbage weight can
+// only make the split uneven, never wrong.
+// First tile of wave w (0..4 grid) when the T tiles are split evenly over
+// the grid's workgroups and each workgroup's share evenly over its four
+// waves (the split when no plan is given).
+__device__ __forceinline__ int64_t stream_wave_start(int64_t T, int64_t w, int grid) {
+  const int64_t b = w >> 2;
+  const int64_t a0 = T * b / grid;
+  const int64_t a1 = T * (b + 1) / grid;
+  return a0 + (a1 - a0) * (w & 3) / 4;
 }
-__device__ __forceinline__ int64_t stream_start(int64_t w, int64_t T, int64_t nw) { return w * T / nw; }
 
 template <class T, int D, int BS, int GMAX, int NSLOT>
 __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
@@ -142,6 +149,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
   static_assert(DPT * (NSLOT - 1) < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint64_t t_begin = __builtin_amdgcn_s_memrealtime();
   const DecodeArgs& a = sa.d;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -159,7 +167,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
   int32_t* pre = s_pre;                              // [B + 1] exclusive prefix of tiles
 
   // ---- tiles per sequence and their prefix sums (whole workgroup) --------
-  {
+  if (sa.pre_in) {
+    for (int i = threadIdx.x; i <= B; i += 256) {
+      pre[i] = sa.pre_in[i];
+      if (i < B) ctxs[i] = min(max(a.ctx[i], 0), a.max_ctx);
+    }
+    __syncthreads();
+  } else {
     int32_t* part = reinterpret_cast<int32_t*>(&s_tbl[0][0]);  // 512 ints of scratch
     const int per = (B + 255) / 256;
     const int i0 = threadIdx.x * per;
@@ -190,9 +204,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
     __syncthreads();
   }
   const int64_t ntot = int64_t(Hkv) * pre[B];
-  // never more workers than tiles: every worker range is then non-empty, so
-  // every worker an item's tiles touch leaves exactly one record for it
-  const int64_t nw = min(int64_t(gridDim.x) * 4, ntot);
 
   // sequences with no context get zero rows
   for (int s = blockIdx.x; s < B; s += gridDim.x) {
@@ -206,9 +217,15 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
   }
 
   const int64_t w = int64_t(blockIdx.x) * 4 + wave;
-  if (w >= nw) return;  // no workgroup barrier below this point
-  const int64_t ga = stream_start(w, ntot, nw);
-  const int64_t gb = stream_start(w + 1, ntot, nw);
+  const int64_t ga = sa.wave_start ? int64_t(sa.wave_start[w]) : stream_wave_start(ntot, w, gridDim.x);
+  const int64_t gb = sa.wave_start ? int64_t(sa.wave_start[w + 1]) : stream_wave_start(ntot, w + 1, gridDim.x);
+  if (ga >= gb) {  // no workgroup barrier below this point
+    if (sa.wave_time && lane == 0) {
+      const int32_t t0 = static_cast<int32_t>(t_begin);
+      *reinterpret_cast<int2*>(sa.wave_time + 2 * w) = make_int2(t0, t0);
+    }
+    return;
+  }
 
   // ---- cursors over the tile list -----------------------------------------
   auto locate = [&](int64_t g) {
@@ -224,9 +241,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
     cu.seq = lo;
     cu.nt = pre[lo + 1] - pre[lo];
     cu.ctx = ctxs[lo];
-    const int64_t r = g - int64_t(Hkv) * pre[lo];
-    cu.kvh = int(r / cu.nt);
-    cu.t = int(r % cu.nt);
+    const int r = int(g - int64_t(Hkv) * pre[lo]);  // < Hkv * nt
+    cu.kvh = r / cu.nt;
+    cu.t = r - cu.kvh * cu.nt;
     return cu;
   };
   auto advance = [&](Cursor& cu) {
@@ -477,53 +494,31 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
     }
   }
   if (have_item) flush();
+  if (sa.wave_time && lane == 0)
+    *reinterpret_cast<int2*>(sa.wave_time + 2 * w) =
+        make_int2(static_cast<int32_t>(t_begin), static_cast<int32_t>(__builtin_amdgcn_s_memrealtime()));
 }
 
-// Merge of the items the stream kernel cut between workers.  One wave per
-// item (sequence, kv head): it recomputes the item's place in the tile list
-// from the context lengths, and if the item spans workers wlo < whi it
-// combines their partial states
+// Log-sum-exp merge of one item (sequence seq, kv head kvh) that the stream
+// kernel cut between waves, from the partial states the waves recorded:
 //     M = max_w m_w,  out = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w
-// in worker order (so the result does not depend on timing), a batch of
-// workers at a time with the running maximum carried between batches.
-template <class T, int D, int GMAX>
-__global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa, int32_t workers) {
+// taken in wave order (so the result does not depend on timing), a batch of
+// R waves at a time with the running maximum carried between batches.
+// next(w) yields the item's waves in order, starting with w0, and returns
+// false after the last; w0 holds its state in record slot r0 (1 when the item
+// starts inside its range), every later wave in slot 0.
+template <class T, int D, int GMAX, class Next>
+__device__ __forceinline__ void merge_item(const StreamArgs& sa, int seq, int kvh, int64_t w0, int r0, Next next) {
   using bits = typename T::bits;
   const DecodeArgs& a = sa.d;
   const int lane = threadIdx.x;
-  const int B = a.num_seqs;
   const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
   const int G = Hq / Hkv;
-  const int seq = blockIdx.x / Hkv;
-  const int kvh = blockIdx.x % Hkv;
-  // tiles of earlier sequences and of all sequences
-  int64_t before = 0, all = 0;
-  int own = 0;
-  for (int i = lane; i < B; i += 64) {
-    const int n = (min(max(a.ctx[i], 0), a.max_ctx) + 15) / 16;
-    all += n;
-    if (i < seq) before += n;
-    if (i == seq) own = n;
-  }
-  for (int off = 32; off; off >>= 1) {
-    all += __shfl_xor(all, off);
-    before += __shfl_xor(before, off);
-    own += __shfl_xor(own, off);
-  }
-  if (own == 0) return;
-  const int64_t ntot = int64_t(Hkv) * all;
-  const int64_t nw = min(int64_t(workers), ntot);
-  const int64_t gs = int64_t(Hkv) * before + int64_t(kvh) * own;
-  const int64_t wlo = stream_owner(gs, ntot, nw);
-  const int64_t whi = stream_owner(gs + own - 1, ntot, nw);
-  if (wlo == whi) return;  // written whole by its worker
-  const int r0 = stream_start(wlo, ntot, nw) < gs ? 1 : 0;
   const int64_t row0 = int64_t(seq) * Hq + int64_t(kvh) * G;
   // each lane merges units idx = lane + 64 u (4 output columns each) of the
-  // G x D item; the records are read in batches of R so that a batch's
-  // loads are in flight together (two round trips per batch: maxima, then
-  // sums and partial outputs)
+  // G x D item; a batch's loads are in flight together (two round trips per
+  // batch: maxima, then sums and partial outputs)
   constexpr int NU = (GMAX * D / 4 + 63) / 64;
   constexpr int R = 4;
   const int units = G * (D / 4);
@@ -535,16 +530,25 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa, int32_t
     L[u] = 0.f;
     O[u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  auto rec_of = [&](int64_t wi, int j) { return (wi * 2 + (wi == wlo ? r0 : 0)) * GMAX + j; };
-  for (int64_t base = wlo; base <= whi; base += R) {
+  auto rec_of = [&](int64_t wi, int j) { return (wi * 2 + (wi == w0 ? r0 : 0)) * GMAX + j; };
+  bool more = true;
+  while (more) {
+    int64_t wr[R];       // the next R waves (w0 again past the last, unused)
+    bool live[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int64_t x = w0;
+      live[r] = more && next(x);
+      more = live[r];
+      wr[r] = live[r] ? x : w0;
+    }
     float m[R][NU];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int idx = lane + 64 * u;
-        const int64_t wi = min(base + r, whi);
-        m[r][u] = idx < units ? sa.rec_ml[rec_of(wi, idx / (D / 4)) * 2] : 0.f;
+        m[r][u] = idx < units ? sa.rec_ml[rec_of(wr[r], idx / (D / 4)) * 2] : 0.f;
       }
     float2 ml[R][NU];
     f32x4 v[R][NU];
@@ -553,8 +557,7 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa, int32_t
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int idx = lane + 64 * u;
-        const int64_t wi = min(base + r, whi);
-        const int64_t rj = rec_of(wi, idx < units ? idx / (D / 4) : 0);
+        const int64_t rj = rec_of(wr[r], idx < units ? idx / (D / 4) : 0);
         ml[r][u] = *reinterpret_cast<const float2*>(sa.rec_ml + rj * 2);
         v[r][u] = *reinterpret_cast<const f32x4*>(sa.rec_acc + rj * D + 4 * (idx < units ? idx % (D / 4) : 0));
       }
@@ -563,13 +566,13 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa, int32_t
       float mb = M[u];
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (base + r <= whi) mb = fmaxf(mb, m[r][u]);
+        if (live[r]) mb = fmaxf(mb, m[r][u]);
       const float c0 = M[u] == kNegInf ? 0.f : fast_exp2(M[u] - mb);
       L[u] *= c0;
       O[u] *= c0;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (base + r <= whi) {
+        if (live[r]) {
           const float e = fast_exp2(ml[r][u].x - mb);
           L[u] = __builtin_fmaf(e, ml[r][u].y, L[u]);
 #pragma unroll
@@ -594,6 +597,76 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa, int32_t
       *reinterpret_cast<u32x2*>(static_cast<bits*>(a.out) + o) = u32x2{lo, hi};
     }
   }
+}
+
+// Merge without a plan: one wave per item (sequence, kv head).  It recomputes
+// the item's place in the tile list from the context lengths and the even
+// split of the grid, and merges when the item spans more than one wave.
+template <class T, int D, int GMAX>
+__global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa, int32_t grid) {
+  const DecodeArgs& a = sa.d;
+  const int lane = threadIdx.x;
+  const int B = a.num_seqs;
+  const int Hkv = a.num_kv_heads;
+  const int seq = blockIdx.x / Hkv;
+  const int kvh = blockIdx.x % Hkv;
+  // tiles of earlier sequences and of all sequences
+  int64_t before = 0, all = 0;
+  int own = 0;
+  for (int i = lane; i < B; i += 64) {
+    const int n = (min(max(a.ctx[i], 0), a.max_ctx) + 15) / 16;
+    all += n;
+    if (i < seq) before += n;
+    if (i == seq) own = n;
+  }
+  for (int off = 32; off; off >>= 1) {
+    all += __shfl_xor(all, off);
+    before += __shfl_xor(before, off);
+    own += __shfl_xor(own, off);
+  }
+  if (own == 0) return;
+  const int64_t ntot = int64_t(Hkv) * all;
+  const int64_t nw = int64_t(grid) * 4;
+  auto start = [&](int64_t w) { return w >= nw ? ntot : stream_wave_start(ntot, w, grid); };
+  // last wave whose range starts at or before g (its range holds g)
+  auto owner = [&](int64_t g) {
+    int64_t lo = 0, hi = nw - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (start(mid) <= g) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  const int64_t gs = int64_t(Hkv) * before + int64_t(kvh) * own;
+  const int64_t wlo = owner(gs);
+  const int64_t whi = owner(gs + own - 1);
+  if (wlo == whi) return;  // written whole by its wave
+  // the waves with tiles from wlo to whi (skipping empty ranges)
+  int64_t cur = wlo;
+  merge_item<T, D, GMAX>(sa, seq, kvh, wlo, start(wlo) < gs ? 1 : 0, [&](int64_t& x) {
+    while (cur <= whi && start(cur) >= start(cur + 1)) ++cur;
+    if (cur > whi) return false;
+    x = cur++;
+    return true;
+  });
+}
+
+// Merge with the host plan: one wave per cut item, which reads the item and
+// its waves from the plan.
+template <class T, int D, int GMAX>
+__global__ __launch_bounds__(64) void stream_merge_planned_kernel(StreamArgs sa) {
+  const int k = blockIdx.x;
+  const int code = sa.cut_item[k];
+  const int item = code >> 1;
+  const int Hkv = sa.d.num_kv_heads;
+  int i = sa.cut_off[k];
+  const int end = sa.cut_off[k + 1];
+  merge_item<T, D, GMAX>(sa, item / Hkv, item % Hkv, sa.cut_workers[i], code & 1, [&](int64_t& x) {
+    if (i >= end) return false;
+    x = sa.cut_workers[i++];
+    return true;
+  });
 }
 
 // ------------------------------------------------------------------ launch
@@ -630,9 +703,15 @@ static hipError_t launch_s(const StreamArgs& sa, size_t lds, int grid, int phase
     if (e != hipSuccess) return e;
   }
   if (!(phases & 2)) return hipSuccess;
+  if (sa.cut_item) {
+    if (sa.num_cut <= 0) return hipSuccess;
+    hipLaunchKernelGGL((stream_merge_planned_kernel<T, D, GMAX>), dim3(static_cast<uint32_t>(sa.num_cut)), dim3(64),
+                       0, stream, sa);
+    return hipGetLastError();
+  }
   const int64_t items = int64_t(sa.d.num_seqs) * sa.d.num_kv_heads;
   hipLaunchKernelGGL((stream_merge_kernel<T, D, GMAX>), dim3(static_cast<uint32_t>(items)), dim3(64), 0, stream, sa,
-                     grid * 4);
+                     grid);
   return hipGetLastError();
 }
 

@@ -153,7 +153,7 @@ StreamPlan stream_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t group, in
   }
   if (!p.nslot) return p;
   const int per_cu = static_cast<int>(kStreamLdsPerCu / (p.lds + kStreamStaticLds));
-  p.grid = device_cus() * std::max(1, per_cu);
+  p.grid = std::min(kStreamMaxGrid, device_cus() * std::max(1, per_cu));
   const size_t workers = size_t(p.grid) * 4;
   p.ml_bytes = round_up(workers * 2 * p.gmax * 2 * sizeof(float));
   p.acc_bytes = round_up(workers * 2 * p.gmax * size_t(head_dim) * sizeof(float));
@@ -188,18 +188,19 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 }  // extern "C"
 
 namespace pa {
-namespace {
 
 // Validates, picks the kernel and launches the phases asked for (bit 0: the
-// pass over the K/V tiles, bit 1: the merge of split items).
+// pass over the K/V tiles, bit 1: the merge of split items; 0 validates
+// only).  `extras` (may be null) passes the stream kernel's host plan and
+// the wave stamp output.
 pa_status decode_impl(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
                       pa_dtype kv_dtype, const int32_t* block_tables, int32_t table_stride,
                       const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                       int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream,
-                      pa_kernel kernel, int phases) {
+                      pa_kernel kernel, int phases, const StreamExtras* extras) {
   const char* fn = "pa_decode";
-  if (phases < 1 || phases > 3) return pa::fail(PA_ERR_INVALID, "%s: phases %d not in 1..3", fn, phases);
+  if (phases < 0 || phases > 3) return pa::fail(PA_ERR_INVALID, "%s: phases %d not in 1..3", fn, phases);
   if (pa_status st = pa::check_cache_shape(fn, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype))
     return st;
   if (out_dtype != PA_F32 && out_dtype != kv_dtype)
@@ -236,6 +237,10 @@ pa_status decode_impl(void* out, pa_dtype out_dtype, const void* q, const void* 
                         workspace_bytes);
       if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return pa::fail(PA_ERR_INVALID, "%s: workspace must be 256-byte aligned", fn);
+      // tile positions within a sequence's kv heads are 32-bit
+      if (int64_t(num_kv_heads) * pa::ceil_div(max_context_len, 16) >= (int64_t(1) << 31))
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: context too long for the stream kernel", fn);
+      if (phases == 0) return PA_OK;
       pa::StreamArgs sa{};
       sa.d.out = out;
       sa.d.q = q;
@@ -255,6 +260,15 @@ pa_status decode_impl(void* out, pa_dtype out_dtype, const void* q, const void* 
       char* w = static_cast<char*>(workspace);
       sa.rec_ml = reinterpret_cast<float*>(w);
       sa.rec_acc = reinterpret_cast<float*>(w + sp.ml_bytes);
+      if (extras) {
+        sa.pre_in = extras->pre;
+        sa.wave_start = extras->wave_start;
+        sa.cut_item = extras->cut_item;
+        sa.cut_off = extras->cut_off;
+        sa.cut_workers = extras->cut_workers;
+        sa.num_cut = extras->num_cut;
+        sa.wave_time = extras->wave_time;
+      }
       return pa::hip_status(fn, pa::launch_decode_stream(sa, kv_dtype, head_dim, block_size, sp.gmax, sp.nslot,
                                                           sp.lds, sp.grid, phases, s));
     }
@@ -299,6 +313,7 @@ pa_status decode_impl(void* out, pa_dtype out_dtype, const void* q, const void* 
     a.ws_l = reinterpret_cast<float*>(w + ml);
     a.ws_acc = reinterpret_cast<float*>(w + 2 * ml);
   }
+  if (phases == 0) return PA_OK;
   const bool use_mfma = kernel == PA_KERNEL_MFMA || (kernel == PA_KERNEL_AUTO && kv_dtype != PA_F32);
   if (phases & 1) {
     hipError_t e = use_mfma ? pa::launch_decode_mfma(a, kv_dtype, head_dim, block_size, group, s)
@@ -312,10 +327,25 @@ pa_status decode_impl(void* out, pa_dtype out_dtype, const void* q, const void* 
   return PA_OK;
 }
 
-}  // namespace
+int32_t stream_grid(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return 0;
+  const StreamPlan sp = stream_plan(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim);
+  return sp.ok ? sp.grid : 0;
+}
+
+int32_t stream_grid_selected(pa_kernel kernel, pa_dtype kv_dtype, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim) {
+  const bool stream = kernel == PA_KERNEL_STREAM || (kernel == PA_KERNEL_AUTO && kv_dtype != PA_F32);
+  return stream ? stream_grid(num_seqs, num_q_heads, num_kv_heads, head_dim) : 0;
+}
+
 }  // namespace pa
 
 extern "C" {
+
+int32_t pa_decode_stream_grid(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  return pa::stream_grid(num_seqs, num_q_heads, num_kv_heads, head_dim);
+}
 
 pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
                             const void* v_cache, pa_dtype kv_dtype, const int32_t* block_tables,
@@ -325,7 +355,7 @@ pa_status pa_decode_variant(void* out, pa_dtype out_dtype, const void* q, const 
                             void* workspace, size_t workspace_bytes, void* stream, pa_kernel kernel) {
   return pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, table_stride, context_lens,
                          max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                         scale, partition_size, workspace, workspace_bytes, stream, kernel, 3);
+                         scale, partition_size, workspace, workspace_bytes, stream, kernel, 3, nullptr);
 }
 
 pa_status pa_decode_phase(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
@@ -334,9 +364,10 @@ pa_status pa_decode_phase(void* out, pa_dtype out_dtype, const void* q, const vo
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           int32_t num_blocks, float scale, int32_t partition_size, void* workspace,
                           size_t workspace_bytes, void* stream, pa_kernel kernel, int32_t phase) {
+  if (phase < 1 || phase > 3) return pa::fail(PA_ERR_INVALID, "pa_decode: phase %d not in 1..3", int(phase));
   return pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, table_stride, context_lens,
                          max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                         scale, partition_size, workspace, workspace_bytes, stream, kernel, phase);
+                         scale, partition_size, workspace, workspace_bytes, stream, kernel, phase, nullptr);
 }
 
 pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,

@@ -34,11 +34,21 @@ struct StreamArgs {
   DecodeArgs d;
   float* rec_ml;                 // [workers][2][gmax][2]  (max, sum) of partial states
   float* rec_acc;                // [workers][2][gmax][D]  unnormalised partial outputs
+  // optional host plan (all null: the kernels derive an equal split themselves)
+  const int32_t* pre_in;         // [B + 1] tiles of the sequences before each one
+  const int32_t* wave_start;     // [grid * 4 + 1] first tile of each wave, non-decreasing, last = all tiles
+  const int32_t* cut_item;       // [num_cut] 2 * (seq * Hkv + kvh) + (1 if its first wave starts before it)
+  const int32_t* cut_off;        // [num_cut + 1] offsets into cut_workers
+  const int32_t* cut_workers;    // waves with tiles of each cut item, in order
+  int32_t num_cut;
+  int32_t* wave_time;            // [grid * 4][2] start and end of each wave (low 32 bits of the
+                                 // 100 MHz real-time counter), or null
 };
 
 // Stream kernel limits: tiles whose block ids a wave stages per pass, the
 // largest batch, and its static LDS (block ids, lengths, prefix sums).
 constexpr int kStreamTcap = 224;
+constexpr int kStreamMaxGrid = 1024;      // workgroups of one stream launch
 constexpr int kStreamMaxSeqs = 1024;
 // (16 KiB bounds the arrays with the compiler's alignment padding)
 constexpr size_t kStreamStaticLds = 16 * 1024;

@@ -11,56 +11,168 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <vector>
 
 #include "pa_internal.h"
 #include "pa_kernels.h"
 
 namespace {
 
-// Device-visible address of pinned host memory (the same address on a
-// unified address space), or nullptr when the runtime reports none.  The
-// last few lookups are cached: callers rotate a handful of step records.
-const int32_t* device_view(const int32_t* host) {
+// Device-visible address of `p`: pinned host memory maps to its device
+// address (the same on a unified address space), device memory to itself
+// when `allow_device`; anything else gives nullptr.  The last few lookups are
+// cached: callers rotate a handful of step records.
+int32_t* device_view(const int32_t* p, bool allow_device) {
   struct Entry {
-    const void* host;
-    const void* dev;
+    const void* p;
+    void* dev;
+    bool device;
   };
-  static thread_local Entry cache[8] = {};
+  static thread_local Entry cache[16] = {};
   static thread_local int next = 0;
   for (const Entry& e : cache)
-    if (e.host == host) return static_cast<const int32_t*>(e.dev);
+    if (e.p == p) return (e.device && !allow_device) ? nullptr : static_cast<int32_t*>(e.dev);
   hipPointerAttribute_t attr{};
-  const void* dev = nullptr;
-  if (hipPointerGetAttributes(&attr, host) == hipSuccess && attr.type == hipMemoryTypeHost && attr.devicePointer)
-    dev = attr.devicePointer;
+  void* dev = nullptr;
+  bool device = false;
+  if (hipPointerGetAttributes(&attr, p) == hipSuccess) {
+    if (attr.type == hipMemoryTypeHost && attr.devicePointer) {
+      dev = attr.devicePointer;
+    } else if (attr.type == hipMemoryTypeDevice) {
+      dev = const_cast<int32_t*>(p);
+      device = true;
+    }
+  }
   (void)hipGetLastError();  // a plain host pointer leaves an error behind
-  cache[next] = Entry{host, dev};
-  next = (next + 1) % 8;
-  return static_cast<const int32_t*>(dev);
+  cache[next] = Entry{p, dev, device};
+  next = (next + 1) % 16;
+  return (device && !allow_device) ? nullptr : static_cast<int32_t*>(dev);
+}
+
+// Words of a step record for n sequences: the bookkeeping, the tile prefix
+// sums and room for the stream kernel's plan with `grid` workgroups.
+size_t record_words(int64_t n, int64_t stride, int64_t hkv, int64_t grid) {
+  const size_t w = size_t(n) * (5 + stride + 2 * hkv) + 1 + (grid ? 12 * grid + 2 : 0);
+  return (w + 3) / 4 * 4;
+}
+
+// The stream kernel's split, planned on the host and written at `out`:
+//   wave starts [4 grid + 1]: workgroup b takes tiles [T P_b / P, T P_(b+1) / P)
+//     of the T = Hkv * pre[n] tiles (P_b the sum of the weights before it,
+//     P their total), split evenly over its four waves;
+//   cut items [ncut]: 2 * (seq * Hkv + kvh) + (1 when the first wave holding
+//     the item started before it), for every item whose tiles fall to more
+//     than one wave;
+//   offsets [ncut + 1] into the list of those waves (non-empty ones only, in
+//     order), and the list.
+// Returns the words written (0 when there are no tiles); sets *ncut_out.
+size_t build_plan(int32_t* out, const int32_t* pre, int32_t n, int32_t hkv, int32_t grid, const int32_t* weights,
+                  int32_t* ncut_out) {
+  const int64_t total = int64_t(hkv) * pre[n];
+  const int64_t nw = int64_t(grid) * 4;
+  int32_t* S = out;
+  int64_t all = 0;
+  for (int32_t b = 0; b < grid; ++b) all += weights ? std::clamp<int64_t>(weights[b], 1, 1 << 16) : 1;
+  int64_t before = 0;
+  for (int32_t b = 0; b < grid; ++b) {
+    const int64_t wb = weights ? std::clamp<int64_t>(weights[b], 1, 1 << 16) : 1;
+    const int64_t a0 = total * before / all;
+    const int64_t a1 = total * (before + wb) / all;
+    for (int k = 0; k < 4; ++k) S[4 * b + k] = static_cast<int32_t>(a0 + (a1 - a0) * k / 4);
+    before += wb;
+  }
+  S[nw] = static_cast<int32_t>(total);
+  // items in tile order, with the wave holding their first and last tile
+  static thread_local std::vector<int32_t> items, offs, waves;
+  items.clear();
+  offs.clear();
+  waves.clear();
+  int64_t w = 0;  // the last wave starting at or before the current tile
+  for (int32_t s = 0; s < n; ++s) {
+    const int64_t nt = pre[s + 1] - pre[s];
+    if (nt == 0) continue;
+    for (int32_t h = 0; h < hkv; ++h) {
+      const int64_t gs = int64_t(hkv) * pre[s] + h * nt;
+      while (w + 1 < nw && S[w + 1] <= gs) ++w;
+      int64_t wh = w;
+      while (wh + 1 < nw && S[wh + 1] <= gs + nt - 1) ++wh;
+      if (wh != w) {
+        items.push_back(static_cast<int32_t>(2 * (int64_t(s) * hkv + h) + (S[w] < gs ? 1 : 0)));
+        offs.push_back(static_cast<int32_t>(waves.size()));
+        for (int64_t x = w; x <= wh; ++x)
+          if (S[x] < S[x + 1]) waves.push_back(static_cast<int32_t>(x));
+      }
+      w = wh;
+    }
+  }
+  offs.push_back(static_cast<int32_t>(waves.size()));
+  const size_t ncut = items.size();
+  int32_t* p = out + nw + 1;
+  std::copy(items.begin(), items.end(), p);
+  std::copy(offs.begin(), offs.end(), p + ncut);
+  std::copy(waves.begin(), waves.end(), p + 2 * ncut + 1);
+  *ncut_out = static_cast<int32_t>(ncut);
+  return size_t(nw) + 1 + 2 * ncut + 1 + waves.size();
 }
 
 }  // namespace
 
 extern "C" {
 
+int64_t pa_stream_plan(const int32_t* tile_prefix, int32_t n, int32_t num_kv_heads, int32_t grid,
+                       const int32_t* weights, int32_t* out, size_t out_words, int32_t* num_cut) {
+  if (!tile_prefix || !out || !num_cut || n < 0 || num_kv_heads <= 0 || grid <= 0 || grid > pa::kStreamMaxGrid)
+    return -1;
+  if (tile_prefix[0] != 0) return -1;
+  for (int32_t i = 0; i < n; ++i)
+    if (tile_prefix[i + 1] < tile_prefix[i]) return -1;
+  if (int64_t(num_kv_heads) * tile_prefix[n] >= (int64_t(1) << 31)) return -1;
+  if (out_words < size_t(4 * grid + 1) + 2 * size_t(n) * num_kv_heads + 1 + 8 * size_t(grid)) return -1;
+  return static_cast<int64_t>(build_plan(out, tile_prefix, n, num_kv_heads, grid, weights, num_cut));
+}
+
+size_t pa_step_record_words(int32_t max_seqs, int32_t table_stride, int32_t num_kv_heads) {
+  if (max_seqs <= 0 || table_stride <= 0 || num_kv_heads <= 0) return 0;
+  return record_words(max_seqs, table_stride, num_kv_heads, pa::kStreamMaxGrid);
+}
+
 pa_status pa_step(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* stage_host, int32_t* stage_dev,
-                  int32_t table_stride, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                  size_t stage_words, int32_t table_stride, void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                   const void* q, void* out, pa_dtype out_dtype, pa_dtype kv_dtype, int32_t num_q_heads,
                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                   int32_t partition_size, void* workspace, size_t workspace_bytes, pa_kernel kernel,
-                  void* stream, void* pass_begin, void* pass_end, int32_t* max_ctx_out) {
+                  void* stream, void* pass_begin, void* pass_end, int32_t* max_ctx_out,
+                  const int32_t* wg_weights, int32_t num_weights, int32_t* wave_times) {
   const char* fn = "pa_step";
   if (!bm || !seqs || !stage_host || !stage_dev || n <= 0 || table_stride <= 0 || block_size <= 0)
     return pa::fail(PA_ERR_INVALID, "%s: bad arguments", fn);
   // every sequence must still fit the table stride after its new token, so
   // that the export below cannot fail once the manager has changed
+  int32_t max_len = 0;
   for (int32_t i = 0; i < n; ++i) {
     const int32_t len = pa_bm_seq_len(bm, seqs[i]);
     if (len < 0) return pa::fail(PA_ERR_INVALID, "%s: unknown sequence %lld", fn, static_cast<long long>(seqs[i]));
     if (static_cast<int64_t>(len) + 1 > static_cast<int64_t>(table_stride) * block_size)
       return pa::fail(PA_ERR_INVALID, "%s: sequence %lld outgrows the table stride %d", fn,
                       static_cast<long long>(seqs[i]), table_stride);
+    max_len = std::max(max_len, len + 1);
   }
+  // the decode arguments, checked before anything changes
+  if (pa_status st = pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, stage_dev, table_stride,
+                                     stage_dev, max_len, n, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     num_blocks, scale, partition_size, workspace, workspace_bytes, stream, kernel, 0,
+                                     nullptr))
+    return st;
+  const int32_t grid = pa::stream_grid_selected(kernel, kv_dtype, n, num_q_heads, num_kv_heads, head_dim);
+  if (stage_words < record_words(n, table_stride, num_kv_heads, grid))
+    return pa::fail(PA_ERR_INVALID, "%s: the step record needs %zu words, %zu given", fn,
+                    record_words(n, table_stride, num_kv_heads, grid), stage_words);
+  if (wg_weights && num_weights != grid)
+    return pa::fail(PA_ERR_INVALID, "%s: %d workgroup weights given, the stream kernel runs %d", fn, num_weights,
+                    grid);
+  int32_t* d_times = nullptr;
+  if (wave_times && !(d_times = device_view(wave_times, true)))
+    return pa::fail(PA_ERR_INVALID, "%s: wave_times is neither pinned host nor device memory", fn);
   int32_t* slots = stage_host;
   int32_t* pairs = stage_host + n;
   int32_t* ctx = stage_host + 3 * n;
@@ -71,12 +183,23 @@ pa_status pa_step(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* stage_host
   int32_t max_ctx = 0;
   for (int32_t i = 0; i < n; ++i) max_ctx = std::max(max_ctx, ctx[i]);
   if (max_ctx_out) *max_ctx_out = max_ctx;
+  // tile (16-token) prefix sums and the stream kernel's plan follow the tables
+  const size_t pre_at = 4 * static_cast<size_t>(n) + static_cast<size_t>(n) * table_stride;
+  int32_t* pre = stage_host + pre_at;
+  pre[0] = 0;
+  for (int32_t i = 0; i < n; ++i) pre[i + 1] = pre[i] + (ctx[i] + 15) / 16;
+  const size_t plan_at = pre_at + n + 1;
+  int32_t ncut = 0;
+  const bool planned = grid > 0 && int64_t(num_kv_heads) * pre[n] < (int64_t(1) << 31);
+  const size_t plan_words =
+      planned ? build_plan(stage_host + plan_at, pre, n, num_kv_heads, grid, wg_weights, &ncut) : 0;
+  const size_t used = plan_at + plan_words;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t words = (4 * static_cast<size_t>(n) + static_cast<size_t>(n) * table_stride + 3) / 4 * 4;
+  const size_t words = (used + 3) / 4 * 4;
   const int32_t* host_view = (reinterpret_cast<uintptr_t>(stage_host) | reinterpret_cast<uintptr_t>(stage_dev)) & 15u
                                  ? nullptr
-                                 : device_view(stage_host);
+                                 : device_view(stage_host, false);
   if (host_view) {
     // the kernels read the record where the host wrote it: copy-on-write
     // copies, then one launch that copies the record to the device and
@@ -113,17 +236,26 @@ pa_status pa_step(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* stage_host
   }
   const int32_t* d_ctx = stage_dev + 3 * n;
   const int32_t* d_tables = stage_dev + 4 * n;
-  if (pa_status st = pa_decode_phase(out, out_dtype, q, k_cache, v_cache, kv_dtype, d_tables, table_stride, d_ctx,
+  pa::StreamExtras ex{stage_dev + pre_at, nullptr, nullptr, nullptr, nullptr, 0, d_times};
+  if (planned) {
+    const int32_t* plan = stage_dev + plan_at;
+    ex.wave_start = plan;
+    ex.cut_item = plan + 4 * int64_t(grid) + 1;
+    ex.cut_off = ex.cut_item + ncut;
+    ex.cut_workers = ex.cut_off + ncut + 1;
+    ex.num_cut = ncut;
+  }
+  if (pa_status st = pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, d_tables, table_stride, d_ctx,
                                      max_ctx, n, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
-                                     partition_size, workspace, workspace_bytes, stream, kernel, PA_PHASE_PASS))
+                                     partition_size, workspace, workspace_bytes, stream, kernel, PA_PHASE_PASS, &ex))
     return st;
   if (pass_end) {
     if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(pass_end), s))
       return pa::fail(PA_ERR_HIP, "%s: event: %s", fn, hipGetErrorString(e));
   }
-  return pa_decode_phase(out, out_dtype, q, k_cache, v_cache, kv_dtype, d_tables, table_stride, d_ctx, max_ctx, n,
+  return pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, d_tables, table_stride, d_ctx, max_ctx, n,
                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
-                         workspace, workspace_bytes, stream, kernel, PA_PHASE_MERGE);
+                         workspace, workspace_bytes, stream, kernel, PA_PHASE_MERGE, &ex);
 }
 
 }  // extern "C"

@@ -16,25 +16,63 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (PA_KERNEL_AUTO, BlockManager, alloc_cache, pa_copy_blocks, pa_decode_variant,
-               pa_decode_workspace_bytes, pa_step, pa_write_kv)
+from . import (PA_KERNEL_AUTO, PA_KERNEL_STREAM, BlockManager, alloc_cache, pa_copy_blocks, pa_decode_stream_grid,
+               pa_decode_variant, pa_decode_workspace_bytes, pa_step, pa_write_kv, step_record_words)
 
-__all__ = ["PagedKVEngine"]
+__all__ = ["PagedKVEngine", "rebalance"]
+
+
+_MAX_GRID = 1024     # the most workgroups the stream kernel launches
+
+
+XCDS = 8     # accelerator dies of the GPU; workgroup b of a launch runs on die b mod 8
+
+
+def rebalance(weights: np.ndarray, stamps: np.ndarray, rate: float = 0.5, groups: int = XCDS) -> np.ndarray:
+    """New stream-kernel workgroup weights from one completed step.
+
+    ``stamps`` holds, for the 4 waves of each workgroup in order, the start
+    and end of the wave (low 32 bits of a 100 MHz counter).  A workgroup's
+    finish time counts from the first start of any wave to the last end of
+    its own.  Workgroups are pooled in ``groups`` classes by index modulo
+    ``groups`` (the dies workgroups are dispatched to in turn, which run at
+    measurably different speeds; single workgroups only add noise).  Each
+    class's weight (its share of the tile list) moves towards what would have
+    let it finish with the others, w <- w * (mean / class mean) ** rate; the
+    result is scaled to a mean of 1024 and kept within 64..16384.  Results of
+    the decode do not depend on the weights, only the split of the work."""
+    g = weights.shape[0]
+    t = np.asarray(stamps[: 8 * g], dtype=np.int64).reshape(g, 4, 2)
+    rel = (t - t[0, 0, 0] + (1 << 31)) % (1 << 32) - (1 << 31)      # signed 32-bit differences
+    finish = (rel[:, :, 1].max(axis=1) - rel[:, :, 0].min()).astype(np.float64)
+    cls = np.arange(g) % groups
+    cnt = np.bincount(cls, minlength=groups)
+    mean_c = np.bincount(cls, weights=finish, minlength=groups) / np.maximum(cnt, 1)
+    w_c = np.bincount(cls, weights=weights.astype(np.float64), minlength=groups) / np.maximum(cnt, 1)
+    target = np.maximum(mean_c[cnt > 0].mean(), 1.0)
+    f = w_c * (target / np.maximum(mean_c, 1.0)) ** rate
+    f = f[cls]
+    f *= 1024.0 / f.mean()
+    return np.clip(np.rint(f), 64, 16384).astype(np.int32)
 
 
 class _Staging:
     """One step's bookkeeping in a single pinned host buffer and its device
     mirror, laid out [slots B | copy pairs 2B | context lengths B | tables
-    B x stride], so a whole step needs one host-to-device copy."""
+    B x stride | tile prefix sums B + 1 | stream plan], so a whole step
+    needs one host-to-device copy; plus a pinned buffer the stream kernel
+    writes its wave start/end stamps into."""
 
-    def __init__(self, max_seqs: int, stride: int, device):
+    def __init__(self, max_seqs: int, stride: int, num_kv_heads: int, device):
         self.stride = stride
         self.max_seqs = max_seqs
-        words = max_seqs * (4 + stride) + 4      # the record is rounded up to 16 bytes
+        words = step_record_words(max_seqs, stride, num_kv_heads)
         self.h = torch.empty(words, dtype=torch.int32, pin_memory=True)
         self.d = torch.empty(words, dtype=torch.int32, device=device)
         self.h_slots, self.h_pairs, self.h_ctx, self.h_tables = self._views(self.h, max_seqs)
         self.d_slots, self.d_pairs, self.d_ctx, self.d_tables = self._views(self.d, max_seqs)
+        self.times = torch.zeros(8 * _MAX_GRID, dtype=torch.int32, pin_memory=True)
+        self.times_key = None     # (balance key, weight version) of the step whose stamps `times` holds
         self.event: Optional[torch.cuda.Event] = None
 
     def _views(self, t, b):
@@ -56,7 +94,8 @@ class _Staging:
 class PagedKVEngine:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int, dtype,
                  order: Optional[Sequence[int]] = None, device: str = "cuda", poison: bool = True,
-                 max_seqs: int = 256, max_context: int = 4096, ring: int = 8, guard_every: int = 4):
+                 max_seqs: int = 256, max_context: int = 4096, ring: int = 8, guard_every: int = 4,
+                 balance: bool = True, balance_rate: float = 0.5):
         self.N, self.H, self.D, self.BS, self.dtype = num_blocks, num_kv_heads, head_dim, block_size, dtype
         self.device = torch.device(device)
         self.bm = BlockManager(num_blocks, block_size, order)
@@ -64,7 +103,7 @@ class PagedKVEngine:
                                                  device=self.device, poison=poison)
         self.max_seqs = max_seqs
         self.stride = -(-max_context // block_size)
-        self._ring = [_Staging(max_seqs, self.stride, self.device) for _ in range(ring)]
+        self._ring = [_Staging(max_seqs, self.stride, num_kv_heads, self.device) for _ in range(ring)]
         self._ri = 0
         # an event packet between kernels costs the stream ~4 us, so only every
         # guard_every-th record is guarded; a slot is reused ring records later,
@@ -74,6 +113,11 @@ class PagedKVEngine:
         self._uses = 0
         self._pending = []
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
+        # workgroup weights of the stream kernel per (batch size, query heads),
+        # fed back from the wave stamps of completed steps (see _balance)
+        self.balance, self.balance_rate = balance, balance_rate
+        self._weights = {}
+        self._wver = {}
 
     # ------------------------------------------------------------- helpers
     def _next(self) -> _Staging:
@@ -83,7 +127,36 @@ class PagedKVEngine:
         # the guard recorded after this slot's last use, or after a later one
         # of the previous lap, has completed before the slot is rewritten
         st.wait()
+        if st.times_key is not None:
+            self._balance(st)
         return st
+
+    def _balance(self, st: _Staging) -> None:
+        """Feedback from a completed step (see rebalance).  Stamps arrive a
+        ring's length of steps late, so only a step that ran with the current
+        weights updates them (at most once per lap): feedback from older
+        weights would correct the same error again and make the loop
+        oscillate."""
+        (key, version), st.times_key = st.times_key, None
+        w = self._weights.get(key)
+        if w is not None and version == self._wver.get(key):
+            w[:] = rebalance(w, st.times[: 8 * w.shape[0]].numpy(), self.balance_rate)
+            self._wver[key] = version + 1
+
+    def weights(self, num_seqs: int, num_q_heads: int) -> Optional[np.ndarray]:
+        """The stream kernel's workgroup weights for this shape (None when the
+        stream kernel is not used or balancing is off)."""
+        if not self.balance or self.dtype == torch.float32:
+            return None
+        key = (num_seqs, num_q_heads)
+        w = self._weights.get(key)
+        if w is None:
+            g = pa_decode_stream_grid(num_seqs, num_q_heads, self.H, self.D)
+            if g <= 0:
+                return None
+            w = self._weights[key] = np.full(g, 1024, dtype=np.int32)
+            self._wver[key] = 0
+        return w
 
     def _record(self, st: _Staging, stream):
         """Guard the records used so far: every guard_every-th use records an
@@ -186,9 +259,11 @@ class PagedKVEngine:
             out = torch.empty(q.shape, dtype=out_dtype, device=self.device)
         # the workspace is sized for the longest context the tables can hold
         ws = self.workspace(n, q.shape[1], self.stride * self.BS, partition_size)
+        w = self.weights(n, q.shape[1]) if kernel in (PA_KERNEL_AUTO, PA_KERNEL_STREAM) else None
         max_ctx = pa_step(self.bm, self._seq_arr, st.h, st.d, self.stride, self.k_cache, self.v_cache, k_new, v_new,
                           q, out, 1.0 / float(self.D) ** 0.5, partition_size, ws if ws.numel() else None, kernel,
-                          stream, pass_events)
+                          stream, pass_events, wg_weights=w, wave_times=None if w is None else st.times)
+        st.times_key = None if w is None else ((n, q.shape[1]), self._wver[(n, q.shape[1])])
         (hs, hp, hc, ht), _, _ = st.packed(n)
         self.last_tables, self.last_ctx, self.last_max_ctx = ht.numpy(), hc.numpy(), max_ctx
         self._record(st, stream)

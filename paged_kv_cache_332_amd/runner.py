@@ -53,13 +53,15 @@ class DeviceRun:
 
 def run_script(w, device="cuda", partition_size: int = 0, kernel: int = PA_KERNEL_AUTO,
                out_dtype=torch.float32, poison: bool = True, decode: bool = True,
-               extra_context: int = 0, use_step: bool = False, extra_blocks: int = 0) -> DeviceRun:
+               extra_context: int = 0, use_step: bool = False, extra_blocks: int = 0,
+               on_engine=None) -> DeviceRun:
     """Replay ``w.ops``; ``extra_context`` widens the table stride for tokens
     appended after the script and ``extra_blocks`` adds spare blocks at the
     bottom of the free list (the script's allocations are unchanged; tokens
     appended after it use them).  With ``use_step`` an append directly followed
     by a decode of the same sequences runs as one engine step (one host to
-    device copy), the way the benchmark drives it."""
+    device copy), the way the benchmark drives it.  ``on_engine(engine)`` is
+    called once the engine exists (to set its options before any step)."""
     cfg = w.cfg
     dtype = TORCH_DTYPE[cfg.dtype]
     dev = torch.device(device)
@@ -102,6 +104,8 @@ def run_script(w, device="cuda", partition_size: int = 0, kernel: int = PA_KERNE
             eng = PagedKVEngine(nb, cfg.num_kv_heads, cfg.head_dim, cfg.block_size, dtype, order,
                                 device=dev, poison=poison, max_seqs=cfg.num_seqs, max_context=max_ctx)
             run = DeviceRun(eng, k_dev=k_dev, v_dev=v_dev, q_dev=q_dev)
+            if on_engine is not None:
+                on_engine(eng)
         elif kind == "add_seq":
             _, seq, n, write = op
             if write and n:

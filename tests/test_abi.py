@@ -252,3 +252,87 @@ def test_workspace_bytes():
     # auto partition sizes never need more than the 256-token bound
     assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 4096, 0) >= max(stream, part)
     assert pa.pa_decode_workspace_bytes(64, 32, 7, 128, 4096, 0) == 0   # heads not a multiple
+
+
+def test_rebalance_feedback():
+    """Host feedback of the stream kernel's workgroup shares: equal finish
+    times keep equal weights; the workgroups of a die class (index modulo 8)
+    that finish late lose share together and early ones gain; single slow
+    workgroups only move their class; counter wrap-around between stamps is
+    harmless; the result stays within its bounds."""
+    from paged_kv_cache_332_amd.engine import rebalance
+    g = 32
+    w = np.full(g, 1024, dtype=np.int32)
+
+    def stamps(finish, base=1000):
+        t = np.zeros((g, 4, 2), dtype=np.int64)
+        t[:, :, 0] = base
+        t[:, :, 1] = base + np.asarray(finish)[:, None]
+        return ((t + (1 << 31)) % (1 << 32) - (1 << 31)).astype(np.int32).ravel()
+
+    assert (rebalance(w, stamps(np.full(g, 500))) == 1024).all()
+    fin = np.full(g, 500)
+    fin[3::8] = 1000          # class 3 slow
+    fin[7::8] = 250           # class 7 fast
+    r = rebalance(w, stamps(fin))
+    assert (r[3::8] == r[3]).all() and (r[7::8] == r[7]).all()
+    assert r[3] < r[0] < r[7] and abs(r.mean() - 1024) < 2
+    # the same finish times across the 32-bit wrap of the counter
+    assert (rebalance(w, stamps(fin, base=(1 << 32) - 300)) == r).all()
+    # one slow workgroup moves only its class, by a quarter of the effect
+    fin = np.full(g, 500)
+    fin[5] = 900
+    r = rebalance(w, stamps(fin))
+    assert (r[5::8] == r[5]).all() and r[5] < r[0] and (r[np.arange(g) % 8 != 5] == r[0]).all()
+    # bounds
+    fin = np.full(g, 10)
+    fin[0::8] = 10 ** 7
+    r = rebalance(w, stamps(fin), rate=1.0)
+    assert r.min() >= 64 and r.max() <= 16384 and r[0] == 64
+
+
+@settings(max_examples=60, deadline=None)
+@given(ctx=st.lists(st.integers(0, 700), min_size=1, max_size=12), hkv=st.sampled_from([1, 2, 8]),
+       grid=st.integers(1, 12), weighted=st.booleans(), seed=st.integers(0, 2 ** 16))
+def test_stream_plan_matches_brute_force(ctx, hkv, grid, weighted, seed):
+    """The host's split of the (sequence, kv head, 16-token tile) list over
+    the stream kernel's waves: workgroup shares follow the weights, every
+    tile has exactly one wave, and the cut items and their waves agree with
+    the owner of every tile found by brute force."""
+    import paged_kv_cache_332_amd as pa
+    tiles = [(c + 15) // 16 for c in ctx]
+    pre = np.concatenate([[0], np.cumsum(tiles)]).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    wts = rng.integers(-3, 70000, size=grid).astype(np.int32) if weighted else None
+    starts, items, offs, waves = pa.pa_stream_plan(pre, hkv, grid, wts)
+    total = hkv * int(pre[-1])
+    nw = 4 * grid
+    # shares: workgroup b holds [T P_b / P, T P_(b+1) / P), quartered
+    wc = np.ones(grid, dtype=np.int64) if wts is None else np.clip(wts.astype(np.int64), 1, 1 << 16)
+    P = np.concatenate([[0], np.cumsum(wc)])
+    for b in range(grid):
+        a0, a1 = total * P[b] // P[-1], total * P[b + 1] // P[-1]
+        assert [int(x) for x in starts[4 * b: 4 * b + 4]] == [a0 + (a1 - a0) * k // 4 for k in range(4)]
+    assert starts[nw] == total and (np.diff(starts) >= 0).all()
+    owner = np.searchsorted(starts[:nw], np.arange(total), side="right") - 1
+    expect = []
+    for s, nt in enumerate(tiles):
+        for h in range(hkv):
+            if nt == 0:
+                continue
+            gs = hkv * int(pre[s]) + h * nt
+            own = sorted(set(owner[gs: gs + nt].tolist()))
+            if len(own) > 1:
+                expect.append((2 * (s * hkv + h) + int(starts[own[0]] < gs), own))
+    assert len(items) == len(expect) and offs[0] == 0
+    for k, (code, own) in enumerate(expect):
+        assert items[k] == code
+        assert waves[offs[k]: offs[k + 1]].tolist() == own
+
+
+def test_stream_plan_rejects_bad_input():
+    import paged_kv_cache_332_amd as pa
+    with pytest.raises(pa.PAError):
+        pa.pa_stream_plan(np.array([0, 5, 3], dtype=np.int32), 2, 4)      # decreasing prefix
+    with pytest.raises(pa.PAError):
+        pa.pa_stream_plan(np.array([0, 5], dtype=np.int32), 2, 2000)      # grid beyond the limit

@@ -314,3 +314,40 @@ def test_stream_work_split(case):
     again = eng.decode(seqs, q, kernel=pa.PA_KERNEL_STREAM)
     torch.cuda.synchronize()
     assert torch.equal(again, dev.decodes[-1].out)
+
+
+@pytest.mark.parametrize("case", ["random", "one_heavy", "alternating"])
+def test_stream_weights(case):
+    """The stream kernel's workgroup weights change only how the tile list is
+    split: random weights over the whole valid range, one workgroup holding
+    nearly all the work (most workgroups empty) and alternating light and
+    heavy ones all match the oracle through the fused step, and the kernel
+    writes a start and end stamp for every wave."""
+    pa, runner = _pa()
+    ctx = [3000, 17, 900, 4100, 1, 250, 1024, 2000]
+    hq, hkv, d = 32, 8, 128
+    w = W.tiny(num_seqs=len(ctx), dtype="bf16", seed=23, ctx=ctx, num_q_heads=hq, num_kv_heads=hkv,
+               head_dim=d, block_size=16)
+    g = pa.pa_decode_stream_grid(len(ctx), hq, hkv, d)
+    assert g > 0
+
+    def set_weights(eng):
+        wt = eng.weights(len(ctx), hq)
+        assert wt is not None and wt.shape == (g,)
+        if case == "random":
+            wt[:] = np.random.default_rng(5).integers(1, 65537, size=g)
+        elif case == "one_heavy":
+            wt[:] = 1
+            wt[g // 3] = 65536
+        else:
+            wt[:] = np.where(np.arange(g) % 2 == 0, 1, 1000)
+
+    say("stream weights", case, "grid", g)
+    ref = oracle.run_scenario(w)
+    dev = runner.run_script(w, use_step=True, kernel=pa.PA_KERNEL_STREAM, on_engine=set_weights)
+    check_run(w, dev, ref, label=f"weights {case}")
+    eng = dev.engine
+    st = eng._ring[(eng._ri - 1) % len(eng._ring)]
+    t = st.times[: 8 * g].numpy().astype(np.int64).reshape(g, 4, 2)
+    span = (t[:, :, 1] - t[:, :, 0] + (1 << 31)) % (1 << 32) - (1 << 31)
+    assert (span >= 0).all() and span.max() > 0
