@@ -253,7 +253,9 @@ pa_status pa_bm_stats(const pa_bm* bm, int64_t* out);
  *   2. pa_bm_export of the grown tables and context lengths;
  *   3. the step record, laid out in int32 words as
  *      [slots n | copy pairs 2n | context lengths n | tables n * table_stride
- *       | tile prefix sums n + 1 | stream plan]
+ *       | tile prefix sums n + 1 | header 4 | stream plan]
+ *      (the header: copy-on-write pairs, the stream grid of the plan or 0,
+ *      cut items, words in use)
  *      (rounded up to a multiple of 4 words), goes from stage_host (pinned
  *      host memory, 16-byte aligned) to stage_dev (device memory): when the
  *      runtime maps stage_host into the device's address space, a kernel on
@@ -293,6 +295,22 @@ pa_status pa_step(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* stage_host
                   int32_t num_blocks, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                   pa_kernel kernel, void* stream, void* pass_begin, void* pass_end, int32_t* max_ctx_out,
                   const int32_t* wg_weights, int32_t num_weights, int32_t* wave_times);
+
+/* The device part of a step again, on the record the last pa_step left in
+ * stage_host / stage_dev (neither rewritten since), for another layer of the
+ * same model: its own pools, k_new / v_new, q and out, the same sequences,
+ * slots, tables and plan (every layer of a decoder shares them).  phases:
+ * bit 0 the copy-on-write copies and the KV write, bit 1 the decode pass,
+ * bit 2 the merge (7 = the whole layer; a pass alone leaves `out` unfinished
+ * for cut items until its merge runs).  Shapes and kernel must be those of
+ * the pa_step call (checked against the record's header: INVALID
+ * otherwise); pass_begin / pass_end / wave_times as in pa_step. */
+pa_status pa_step_layer(const int32_t* stage_host, int32_t* stage_dev, int32_t n, int32_t table_stride,
+                        void* k_cache, void* v_cache, const void* k_new, const void* v_new, const void* q, void* out,
+                        pa_dtype out_dtype, pa_dtype kv_dtype, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
+                        void* workspace, size_t workspace_bytes, pa_kernel kernel, void* stream, int32_t phases,
+                        void* pass_begin, void* pass_end, int32_t* wave_times);
 
 /* Int32 words of a pa_step record for up to max_seqs sequences (0 for bad
  * sizes). */

@@ -23,7 +23,8 @@ __all__ = [
     "PA_PHASE_PASS", "PA_PHASE_MERGE", "PA_PHASE_ALL",
     "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
     "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version", "pa_step",
-    "pa_decode_stream_grid", "step_record_words", "pa_stream_plan",
+    "pa_decode_stream_grid", "step_record_words", "pa_stream_plan", "pa_step_layer",
+    "STEP_KV", "STEP_PASS", "STEP_MERGE", "STEP_ALL",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -76,6 +77,8 @@ _sig("pa_check_tables", _i32, _pi32, _i32, _i32, _pi32, _i32, _i32)
 _sig("pa_step", _i32, _vp, _pi64, _i32, _vp, _vp, _sz, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
      _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp, _vp, _pi32, _pi32, _i32, _vp)
 _sig("pa_decode_stream_grid", _i32, _i32, _i32, _i32, _i32)
+_sig("pa_step_layer", _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+     _i32, _f32, _i32, _vp, _sz, _i32, _vp, _i32, _vp, _vp, _vp)
 _sig("pa_step_record_words", _sz, _i32, _i32, _i32)
 _sig("pa_stream_plan", _i64, _pi32, _i32, _i32, _i32, _pi32, _pi32, _sz, _pi32)
 
@@ -224,6 +227,29 @@ def pa_step(bm: "BlockManager", seqs_i64: np.ndarray, stage_host, stage_dev, tab
                        0 if wg_weights is None else int(wg_weights.shape[0]),
                        None if wave_times is None else wave_times.data_ptr()))
     return int(max_ctx.value)
+
+
+STEP_KV, STEP_PASS, STEP_MERGE, STEP_ALL = 1, 2, 4, 7
+
+
+def pa_step_layer(stage_host, stage_dev, n: int, table_stride: int, k_cache, v_cache, k_new, v_new, q, out,
+                  scale: float, partition_size: int = 0, workspace=None, kernel: int = PA_KERNEL_AUTO, stream=None,
+                  phases: int = STEP_ALL, pass_events=None, wave_times=None) -> None:
+    """The device part of the last pa_step again on its record, for another
+    layer (see pa_step_layer in pa.h); ``phases`` from STEP_KV | STEP_PASS |
+    STEP_MERGE."""
+    n_, hkv, d, bs = _pool_dims(k_cache, v_cache)
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(),
+                                                          workspace.numel() * workspace.element_size())
+    ev0, ev1 = (None, None) if pass_events is None else (pass_events[0].cuda_event, pass_events[1].cuda_event)
+    nil = 0
+    _check(lib.pa_step_layer(stage_host.data_ptr(), stage_dev.data_ptr(), int(n), int(table_stride),
+                             k_cache.data_ptr(), v_cache.data_ptr(),
+                             nil if k_new is None else k_new.data_ptr(), nil if v_new is None else v_new.data_ptr(),
+                             q.data_ptr(), out.data_ptr(), torch_dtype_code(out.dtype),
+                             torch_dtype_code(k_cache.dtype), int(q.shape[1]), hkv, d, bs, n_, float(scale),
+                             int(partition_size), ws_ptr, ws_bytes, int(kernel), _stream(stream), int(phases), ev0, ev1,
+                             None if wave_times is None else wave_times.data_ptr()))
 
 
 def pa_decode_stream_grid(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:

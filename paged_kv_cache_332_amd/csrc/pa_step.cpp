@@ -49,11 +49,112 @@ int32_t* device_view(const int32_t* p, bool allow_device) {
   return (device && !allow_device) ? nullptr : static_cast<int32_t*>(dev);
 }
 
+constexpr size_t kHeaderWords = 4;
+
 // Words of a step record for n sequences: the bookkeeping, the tile prefix
 // sums and room for the stream kernel's plan with `grid` workgroups.
 size_t record_words(int64_t n, int64_t stride, int64_t hkv, int64_t grid) {
-  const size_t w = size_t(n) * (5 + stride + 2 * hkv) + 1 + (grid ? 12 * grid + 2 : 0);
+  const size_t w = size_t(n) * (5 + stride + 2 * hkv) + 1 + kHeaderWords + (grid ? 12 * grid + 2 : 0);
   return (w + 3) / 4 * 4;
+}
+
+// Where the parts of a record for n sequences start.  The header holds the
+// copy-on-write pair count, the stream grid the plan was made for (0: no
+// plan), the cut-item count and the words in use.
+struct Layout {
+  size_t pre, header, plan;
+};
+Layout layout(int64_t n, int64_t stride) {
+  Layout l;
+  l.pre = size_t(4 * n + n * stride);
+  l.header = l.pre + size_t(n) + 1;
+  l.plan = l.header + kHeaderWords;
+  return l;
+}
+
+// The device part of a step (or of another layer's step on the same record):
+// phases bit 0 = copy-on-write copies and the KV write, bit 1 = the decode
+// pass, bit 2 = the merge.  With `stage`, bit 0 also copies the record from
+// its host view to stage_dev in the same launch as the KV write.
+pa_status run_device(const char* fn, const int32_t* stage_host, const int32_t* host_view, int32_t* stage_dev,
+                     int32_t n, int32_t table_stride, bool stage, void* k_cache, void* v_cache, const void* k_new,
+                     const void* v_new, const void* q, void* out, pa_dtype out_dtype, pa_dtype kv_dtype,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t num_blocks, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                     pa_kernel kernel, void* stream, int phases, void* pass_begin, void* pass_end,
+                     int32_t* d_times) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout lo = layout(n, table_stride);
+  const int32_t* hdr = stage_host + lo.header;
+  const int32_t ncow = hdr[0], grid = hdr[1], ncut = hdr[2];
+  const size_t words = (size_t(hdr[3]) + 3) / 4 * 4;
+  int32_t max_ctx = 0;
+  for (int32_t i = 0; i < n; ++i) max_ctx = std::max(max_ctx, stage_host[3 * n + i]);
+  if (phases & 1) {
+    if (!k_new || !v_new || (reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15u)
+      return pa::fail(PA_ERR_INVALID, "%s: k_new and v_new must be 16-byte aligned device memory", fn);
+    if (stage && host_view) {
+      // the kernels read the record where the host wrote it: copy-on-write
+      // copies, then one launch that copies the record to the device and
+      // writes the new tokens' keys and values
+      if (ncow) {
+        if (pa_status st = pa_copy_blocks(k_cache, v_cache, host_view + n, ncow, num_kv_heads, head_dim, block_size,
+                                          num_blocks, kv_dtype, stream))
+          return st;
+      }
+      if (pa_status st = pa_write_kv(k_cache, v_cache, k_new, v_new, stage_dev, 0, num_kv_heads, head_dim,
+                                     block_size, num_blocks, kv_dtype, stream))
+        return st;  // validates the cache arguments; writes nothing
+      if (hipError_t e = pa::launch_step_stage(host_view, stage_dev, static_cast<int64_t>(words), n, k_cache,
+                                               v_cache, k_new, v_new, num_kv_heads, head_dim, block_size,
+                                               kv_dtype == PA_F32 ? 4 : 2, s))
+        return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    } else {
+      if (stage) {
+        if (hipError_t e = hipMemcpyAsync(stage_dev, stage_host, words * sizeof(int32_t), hipMemcpyHostToDevice, s))
+          return pa::fail(PA_ERR_HIP, "%s: copy of the step record: %s", fn, hipGetErrorString(e));
+      }
+      if (ncow) {
+        if (pa_status st = pa_copy_blocks(k_cache, v_cache, stage_dev + n, ncow, num_kv_heads, head_dim, block_size,
+                                          num_blocks, kv_dtype, stream))
+          return st;
+      }
+      if (pa_status st = pa_write_kv(k_cache, v_cache, k_new, v_new, stage_dev, n, num_kv_heads, head_dim,
+                                     block_size, num_blocks, kv_dtype, stream))
+        return st;
+    }
+  }
+  const int32_t* d_ctx = stage_dev + 3 * n;
+  const int32_t* d_tables = stage_dev + 4 * n;
+  pa::StreamExtras ex{stage_dev + lo.pre, nullptr, nullptr, nullptr, nullptr, 0, d_times};
+  if (grid > 0) {
+    const int32_t* plan = stage_dev + lo.plan;
+    ex.wave_start = plan;
+    ex.cut_item = plan + 4 * int64_t(grid) + 1;
+    ex.cut_off = ex.cut_item + ncut;
+    ex.cut_workers = ex.cut_off + ncut + 1;
+    ex.num_cut = ncut;
+  }
+  if (phases & 2) {
+    if (pass_begin) {
+      if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(pass_begin), s))
+        return pa::fail(PA_ERR_HIP, "%s: event: %s", fn, hipGetErrorString(e));
+    }
+    if (pa_status st = pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, d_tables, table_stride, d_ctx,
+                                       max_ctx, n, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                       partition_size, workspace, workspace_bytes, stream, kernel, PA_PHASE_PASS,
+                                       &ex))
+      return st;
+    if (pass_end) {
+      if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(pass_end), s))
+        return pa::fail(PA_ERR_HIP, "%s: event: %s", fn, hipGetErrorString(e));
+    }
+  }
+  if (phases & 4)
+    return pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, d_tables, table_stride, d_ctx, max_ctx, n,
+                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
+                           workspace, workspace_bytes, stream, kernel, PA_PHASE_MERGE, &ex);
+  return PA_OK;
 }
 
 // The stream kernel's split, planned on the host and written at `out`:
@@ -183,79 +284,59 @@ pa_status pa_step(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* stage_host
   int32_t max_ctx = 0;
   for (int32_t i = 0; i < n; ++i) max_ctx = std::max(max_ctx, ctx[i]);
   if (max_ctx_out) *max_ctx_out = max_ctx;
-  // tile (16-token) prefix sums and the stream kernel's plan follow the tables
-  const size_t pre_at = 4 * static_cast<size_t>(n) + static_cast<size_t>(n) * table_stride;
-  int32_t* pre = stage_host + pre_at;
+  // tile (16-token) prefix sums, the header and the stream kernel's plan
+  // follow the tables
+  const Layout lo = layout(n, table_stride);
+  int32_t* pre = stage_host + lo.pre;
   pre[0] = 0;
   for (int32_t i = 0; i < n; ++i) pre[i + 1] = pre[i] + (ctx[i] + 15) / 16;
-  const size_t plan_at = pre_at + n + 1;
   int32_t ncut = 0;
   const bool planned = grid > 0 && int64_t(num_kv_heads) * pre[n] < (int64_t(1) << 31);
   const size_t plan_words =
-      planned ? build_plan(stage_host + plan_at, pre, n, num_kv_heads, grid, wg_weights, &ncut) : 0;
-  const size_t used = plan_at + plan_words;
+      planned ? build_plan(stage_host + lo.plan, pre, n, num_kv_heads, grid, wg_weights, &ncut) : 0;
+  int32_t* hdr = stage_host + lo.header;
+  hdr[0] = ncow;
+  hdr[1] = planned ? grid : 0;
+  hdr[2] = ncut;
+  hdr[3] = static_cast<int32_t>(lo.plan + plan_words);
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t words = (used + 3) / 4 * 4;
   const int32_t* host_view = (reinterpret_cast<uintptr_t>(stage_host) | reinterpret_cast<uintptr_t>(stage_dev)) & 15u
                                  ? nullptr
                                  : device_view(stage_host, false);
-  if (host_view) {
-    // the kernels read the record where the host wrote it: copy-on-write
-    // copies, then one launch that copies the record to the device and
-    // writes the new tokens' keys and values
-    if (ncow) {
-      if (pa_status st = pa_copy_blocks(k_cache, v_cache, host_view + n, ncow, num_kv_heads, head_dim, block_size,
-                                        num_blocks, kv_dtype, stream))
-        return st;
-    }
-    if (pa_status st = pa_write_kv(k_cache, v_cache, k_new, v_new, stage_dev, 0, num_kv_heads, head_dim, block_size,
-                                   num_blocks, kv_dtype, stream))
-      return st;  // validates the cache arguments; writes nothing
-    if (!k_new || !v_new || (reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15u)
-      return pa::fail(PA_ERR_INVALID, "%s: k_new and v_new must be 16-byte aligned device memory", fn);
-    if (hipError_t e = pa::launch_step_stage(host_view, stage_dev, static_cast<int64_t>(words), n, k_cache, v_cache,
-                                             k_new, v_new, num_kv_heads, head_dim, block_size,
-                                             kv_dtype == PA_F32 ? 4 : 2, s))
-      return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
-  } else {
-    if (hipError_t e = hipMemcpyAsync(stage_dev, stage_host, words * sizeof(int32_t), hipMemcpyHostToDevice, s))
-      return pa::fail(PA_ERR_HIP, "%s: copy of the step record: %s", fn, hipGetErrorString(e));
-    if (ncow) {
-      if (pa_status st = pa_copy_blocks(k_cache, v_cache, stage_dev + n, ncow, num_kv_heads, head_dim, block_size,
-                                        num_blocks, kv_dtype, stream))
-        return st;
-    }
-    if (pa_status st = pa_write_kv(k_cache, v_cache, k_new, v_new, stage_dev, n, num_kv_heads, head_dim,
-                                   block_size, num_blocks, kv_dtype, stream))
-      return st;
-  }
-  if (pass_begin) {
-    if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(pass_begin), s))
-      return pa::fail(PA_ERR_HIP, "%s: event: %s", fn, hipGetErrorString(e));
-  }
-  const int32_t* d_ctx = stage_dev + 3 * n;
-  const int32_t* d_tables = stage_dev + 4 * n;
-  pa::StreamExtras ex{stage_dev + pre_at, nullptr, nullptr, nullptr, nullptr, 0, d_times};
-  if (planned) {
-    const int32_t* plan = stage_dev + plan_at;
-    ex.wave_start = plan;
-    ex.cut_item = plan + 4 * int64_t(grid) + 1;
-    ex.cut_off = ex.cut_item + ncut;
-    ex.cut_workers = ex.cut_off + ncut + 1;
-    ex.num_cut = ncut;
-  }
-  if (pa_status st = pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, d_tables, table_stride, d_ctx,
-                                     max_ctx, n, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
-                                     partition_size, workspace, workspace_bytes, stream, kernel, PA_PHASE_PASS, &ex))
+  return run_device(fn, stage_host, host_view, stage_dev, n, table_stride, true, k_cache, v_cache, k_new, v_new, q,
+                    out, out_dtype, kv_dtype, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                    partition_size, workspace, workspace_bytes, kernel, stream, 7, pass_begin, pass_end, d_times);
+}
+
+pa_status pa_step_layer(const int32_t* stage_host, int32_t* stage_dev, int32_t n, int32_t table_stride,
+                        void* k_cache, void* v_cache, const void* k_new, const void* v_new, const void* q, void* out,
+                        pa_dtype out_dtype, pa_dtype kv_dtype, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
+                        void* workspace, size_t workspace_bytes, pa_kernel kernel, void* stream, int32_t phases,
+                        void* pass_begin, void* pass_end, int32_t* wave_times) {
+  const char* fn = "pa_step_layer";
+  if (!stage_host || !stage_dev || n <= 0 || table_stride <= 0 || phases < 1 || phases > 7)
+    return pa::fail(PA_ERR_INVALID, "%s: bad arguments", fn);
+  const Layout lo = layout(n, table_stride);
+  const int32_t* hdr = stage_host + lo.header;
+  const int32_t grid = pa::stream_grid_selected(kernel, kv_dtype, n, num_q_heads, num_kv_heads, head_dim);
+  if (hdr[0] < 0 || hdr[0] > n || hdr[2] < 0 || hdr[2] > int64_t(n) * num_kv_heads ||
+      size_t(hdr[3]) < lo.plan || (hdr[1] != 0 && hdr[1] != grid))
+    return pa::fail(PA_ERR_INVALID, "%s: the record does not match this shape and kernel", fn);
+  int32_t max_ctx = 0;
+  for (int32_t i = 0; i < n; ++i) max_ctx = std::max(max_ctx, stage_host[3 * n + i]);
+  if (pa_status st = pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, stage_dev, table_stride,
+                                     stage_dev, max_ctx, n, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     num_blocks, scale, partition_size, workspace, workspace_bytes, stream, kernel, 0,
+                                     nullptr))
     return st;
-  if (pass_end) {
-    if (hipError_t e = hipEventRecord(static_cast<hipEvent_t>(pass_end), s))
-      return pa::fail(PA_ERR_HIP, "%s: event: %s", fn, hipGetErrorString(e));
-  }
-  return pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, d_tables, table_stride, d_ctx, max_ctx, n,
-                         num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size,
-                         workspace, workspace_bytes, stream, kernel, PA_PHASE_MERGE, &ex);
+  int32_t* d_times = nullptr;
+  if (wave_times && !(d_times = device_view(wave_times, true)))
+    return pa::fail(PA_ERR_INVALID, "%s: wave_times is neither pinned host nor device memory", fn);
+  return run_device(fn, stage_host, nullptr, stage_dev, n, table_stride, false, k_cache, v_cache, k_new, v_new, q,
+                    out, out_dtype, kv_dtype, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                    partition_size, workspace, workspace_bytes, kernel, stream, phases, pass_begin, pass_end,
+                    d_times);
 }
 
 }  // extern "C"

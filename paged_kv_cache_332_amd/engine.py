@@ -16,8 +16,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (PA_KERNEL_AUTO, PA_KERNEL_STREAM, BlockManager, alloc_cache, pa_copy_blocks, pa_decode_stream_grid,
-               pa_decode_variant, pa_decode_workspace_bytes, pa_step, pa_write_kv, step_record_words)
+from . import (PA_KERNEL_AUTO, PA_KERNEL_STREAM, STEP_ALL, BlockManager, alloc_cache, pa_copy_blocks, pa_decode_stream_grid,
+               pa_decode_variant, pa_decode_workspace_bytes, pa_step, pa_step_layer, pa_write_kv,
+               step_record_words)
 
 __all__ = ["PagedKVEngine", "rebalance"]
 
@@ -266,5 +267,19 @@ class PagedKVEngine:
         st.times_key = None if w is None else ((n, q.shape[1]), self._wver[(n, q.shape[1])])
         (hs, hp, hc, ht), _, _ = st.packed(n)
         self.last_tables, self.last_ctx, self.last_max_ctx = ht.numpy(), hc.numpy(), max_ctx
+        self._last = (st, n, kernel, partition_size)
         self._record(st, stream)
+        return out
+
+    def step_layer(self, k_cache, v_cache, k_new, v_new, q, out, phases: int = STEP_ALL, stream=None,
+                   pass_events=None) -> torch.Tensor:
+        """The device part of the last step again for another layer: its own
+        pools (shaped like this engine's), new keys/values, queries and output,
+        on the same sequences, slots, tables and split.  Must come before the
+        next step() (which may reuse the record)."""
+        stream = stream or torch.cuda.current_stream()
+        st, n, kernel, partition_size = self._last
+        ws = self.workspace(n, q.shape[1], self.stride * self.BS, partition_size)
+        pa_step_layer(st.h, st.d, n, self.stride, k_cache, v_cache, k_new, v_new, q, out, 1.0 / float(self.D) ** 0.5,
+                      partition_size, ws if ws.numel() else None, kernel, stream, phases, pass_events)
         return out

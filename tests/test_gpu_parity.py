@@ -351,3 +351,42 @@ def test_stream_weights(case):
     t = st.times[: 8 * g].numpy().astype(np.int64).reshape(g, 4, 2)
     span = (t[:, :, 1] - t[:, :, 0] + (1 << 31)) % (1 << 32) - (1 << 31)
     assert (span >= 0).all() and span.max() > 0
+
+
+@pytest.mark.parametrize("kern", ["auto", "mfma"])
+def test_step_layer_reuses_the_record(kern):
+    """A second layer run on the last step's record (pa_step_layer: its own
+    pools, new tokens and queries; the same slots, tables and split): with a
+    copy of the first layer's pools it reproduces the first layer's output
+    bit for bit, and with every value of V negated (pool and new token) it
+    gives the negated output, so it reads its own pools (to 1e-6: the matrix
+    cores' accumulation need not round symmetrically about zero).  The first
+    layer matches the oracle."""
+    pa, runner = _pa()
+    ctx = [700, 33, 1500, 16, 2049, 5]
+    w = W.tiny(num_seqs=len(ctx), dtype="bf16", seed=31, ctx=ctx, num_q_heads=16, num_kv_heads=4, head_dim=128,
+               block_size=16)
+    say("step layer", kern)
+    ref = oracle.run_scenario(w)
+    dev = runner.run_script(w, use_step=True, kernel=KERNELS[kern])
+    check_run(w, dev, ref, label=f"layer 0 {kern}")
+    eng = dev.engine
+    seqs = dev.decodes[-1].seqs
+    a = dev.appends[-1]
+    rows = np.array([w.row_of(s, np.array([p]))[0] for s, p in zip(a["seqs"], a["pos"])], dtype=np.int64)
+    idx = torch.from_numpy(rows).to("cuda")
+    k_new, v_new = dev.k_dev[idx].contiguous(), dev.v_dev[idx].contiguous()
+    q = dev.q_dev[dev.decodes[-1].q_index][torch.tensor(seqs, device="cuda")].contiguous()
+    out0 = dev.decodes[-1].out
+    kb, vb = eng.k_cache.clone(), eng.v_cache.clone()
+    out1 = torch.empty_like(out0)
+    eng.step_layer(kb, vb, k_new, v_new, q, out1)
+    vn = -eng.v_cache
+    out2 = torch.empty_like(out0)
+    eng.step_layer(eng.k_cache.clone(), vn, k_new, (-v_new).contiguous(), q, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out0)
+    err = float((out2 + out0).abs().max())
+    say("negated V: max |out2 + out0|", err)
+    assert err <= 1e-6 and float(out0.abs().max()) > 0.1
+    assert torch.equal(kb.view(torch.int16), eng.k_cache.view(torch.int16))
