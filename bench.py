@@ -49,6 +49,7 @@ def parse():
                     help="time the decode pass with HIP events on every k-th timed step (an event packet "
                          "between kernels costs the stream ~4 us, so sparse timing keeps the step intact)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", type=int, default=8, help="passes timed after evicting the Infinity Cache")
     ap.add_argument("--burst", type=int, default=16,
                     help="back-to-back pass launches timed for the roofline's launch duration")
     ap.add_argument("--no-balance", action="store_true",
@@ -230,6 +231,22 @@ def main():
     burst_us = b0.elapsed_time(b1) * 1e3 / args.burst
     burst_bytes = decode_bytes(step_ctx[-1], cfg, esize)
     achieved = float(burst_bytes / (burst_us * 1e-6) / 1e9)
+
+    # the same pass with a cold Infinity Cache: 1 GiB read before each one, so
+    # the cache holds clean lines of another buffer (a write would leave dirty
+    # lines whose write-back lands in the pass); the read is outside the events
+    cold_us = []
+    if args.cold:
+        scrub = torch.zeros(1 << 27, dtype=torch.int64, device="cuda")
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(args.cold):
+            scrub.sum()
+            c0.record(stream)
+            eng.step_layer(eng.k_cache, eng.v_cache, None, None, q, out, phases=pa.STEP_PASS, stream=stream)
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold_us.append(c0.elapsed_time(c1) * 1e3)
+        del scrub
     value = kv_total / elapsed / 1e9
     kname = ("stream" if kernel in (pa.PA_KERNEL_AUTO, pa.PA_KERNEL_STREAM) and cfg.dtype != "f32"
              else args.kernel if args.kernel != "auto" else "valu")
@@ -260,6 +277,13 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(kname, args.config), "avg_launch_us": round(burst_us, 2),
                      "bytes_per_launch": int(burst_bytes), "timed_launches": args.burst,
+                     "cold": None if not cold_us else {
+                         "median_us": round(float(np.median(cold_us)), 2),
+                         "GBps": round(burst_bytes / (float(np.median(cold_us)) * 1e-6) / 1e9, 2),
+                         "launches": len(cold_us),
+                         "note": "one pass after reading 1 GiB of another buffer (Infinity Cache evicted); "
+                                 "events around the pass alone, so the figure includes one event packet's "
+                                 "latency"},
                      "in_step": {"mean_us": round(float(dec_ms.mean()) * 1e3, 2),
                                  "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                                  "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
