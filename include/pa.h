@@ -253,7 +253,7 @@ pa_status pa_bm_stats(const pa_bm* bm, int64_t* out);
  *   2. pa_bm_export of the grown tables and context lengths;
  *   3. the step record, laid out in int32 words as
  *      [slots n | copy pairs 2n | context lengths n | tables n * table_stride
- *       | tile prefix sums n + 1 | header 4 | stream plan]
+ *       | tile prefix sums n + 1 | header 4 | stream plan (16-byte aligned)]
  *      (the header: copy-on-write pairs, the stream grid of the plan or 0,
  *      cut items, words in use)
  *      (rounded up to a multiple of 4 words), goes from stage_host (pinned
@@ -319,11 +319,15 @@ size_t pa_step_record_words(int32_t max_seqs, int32_t table_stride, int32_t num_
 /* The stream plan pa_step writes into its record, computed on the host for
  * inspection: tile_prefix[n + 1] (tiles of 16 tokens of the sequences before
  * each one; non-decreasing from 0), `grid` workgroups (1..1024) with weights
- * (NULL = equal).  Writes into out (out_words >= 4 grid + 1 + 2 n
- * num_kv_heads + 1 + 8 grid): the first tile of each of the 4 grid waves and
- * the end, the cut items (2 * (seq * num_kv_heads + kvh) + 1 when the item's
- * first wave starts before it), their num_cut + 1 offsets and the waves of
- * each.  Returns the words written, or -1 for bad arguments. */
+ * (NULL = equal).  Writes into out (out_words >= E + 8 n num_kv_heads +
+ * 8 grid, E = 4 grid + 1 rounded up to a multiple of 4): the first tile of
+ * each of the 4 grid waves and the end; from word E on, one 8-word entry per
+ * item whose tiles fall to more than one wave, {2 * (seq * num_kv_heads +
+ * kvh) + 1 when the item's first wave starts before it, its number of waves,
+ * the offset of the first in the wave list, the first four waves (0 past the
+ * count), 0}; then the wave list (every cut item's waves, in order).
+ * *num_cut receives the entries.  Returns the words written, or -1 for bad
+ * arguments. */
 int64_t pa_stream_plan(const int32_t* tile_prefix, int32_t n, int32_t num_kv_heads, int32_t grid,
                        const int32_t* weights, int32_t* out, size_t out_words, int32_t* num_cut);
 

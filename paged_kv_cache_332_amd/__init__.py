@@ -259,10 +259,11 @@ def pa_decode_stream_grid(num_seqs: int, num_q_heads: int, num_kv_heads: int, he
 
 def pa_stream_plan(tile_prefix: np.ndarray, num_kv_heads: int, grid: int, weights: Optional[np.ndarray] = None):
     """The stream plan of pa_step for these tile counts: (wave starts [4 grid
-    + 1], cut item codes, offsets, waves)."""
+    + 1], cut-item entries [ncut][8], wave list)."""
     pre = np.ascontiguousarray(tile_prefix, dtype=np.int32)
     n = pre.shape[0] - 1
-    cap = 4 * grid + 1 + 2 * n * num_kv_heads + 1 + 8 * grid
+    at = -(-(4 * grid + 1) // 4) * 4
+    cap = at + 8 * n * num_kv_heads + 8 * grid
     out = np.zeros(cap, dtype=np.int32)
     ncut = ctypes.c_int32(0)
     w = None if weights is None else np.ascontiguousarray(weights, dtype=np.int32)
@@ -271,12 +272,8 @@ def pa_stream_plan(tile_prefix: np.ndarray, num_kv_heads: int, grid: int, weight
                                ctypes.byref(ncut))
     if words < 0:
         raise PAError(1, "pa_stream_plan: bad arguments")
-    nw, k = 4 * grid, int(ncut.value)
-    starts = out[: nw + 1]
-    items = out[nw + 1: nw + 1 + k]
-    offs = out[nw + 1 + k: nw + 2 + 2 * k]
-    waves = out[nw + 2 + 2 * k: int(words)]
-    return starts, items, offs, waves
+    k = int(ncut.value)
+    return out[: 4 * grid + 1], out[at: at + 8 * k].reshape(k, 8), out[at + 8 * k: int(words)]
 
 
 def step_record_words(max_seqs: int, table_stride: int, num_kv_heads: int) -> int:

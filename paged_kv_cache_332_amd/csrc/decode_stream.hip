@@ -517,8 +517,7 @@ __device__ __forceinline__ void merge_item(const StreamArgs& sa, int seq, int kv
   const int G = Hq / Hkv;
   const int64_t row0 = int64_t(seq) * Hq + int64_t(kvh) * G;
   // each lane merges units idx = lane + 64 u (4 output columns each) of the
-  // G x D item; a batch's loads are in flight together (two round trips per
-  // batch: maxima, then sums and partial outputs)
+  // G x D item; a batch's loads are in flight together
   constexpr int NU = (GMAX * D / 4 + 63) / 64;
   constexpr int R = 4;
   const int units = G * (D / 4);
@@ -542,14 +541,7 @@ __device__ __forceinline__ void merge_item(const StreamArgs& sa, int seq, int kv
       more = live[r];
       wr[r] = live[r] ? x : w0;
     }
-    float m[R][NU];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int idx = lane + 64 * u;
-        m[r][u] = idx < units ? sa.rec_ml[rec_of(wr[r], idx / (D / 4)) * 2] : 0.f;
-      }
+    // one round trip per batch: every record's (max, sum) and partial output
     float2 ml[R][NU];
     f32x4 v[R][NU];
 #pragma unroll
@@ -566,7 +558,7 @@ __device__ __forceinline__ void merge_item(const StreamArgs& sa, int seq, int kv
       float mb = M[u];
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (live[r]) mb = fmaxf(mb, m[r][u]);
+        if (live[r]) mb = fmaxf(mb, ml[r][u].x);
       const float c0 = M[u] == kNegInf ? 0.f : fast_exp2(M[u] - mb);
       L[u] *= c0;
       O[u] *= c0;
@@ -652,19 +644,22 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa, int32_t
   });
 }
 
-// Merge with the host plan: one wave per cut item, which reads the item and
-// its waves from the plan.
+// Merge with the host plan: one wave per cut item.  Its plan entry (one
+// 32-byte load) holds the item, its wave count, the offset of its waves in
+// the full list and the first four of them, so an item cut over at most
+// four waves needs one round trip for the entry and one for the records.
 template <class T, int D, int GMAX>
 __global__ __launch_bounds__(64) void stream_merge_planned_kernel(StreamArgs sa) {
-  const int k = blockIdx.x;
-  const int code = sa.cut_item[k];
+  const int4* e = reinterpret_cast<const int4*>(sa.cut_entry + 8 * int64_t(blockIdx.x));
+  const int4 e0 = e[0], e1 = e[1];            // {code, count, off, w0}, {w1, w2, w3, -}
+  const int code = e0.x, count = e0.y, off = e0.z;
   const int item = code >> 1;
   const int Hkv = sa.d.num_kv_heads;
-  int i = sa.cut_off[k];
-  const int end = sa.cut_off[k + 1];
-  merge_item<T, D, GMAX>(sa, item / Hkv, item % Hkv, sa.cut_workers[i], code & 1, [&](int64_t& x) {
-    if (i >= end) return false;
-    x = sa.cut_workers[i++];
+  int i = 0;
+  merge_item<T, D, GMAX>(sa, item / Hkv, item % Hkv, e0.w, code & 1, [&](int64_t& x) {
+    if (i >= count) return false;
+    x = i == 0 ? e0.w : i == 1 ? e1.x : i == 2 ? e1.y : i == 3 ? e1.z : sa.cut_workers[off + i];
+    ++i;
     return true;
   });
 }
@@ -703,7 +698,7 @@ static hipError_t launch_s(const StreamArgs& sa, size_t lds, int grid, int phase
     if (e != hipSuccess) return e;
   }
   if (!(phases & 2)) return hipSuccess;
-  if (sa.cut_item) {
+  if (sa.cut_entry) {
     if (sa.num_cut <= 0) return hipSuccess;
     hipLaunchKernelGGL((stream_merge_planned_kernel<T, D, GMAX>), dim3(static_cast<uint32_t>(sa.num_cut)), dim3(64),
                        0, stream, sa);

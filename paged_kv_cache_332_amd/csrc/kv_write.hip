@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void step_stage_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ rec_dev, int64_t words, int32_t n,
                                                          u32x4* __restrict__ kc, Bits* __restrict__ vc,
                                                          const u32x4* __restrict__ kn, const Bits* __restrict__ vn,
-                                                         int32_t hkv, int32_t d, int32_t bs) {
+                                                         int32_t hkv, int32_t d, int32_t bs, StageSlots sl) {
   if (blockIdx.x >= n) {
     const int64_t units = words / 4;                  // words is a multiple of 4
     const u32x4* src = reinterpret_cast<const u32x4*>(rec_host);
@@ -80,7 +80,9 @@ __global__ __launch_bounds__(256) void step_stage_kernel(const int32_t* __restri
     return;
   }
   const int64_t t = blockIdx.x;
-  const int32_t s = rec_host[t];
+  // the slot travels in the launch arguments when it fits (no host-memory
+  // round trip before the writes), else it is read from the record
+  const int32_t s = n <= kStageArgSlots ? sl.slot[t] : rec_host[t];
   if (s < 0) return;
   const int64_t blk = s / bs;
   const int32_t off = s % bs;
@@ -100,18 +102,20 @@ __global__ __launch_bounds__(256) void step_stage_kernel(const int32_t* __restri
 
 hipError_t launch_step_stage(const int32_t* rec_host, int32_t* rec_dev, int64_t words, int32_t n, void* k_cache,
                              void* v_cache, const void* k_new, const void* v_new, int32_t hkv, int32_t d,
-                             int32_t bs, int32_t elem_bytes, hipStream_t stream) {
+                             int32_t bs, int32_t elem_bytes, const int32_t* slots_host, hipStream_t stream) {
   const int64_t units = words / 4;
   const int32_t copiers = static_cast<int32_t>(std::min<int64_t>(64, std::max<int64_t>(1, (units + 255) / 256)));
   dim3 grid(n + copiers), block(256);
+  StageSlots sl;
+  if (n <= kStageArgSlots) std::copy(slots_host, slots_host + n, sl.slot);
   if (elem_bytes == 2) {
     hipLaunchKernelGGL(step_stage_kernel<uint16_t>, grid, block, 0, stream, rec_host, rec_dev, words, n,
                        static_cast<u32x4*>(k_cache), static_cast<uint16_t*>(v_cache),
-                       static_cast<const u32x4*>(k_new), static_cast<const uint16_t*>(v_new), hkv, d, bs);
+                       static_cast<const u32x4*>(k_new), static_cast<const uint16_t*>(v_new), hkv, d, bs, sl);
   } else {
     hipLaunchKernelGGL(step_stage_kernel<uint32_t>, grid, block, 0, stream, rec_host, rec_dev, words, n,
                        static_cast<u32x4*>(k_cache), static_cast<uint32_t*>(v_cache),
-                       static_cast<const u32x4*>(k_new), static_cast<const uint32_t*>(v_new), hkv, d, bs);
+                       static_cast<const u32x4*>(k_new), static_cast<const uint32_t*>(v_new), hkv, d, bs, sl);
   }
   return hipGetLastError();
 }

@@ -263,8 +263,7 @@ pa_status decode_impl(void* out, pa_dtype out_dtype, const void* q, const void* 
       if (extras) {
         sa.pre_in = extras->pre;
         sa.wave_start = extras->wave_start;
-        sa.cut_item = extras->cut_item;
-        sa.cut_off = extras->cut_off;
+        sa.cut_entry = extras->cut_entry;
         sa.cut_workers = extras->cut_workers;
         sa.num_cut = extras->num_cut;
         sa.wave_time = extras->wave_time;

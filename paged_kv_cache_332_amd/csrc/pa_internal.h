@@ -16,8 +16,7 @@ pa_status fail(pa_status st, const char* fmt, ...);
 struct StreamExtras {
   const int32_t* pre;          // [B + 1] tiles (16 tokens) of the sequences before each one
   const int32_t* wave_start;   // [grid * 4 + 1] first tile of each wave
-  const int32_t* cut_item;     // [num_cut] 2 * item + (1 if its first wave starts before it)
-  const int32_t* cut_off;      // [num_cut + 1] offsets into cut_workers
+  const int32_t* cut_entry;    // [num_cut][8] item code, wave count, offset, first four waves
   const int32_t* cut_workers;  // the waves of each cut item, in order
   int32_t num_cut;
   int32_t* wave_time;          // [grid * 4][2] wave start and end stamps, 10 ns units (written)

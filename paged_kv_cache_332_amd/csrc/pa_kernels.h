@@ -37,8 +37,8 @@ struct StreamArgs {
   // optional host plan (all null: the kernels derive an equal split themselves)
   const int32_t* pre_in;         // [B + 1] tiles of the sequences before each one
   const int32_t* wave_start;     // [grid * 4 + 1] first tile of each wave, non-decreasing, last = all tiles
-  const int32_t* cut_item;       // [num_cut] 2 * (seq * Hkv + kvh) + (1 if its first wave starts before it)
-  const int32_t* cut_off;        // [num_cut + 1] offsets into cut_workers
+  const int32_t* cut_entry;      // [num_cut][8] {2 * (seq * Hkv + kvh) + (1 if its first wave starts before
+                                 // it), its wave count, offset in cut_workers, first four waves}
   const int32_t* cut_workers;    // waves with tiles of each cut item, in order
   int32_t num_cut;
   int32_t* wave_time;            // [grid * 4][2] start and end of each wave (low 32 bits of the
@@ -66,10 +66,16 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
                            int32_t bs, int32_t elem_bytes, hipStream_t stream);
 
 // Step record copy (pinned host -> device, `words` a multiple of 4) fused with
-// the KV write of its n tokens (slots = the record's first n words).
+// the KV write of its n tokens (slots = the record's first n words; up to
+// kStageArgSlots of them, read on the host through slots_host, travel in the
+// launch arguments).
+constexpr int kStageArgSlots = 512;
+struct StageSlots {
+  int32_t slot[kStageArgSlots];
+};
 hipError_t launch_step_stage(const int32_t* rec_host, int32_t* rec_dev, int64_t words, int32_t n, void* k_cache,
                              void* v_cache, const void* k_new, const void* v_new, int32_t hkv, int32_t d,
-                             int32_t bs, int32_t elem_bytes, hipStream_t stream);
+                             int32_t bs, int32_t elem_bytes, const int32_t* slots_host, hipStream_t stream);
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                               int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,

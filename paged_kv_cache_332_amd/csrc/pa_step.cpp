@@ -51,10 +51,16 @@ int32_t* device_view(const int32_t* p, bool allow_device) {
 
 constexpr size_t kHeaderWords = 4;
 
+// Word where the cut-item entries start in a plan for `grid` workgroups
+// (after the 4 grid + 1 wave starts, rounded up to 4 words).
+size_t plan_entries(int64_t grid) { return size_t(4 * grid + 1 + 3) / 4 * 4; }
+
 // Words of a step record for n sequences: the bookkeeping, the tile prefix
 // sums and room for the stream kernel's plan with `grid` workgroups.
 size_t record_words(int64_t n, int64_t stride, int64_t hkv, int64_t grid) {
-  const size_t w = size_t(n) * (5 + stride + 2 * hkv) + 1 + kHeaderWords + (grid ? 12 * grid + 2 : 0);
+  // (the plan: wave starts padded to 4 words, an 8-word entry per cut item,
+  // at most two cut items per wave in the full wave list)
+  const size_t w = size_t(n) * (5 + stride + 8 * hkv) + 1 + kHeaderWords + 3 + (grid ? 12 * grid + 4 : 0);
   return (w + 3) / 4 * 4;
 }
 
@@ -68,7 +74,7 @@ Layout layout(int64_t n, int64_t stride) {
   Layout l;
   l.pre = size_t(4 * n + n * stride);
   l.header = l.pre + size_t(n) + 1;
-  l.plan = l.header + kHeaderWords;
+  l.plan = (l.header + kHeaderWords + 3) / 4 * 4;  // 16-byte aligned, as are the entries
   return l;
 }
 
@@ -107,7 +113,7 @@ pa_status run_device(const char* fn, const int32_t* stage_host, const int32_t* h
         return st;  // validates the cache arguments; writes nothing
       if (hipError_t e = pa::launch_step_stage(host_view, stage_dev, static_cast<int64_t>(words), n, k_cache,
                                                v_cache, k_new, v_new, num_kv_heads, head_dim, block_size,
-                                               kv_dtype == PA_F32 ? 4 : 2, s))
+                                               kv_dtype == PA_F32 ? 4 : 2, stage_host, s))
         return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     } else {
       if (stage) {
@@ -126,13 +132,12 @@ pa_status run_device(const char* fn, const int32_t* stage_host, const int32_t* h
   }
   const int32_t* d_ctx = stage_dev + 3 * n;
   const int32_t* d_tables = stage_dev + 4 * n;
-  pa::StreamExtras ex{stage_dev + lo.pre, nullptr, nullptr, nullptr, nullptr, 0, d_times};
+  pa::StreamExtras ex{stage_dev + lo.pre, nullptr, nullptr, nullptr, 0, d_times};
   if (grid > 0) {
     const int32_t* plan = stage_dev + lo.plan;
     ex.wave_start = plan;
-    ex.cut_item = plan + 4 * int64_t(grid) + 1;
-    ex.cut_off = ex.cut_item + ncut;
-    ex.cut_workers = ex.cut_off + ncut + 1;
+    ex.cut_entry = plan + plan_entries(grid);
+    ex.cut_workers = ex.cut_entry + 8 * int64_t(ncut);
     ex.num_cut = ncut;
   }
   if (phases & 2) {
@@ -161,12 +166,13 @@ pa_status run_device(const char* fn, const int32_t* stage_host, const int32_t* h
 //   wave starts [4 grid + 1]: workgroup b takes tiles [T P_b / P, T P_(b+1) / P)
 //     of the T = Hkv * pre[n] tiles (P_b the sum of the weights before it,
 //     P their total), split evenly over its four waves;
-//   cut items [ncut]: 2 * (seq * Hkv + kvh) + (1 when the first wave holding
-//     the item started before it), for every item whose tiles fall to more
-//     than one wave;
-//   offsets [ncut + 1] into the list of those waves (non-empty ones only, in
-//     order), and the list.
-// Returns the words written (0 when there are no tiles); sets *ncut_out.
+//   then, from word plan_entries(grid) on (a multiple of 4), one 8-word entry
+//     per item whose tiles fall to more than one wave: {2 * (seq * Hkv +
+//     kvh) + (1 when the first wave holding the item started before it), the
+//     number of those waves (non-empty ones only), the offset of the first in
+//     the wave list, the first four of them (0 past the count), 0};
+//   the wave list: every cut item's waves in order.
+// Returns the words written; sets *ncut_out.
 size_t build_plan(int32_t* out, const int32_t* pre, int32_t n, int32_t hkv, int32_t grid, const int32_t* weights,
                   int32_t* ncut_out) {
   const int64_t total = int64_t(hkv) * pre[n];
@@ -184,9 +190,8 @@ size_t build_plan(int32_t* out, const int32_t* pre, int32_t n, int32_t hkv, int3
   }
   S[nw] = static_cast<int32_t>(total);
   // items in tile order, with the wave holding their first and last tile
-  static thread_local std::vector<int32_t> items, offs, waves;
-  items.clear();
-  offs.clear();
+  static thread_local std::vector<int32_t> entries, waves;
+  entries.clear();
   waves.clear();
   int64_t w = 0;  // the last wave starting at or before the current tile
   for (int32_t s = 0; s < n; ++s) {
@@ -198,22 +203,30 @@ size_t build_plan(int32_t* out, const int32_t* pre, int32_t n, int32_t hkv, int3
       int64_t wh = w;
       while (wh + 1 < nw && S[wh + 1] <= gs + nt - 1) ++wh;
       if (wh != w) {
-        items.push_back(static_cast<int32_t>(2 * (int64_t(s) * hkv + h) + (S[w] < gs ? 1 : 0)));
-        offs.push_back(static_cast<int32_t>(waves.size()));
+        const size_t off = waves.size();
         for (int64_t x = w; x <= wh; ++x)
           if (S[x] < S[x + 1]) waves.push_back(static_cast<int32_t>(x));
+        const int32_t cnt = static_cast<int32_t>(waves.size() - off);
+        const int32_t e[8] = {static_cast<int32_t>(2 * (int64_t(s) * hkv + h) + (S[w] < gs ? 1 : 0)),
+                              cnt,
+                              static_cast<int32_t>(off),
+                              waves[off],
+                              cnt > 1 ? waves[off + 1] : 0,
+                              cnt > 2 ? waves[off + 2] : 0,
+                              cnt > 3 ? waves[off + 3] : 0,
+                              0};
+        entries.insert(entries.end(), e, e + 8);
       }
       w = wh;
     }
   }
-  offs.push_back(static_cast<int32_t>(waves.size()));
-  const size_t ncut = items.size();
-  int32_t* p = out + nw + 1;
-  std::copy(items.begin(), items.end(), p);
-  std::copy(offs.begin(), offs.end(), p + ncut);
-  std::copy(waves.begin(), waves.end(), p + 2 * ncut + 1);
+  const size_t ncut = entries.size() / 8;
+  const size_t at = plan_entries(grid);
+  std::fill(out + nw + 1, out + at, 0);
+  std::copy(entries.begin(), entries.end(), out + at);
+  std::copy(waves.begin(), waves.end(), out + at + entries.size());
   *ncut_out = static_cast<int32_t>(ncut);
-  return size_t(nw) + 1 + 2 * ncut + 1 + waves.size();
+  return at + entries.size() + waves.size();
 }
 
 }  // namespace
@@ -228,7 +241,7 @@ int64_t pa_stream_plan(const int32_t* tile_prefix, int32_t n, int32_t num_kv_hea
   for (int32_t i = 0; i < n; ++i)
     if (tile_prefix[i + 1] < tile_prefix[i]) return -1;
   if (int64_t(num_kv_heads) * tile_prefix[n] >= (int64_t(1) << 31)) return -1;
-  if (out_words < size_t(4 * grid + 1) + 2 * size_t(n) * num_kv_heads + 1 + 8 * size_t(grid)) return -1;
+  if (out_words < plan_entries(grid) + 8 * size_t(n) * num_kv_heads + 8 * size_t(grid)) return -1;
   return static_cast<int64_t>(build_plan(out, tile_prefix, n, num_kv_heads, grid, weights, num_cut));
 }
 

@@ -304,7 +304,7 @@ def test_stream_plan_matches_brute_force(ctx, hkv, grid, weighted, seed):
     pre = np.concatenate([[0], np.cumsum(tiles)]).astype(np.int32)
     rng = np.random.default_rng(seed)
     wts = rng.integers(-3, 70000, size=grid).astype(np.int32) if weighted else None
-    starts, items, offs, waves = pa.pa_stream_plan(pre, hkv, grid, wts)
+    starts, entries, wave_list = pa.pa_stream_plan(pre, hkv, grid, wts)
     total = hkv * int(pre[-1])
     nw = 4 * grid
     # shares: workgroup b holds [T P_b / P, T P_(b+1) / P), quartered
@@ -324,10 +324,16 @@ def test_stream_plan_matches_brute_force(ctx, hkv, grid, weighted, seed):
             own = sorted(set(owner[gs: gs + nt].tolist()))
             if len(own) > 1:
                 expect.append((2 * (s * hkv + h) + int(starts[own[0]] < gs), own))
-    assert len(items) == len(expect) and offs[0] == 0
+    assert len(entries) == len(expect)
+    off = 0
     for k, (code, own) in enumerate(expect):
-        assert items[k] == code
-        assert waves[offs[k]: offs[k + 1]].tolist() == own
+        code_k, cnt, off_k = (int(x) for x in entries[k, :3])
+        assert (code_k, cnt, off_k) == (code, len(own), off)
+        assert wave_list[off: off + cnt].tolist() == own
+        inline = (own + [0, 0, 0])[:4]
+        assert entries[k, 3:7].tolist() == inline and entries[k, 7] == 0
+        off += cnt
+    assert off == len(wave_list)
 
 
 def test_stream_plan_rejects_bad_input():
