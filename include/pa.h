@@ -235,6 +235,19 @@ pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t 
 /* Free blocks: the headroom a server can admit against ([VM] §What it buys
  * in practice). */
 int32_t pa_bm_num_free(const pa_bm* bm);
+/* Admission that keeps headroom ([VM] §What it buys in practice: memory is
+ * handed out in small increments, so a server can admit without committing to
+ * a request's worst case and can tell how close it is to the ceiling):
+ * pa_bm_add_seq only if the blocks of num_tokens plus reserve_blocks (room the
+ * caller keeps for the growth of live sequences) are free; else PA_ERR_OOM
+ * and nothing changes. */
+pa_status pa_bm_admit(pa_bm* bm, int64_t seq, int32_t num_tokens, int32_t reserve_blocks, int32_t* slots_out);
+/* Occupancy in token slots ([VM] §The fix borrowed from operating systems:
+ * at most one partly filled block per request):
+ * out[4] = {slots of the blocks held (shared blocks once), tokens of all
+ * sequences (shared tokens once per sequence), unused slots in the sequences'
+ * last blocks, free slots}. */
+pa_status pa_bm_occupancy(const pa_bm* bm, int64_t* out);
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);      /* -1 if out of range */
 int32_t pa_bm_seq_len(const pa_bm* bm, int64_t seq);         /* -1 if unknown */
 int32_t pa_bm_num_seqs(const pa_bm* bm);

@@ -30,12 +30,18 @@ What it computes, and from which passage:
   layout, written token by token through slots and copied block by block.
 * ``scenario`` — runs a workload's construction script through the model and
   the cache and returns every integer result and the expected outputs.
+* ``accounting`` — the unused fraction of a cache reserved for the longest
+  context per request against the last-block slack of blocks taken on demand,
+  and the headroom admission test ("Paged Attention as a Memory Manager",
+  §The KV-Cache Fragmentation Problem; "Paged Attention: Virtual Memory for the
+  KV Cache", §The fix borrowed from operating systems, §What it buys in
+  practice).
 
 Every function is pinned by tests in ``tests/test_oracle*.py`` against closed
 forms, a library routine (torch's scaled_dot_product_attention in float64),
 hand-traced fixtures under ``tests/golden/`` and invariants the pages fix.
 """
-from . import attention, block_manager, cache, scenario  # noqa: F401
+from . import accounting, attention, block_manager, cache, scenario  # noqa: F401
 from .attention import decode_attention, split_k, lse_merge, decode_attention_split  # noqa: F401
 from .block_manager import BlockManagerModel, OutOfBlocks, InvalidOp  # noqa: F401
 from .cache import PagedCacheModel  # noqa: F401

@@ -68,6 +68,8 @@ _sig("pa_bm_fork", _i32, _vp, _i64, _i64)
 _sig("pa_bm_free_seq", _i32, _vp, _i64)
 _sig("pa_bm_export", _i32, _vp, _pi64, _i32, _i32, _pi32, _pi32)
 _sig("pa_bm_num_free", _i32, _vp)
+_sig("pa_bm_admit", _i32, _vp, _i64, _i32, _i32, _pi32)
+_sig("pa_bm_occupancy", _i32, _vp, _pi64)
 _sig("pa_bm_refcount", _i32, _vp, _i32)
 _sig("pa_bm_seq_len", _i32, _vp, _i64)
 _sig("pa_bm_num_seqs", _i32, _vp)
@@ -312,6 +314,18 @@ class BlockManager:
         out = np.empty(max(num_tokens, 0), dtype=np.int32)
         _check(lib.pa_bm_add_seq(self._h, int(seq), int(num_tokens), out.ctypes.data_as(_pi32)))
         return out
+
+    def admit(self, seq: int, num_tokens: int, reserve_blocks: int = 0) -> np.ndarray:
+        """add_seq only if reserve_blocks stay free afterwards (else OutOfBlocks)."""
+        out = np.empty(max(num_tokens, 0), dtype=np.int32)
+        _check(lib.pa_bm_admit(self._h, int(seq), int(num_tokens), int(reserve_blocks), out.ctypes.data_as(_pi32)))
+        return out
+
+    def occupancy(self) -> Tuple[int, int, int, int]:
+        """(slots of held blocks, tokens, unused slots in last blocks, free slots)."""
+        out = np.zeros(4, dtype=np.int64)
+        _check(lib.pa_bm_occupancy(self._h, out.ctypes.data_as(_pi64)))
+        return tuple(int(x) for x in out)
 
     def append_slots(self, seqs: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
         s = np.ascontiguousarray(seqs, dtype=np.int64)

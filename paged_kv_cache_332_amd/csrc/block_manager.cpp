@@ -86,6 +86,31 @@ pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t num_tokens, int32_t* slo
   return PA_OK;
 }
 
+pa_status pa_bm_admit(pa_bm* bm, int64_t seq, int32_t num_tokens, int32_t reserve_blocks, int32_t* slots_out) {
+  if (!bm || num_tokens < 0 || reserve_blocks < 0) return pa::fail(PA_ERR_INVALID, "pa_bm_admit: bad arguments");
+  const int64_t need = (static_cast<int64_t>(num_tokens) + bm->block_size - 1) / bm->block_size;
+  const int64_t free_blocks = static_cast<int64_t>(bm->free_stack.size());
+  if (need + reserve_blocks > free_blocks)
+    return pa::fail(PA_ERR_OOM, "pa_bm_admit: need %lld blocks and a reserve of %d, %lld free", (long long)need,
+                    reserve_blocks, (long long)free_blocks);
+  return pa_bm_add_seq(bm, seq, num_tokens, slots_out);
+}
+
+pa_status pa_bm_occupancy(const pa_bm* bm, int64_t* out) {
+  if (!bm || !out) return pa::fail(PA_ERR_INVALID, "pa_bm_occupancy: bad arguments");
+  int64_t held = 0, tokens = 0, slack = 0;
+  for (int32_t c : bm->refcount) held += c > 0;
+  for (const auto& kv : bm->seqs) {
+    tokens += kv.second.len;
+    slack += static_cast<int64_t>(kv.second.table.size()) * bm->block_size - kv.second.len;
+  }
+  out[0] = held * bm->block_size;
+  out[1] = tokens;
+  out[2] = slack;
+  out[3] = static_cast<int64_t>(bm->free_stack.size()) * bm->block_size;
+  return PA_OK;
+}
+
 pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* slots_out,
                              int32_t* cow_pairs_out, int32_t* num_cow_out) {
   if (!bm || n < 0 || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)) || !num_cow_out)
