@@ -259,6 +259,33 @@ int32_t pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap);
 pa_status pa_bm_stats(const pa_bm* bm, int64_t* out);
 
 /* ------------------------------------------------------------------------
+ * pa_prefill — causal attention of new tokens over their sequences' paged
+ * context, the step before decode ([MM] §How the Kernel Executes Paged
+ * Attention; [VM] §The fix borrowed from operating systems).
+ * Sequence i's chunk is the query rows query_start[i] .. query_start[i+1] - 1
+ * of q ([T][num_q_heads][head_dim], kv dtype, T = query_start[num_seqs]);
+ * its context_lens[i] tokens (the chunk's own last, their K/V written through
+ * the slots before this call) are read through block_tables like pa_decode.
+ * Row t of a chunk of L tokens sits at position context_lens[i] - L + t and
+ * attends to positions 0 .. itself (textbook causal attention; the pages give
+ * no formula):
+ *   out[row][h] = softmax_j(scale * q[row][h] . K[j][h / g]) V[j][h / g],
+ *   j = 0 .. position.
+ * out: [T][num_q_heads][head_dim] in F32 or the kv dtype.  query_start and
+ * context_lens are device arrays; max_query_len (>= every chunk length) and
+ * max_context_len (>= every context length, <= table_stride * block_size)
+ * are host bounds that size the grid; device lengths are clamped to them.
+ * 16-bit caches only (PA_ERR_UNSUPPORTED for F32); group in {1,2,4,8,16};
+ * at most 65535 (sequence, kv head) pairs.  No workspace.  Asynchronous on
+ * `stream`.
+ * ---------------------------------------------------------------------- */
+pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
+                     pa_dtype kv_dtype, const int32_t* block_tables, int32_t table_stride,
+                     const int32_t* query_start, const int32_t* context_lens, int32_t max_query_len,
+                     int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, void* stream);
+
+/* ------------------------------------------------------------------------
  * pa_step — one decode step of a batch, host and device parts in one call:
  *   1. pa_bm_append_slots: the new token of each of seqs[0..n) gets a slot
  *      (a fresh block when the last one is full; a copy of a shared last

@@ -17,7 +17,9 @@ What it computes, and from which passage:
   print no formula, so the plainest reading (scaled dot product, scale
   1/sqrt(head_dim), max-subtracted softmax) is used.  ``split_k`` /
   ``lse_merge`` are the same result computed over fixed token partitions and
-  recombined by log-sum-exp.
+  recombined by log-sum-exp.  ``prefill_attention`` is the step before decode:
+  each new token of a chunk attends to its context up to its own position
+  (causal, the plain reading: the pages give no formula).
 * ``block_manager`` — a model of the block allocator the pages describe: a
   shared pool of interchangeable fixed-size blocks handed out one at a time on
   demand and returned when a request finishes, tables of block references,
@@ -42,7 +44,7 @@ forms, a library routine (torch's scaled_dot_product_attention in float64),
 hand-traced fixtures under ``tests/golden/`` and invariants the pages fix.
 """
 from . import accounting, attention, block_manager, cache, scenario  # noqa: F401
-from .attention import decode_attention, split_k, lse_merge, decode_attention_split  # noqa: F401
+from .attention import decode_attention, prefill_attention, split_k, lse_merge, decode_attention_split  # noqa: F401
 from .block_manager import BlockManagerModel, OutOfBlocks, InvalidOp  # noqa: F401
 from .cache import PagedCacheModel  # noqa: F401
 from .scenario import run_scenario, ScenarioResult  # noqa: F401

@@ -57,6 +57,24 @@ def decode_attention(q, K, V, scale: float) -> np.ndarray:
     return out
 
 
+def prefill_attention(Q, K, V, scale: float) -> np.ndarray:
+    """A chunk of new tokens at the end of an n-token context: Q [L, Hq, D],
+    K/V [n, Hkv, D] (the chunk's own keys and values last) -> [L, Hq, D]
+    float64.  Row t sits at position n - L + t and sees positions 0 .. itself:
+    the causal attention of a decoder, which the pages do not spell out (the
+    step before decode, "Paged Attention as a Memory Manager", §How the Kernel
+    Executes Paged Attention), so each row is exactly the decode result over
+    the context up to and including its own position."""
+    Q = np.asarray(Q, dtype=np.float64)
+    L, n = Q.shape[0], K.shape[0]
+    if L > n:
+        raise ValueError("the chunk is longer than its context")
+    out = np.zeros(Q.shape, dtype=np.float64)
+    for t in range(L):
+        out[t] = decode_attention(Q[t], K[: n - L + t + 1], V[: n - L + t + 1], scale)
+    return out
+
+
 def split_k(q, K, V, scale: float, part: int):
     """Partials of one sequence over partitions of ``part`` tokens.
 

@@ -23,7 +23,7 @@ __all__ = [
     "PA_PHASE_PASS", "PA_PHASE_MERGE", "PA_PHASE_ALL",
     "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
     "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version", "pa_step",
-    "pa_decode_stream_grid", "step_record_words", "pa_stream_plan", "pa_step_layer",
+    "pa_decode_stream_grid", "step_record_words", "pa_stream_plan", "pa_prefill", "pa_step_layer",
     "STEP_KV", "STEP_PASS", "STEP_MERGE", "STEP_ALL",
 ]
 
@@ -60,6 +60,8 @@ _DECODE_ARGS = [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32
 _sig("pa_decode", _i32, *_DECODE_ARGS)
 _sig("pa_decode_variant", _i32, *_DECODE_ARGS, _i32)
 _sig("pa_decode_phase", _i32, *_DECODE_ARGS, _i32, _i32)
+_sig("pa_prefill", _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+     _i32, _i32, _f32, _vp)
 _sig("pa_bm_create", _vp, _i32, _i32, _pi32)
 _sig("pa_bm_destroy", None, _vp)
 _sig("pa_bm_add_seq", _i32, _vp, _i64, _i32, _pi32)
@@ -198,6 +200,19 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
               partition_size: int = 0, workspace=None, stream=None) -> None:
     pa_decode_variant(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                       partition_size, workspace, stream, PA_KERNEL_AUTO)
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, query_start, context_lens, max_query_len: int,
+               max_context_len: int, scale: float, stream=None) -> None:
+    """Causal attention of the chunks q[query_start[i]:query_start[i+1]] over
+    their sequences' paged context (see pa_prefill in pa.h).  Tensors on the
+    device; query_start / context_lens int32."""
+    n_, hkv, d, bs = _pool_dims(k_cache, v_cache)
+    _check(lib.pa_prefill(out.data_ptr(), torch_dtype_code(out.dtype), q.data_ptr(), k_cache.data_ptr(),
+                          v_cache.data_ptr(), torch_dtype_code(k_cache.dtype), block_tables.data_ptr(),
+                          int(block_tables.shape[1]), query_start.data_ptr(), context_lens.data_ptr(),
+                          int(max_query_len), int(max_context_len), int(context_lens.shape[0]), int(q.shape[1]), hkv,
+                          d, bs, n_, float(scale), _stream(stream)))
 
 
 def pa_step(bm: "BlockManager", seqs_i64: np.ndarray, stage_host, stage_dev, table_stride: int, k_cache, v_cache,

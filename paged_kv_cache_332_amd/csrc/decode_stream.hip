@@ -57,56 +57,6 @@ namespace pa {
 
 namespace {
 
-template <class T>
-struct StreamMfma;
-
-template <>
-struct StreamMfma<BF16> {
-  using v8 = bf16x8;
-  using v4 = bf16x4;
-  using e = __bf16;
-  __device__ static f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b),
-                                                   c, 0, 0, 0);
-  }
-  __device__ static f32x4 pv(u32x2 a, v4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4, a), b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct StreamMfma<F16> {
-  using v8 = f16x8;
-  using v4 = f16x4;
-  using e = _Float16;
-  __device__ static f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c,
-                                                  0, 0, 0);
-  }
-  __device__ static f32x4 pv(u32x2 a, v4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4, a), b, c, 0, 0, 0);
-  }
-};
-
-typedef const void __attribute__((address_space(1)))* gptr_t;
-typedef void __attribute__((address_space(3)))* lptr_t;
-
-// 16 bytes per lane from src into LDS at dst + 16 * lane.
-__device__ __forceinline__ void dma16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-// The memory clobber keeps LDS reads of the landed tile below the wait.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
 // Position in the tile list: item (seq, kvh), tile t of nt, global index g.
 struct Cursor {
   int64_t g;
@@ -115,8 +65,6 @@ struct Cursor {
 
 }  // namespace
 
-// Weights are clamped to [1, 2^16]; a zero, negative or garbage weight can
-// only make the split uneven, never wrong.
 // First tile of wave w (0..4 grid) when the T tiles are split evenly over
 // the grid's workgroups and each workgroup's share evenly over its four
 // waves (the split when no plan is given).
@@ -136,7 +84,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
   __shared__ int32_t s_ctx[kStreamMaxSeqs];
   __shared__ int32_t s_pre[kStreamMaxSeqs + 1];
   using bits = typename T::bits;
-  using MF = StreamMfma<T>;
+  using MF = MfmaOps<T>;
   using v4 = typename MF::v4;
   using el = typename MF::e;
   constexpr int NS = D / 32;                         // QK slices of 32 dims

@@ -369,6 +369,56 @@ pa_status pa_decode_phase(void* out, pa_dtype out_dtype, const void* q, const vo
                          scale, partition_size, workspace, workspace_bytes, stream, kernel, phase, nullptr);
 }
 
+pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
+                     pa_dtype kv_dtype, const int32_t* block_tables, int32_t table_stride,
+                     const int32_t* query_start, const int32_t* context_lens, int32_t max_query_len,
+                     int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, void* stream) {
+  const char* fn = "pa_prefill";
+  if (pa_status st = pa::check_cache_shape(fn, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype)) return st;
+  if (kv_dtype == PA_F32) return pa::fail(PA_ERR_UNSUPPORTED, "%s: the prefill kernel needs a 16-bit cache", fn);
+  if (out_dtype != PA_F32 && out_dtype != kv_dtype)
+    return pa::fail(PA_ERR_INVALID, "%s: out_dtype must be F32 or the kv dtype", fn);
+  if (num_seqs < 0 || num_q_heads <= 0 || max_query_len < 0 || max_context_len < 0 || table_stride < 0)
+    return pa::fail(PA_ERR_INVALID, "%s: bad sizes", fn);
+  if (num_q_heads % num_kv_heads)
+    return pa::fail(PA_ERR_INVALID, "%s: %d query heads not a multiple of %d kv heads", fn, num_q_heads,
+                    num_kv_heads);
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: group size %d not in {1,2,4,8,16}", fn, group);
+  if (max_query_len > max_context_len)
+    return pa::fail(PA_ERR_INVALID, "%s: max_query_len %d exceeds max_context_len %d", fn, max_query_len,
+                    max_context_len);
+  if (pa::ceil_div(max_context_len, block_size) > table_stride)
+    return pa::fail(PA_ERR_INVALID, "%s: table_stride %d < blocks of max_context_len %d", fn, table_stride,
+                    max_context_len);
+  if (int64_t(num_seqs) * num_kv_heads > 65535)
+    return pa::fail(PA_ERR_UNSUPPORTED, "%s: more than 65535 (sequence, kv head) pairs", fn);
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)
+    return pa::fail(PA_ERR_INVALID, "%s: null pointer", fn);
+  if (!pa::aligned16(q) || !pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(out))
+    return pa::fail(PA_ERR_INVALID, "%s: q, out and caches must be 16-byte aligned", fn);
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.tables = block_tables;
+  a.query_start = query_start;
+  a.ctx = context_lens;
+  a.table_stride = table_stride;
+  a.max_ctx = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_f32 = out_dtype == PA_F32;
+  return pa::hip_status(fn, pa::launch_prefill(a, kv_dtype, head_dim, block_size, group, max_query_len,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
                     pa_dtype kv_dtype, const int32_t* block_tables, int32_t table_stride,
                     const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,

@@ -151,4 +151,58 @@ __device__ __forceinline__ int64_t xcd_rank(int64_t total) {
 }
 inline int64_t xcd_grid(int64_t total) { return ((total + kNumXcd - 1) / kNumXcd) * kNumXcd; }
 
+// ---------------------------------------------------------------- matrix cores
+// v_mfma_f32_16x16x32 for S^T = K Q^T (A: 8 key dims of a token per lane,
+// B: 8 query dims of a column per lane) and v_mfma_f32_16x16x16 for
+// O^T += V^T P^T (A: 4 tokens of a V row, B: 4 probabilities of a column).
+template <class T>
+struct MfmaOps;
+
+template <>
+struct MfmaOps<BF16> {
+  using v8 = bf16x8;
+  using v4 = bf16x4;
+  using e = __bf16;
+  __device__ static f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b),
+                                                   c, 0, 0, 0);
+  }
+  __device__ static f32x4 pv(u32x2 a, v4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4, a), b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct MfmaOps<F16> {
+  using v8 = f16x8;
+  using v4 = f16x4;
+  using e = _Float16;
+  __device__ static f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b), c,
+                                                  0, 0, 0);
+  }
+  __device__ static f32x4 pv(u32x2 a, v4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4, a), b, c, 0, 0, 0);
+  }
+};
+
+typedef const void __attribute__((address_space(1)))* gptr_t;
+typedef void __attribute__((address_space(3)))* lptr_t;
+
+// 16 bytes per lane from src into LDS at dst + 16 * lane.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+// The memory clobber keeps LDS reads of the landed tile below the wait.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 }  // namespace pa

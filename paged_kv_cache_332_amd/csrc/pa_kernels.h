@@ -61,6 +61,28 @@ size_t stream_lds_bytes(int d, int gmax, int nslot);
 hipError_t launch_decode_stream(const StreamArgs& sa, int32_t dtype, int32_t d, int32_t bs, int32_t gmax,
                                 int32_t nslot, size_t lds, int32_t grid, int32_t phases, hipStream_t stream);
 
+// Arguments of the paged prefill kernel.
+struct PrefillArgs {
+  void* out;                     // [T][Hq][D], fp32 or the kv dtype (T = query rows of all chunks)
+  const void* q;                 // [T][Hq][D], kv dtype
+  const void* k;                 // K pool
+  const void* v;                 // V pool
+  const int32_t* tables;         // [B][table_stride]
+  const int32_t* query_start;    // [B + 1] first query row of each sequence's chunk
+  const int32_t* ctx;            // [B] context length including the chunk
+  int32_t table_stride;
+  int32_t max_ctx;               // host bound; device lengths are clamped to it
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  float scale_log2;              // scale * log2(e)
+  int32_t out_f32;
+};
+// Query tokens one prefill workgroup takes (four waves of 16 / group columns).
+inline int32_t prefill_tokens_per_wg(int32_t group) { return 4 * (16 / group); }
+hipError_t launch_prefill(const PrefillArgs& a, int32_t dtype, int32_t d, int32_t bs, int32_t group,
+                          int32_t max_query_len, hipStream_t stream);
+
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                            const int32_t* slots, int32_t num_tokens, int32_t hkv, int32_t d,
                            int32_t bs, int32_t elem_bytes, hipStream_t stream);

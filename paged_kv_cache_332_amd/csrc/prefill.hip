@@ -1,0 +1,331 @@
+// Paged prefill attention for 16-bit caches (gfx950): the step before decode.
+//
+// A chunk of a sequence's new tokens attends causally over the sequence's
+// whole context -- its earlier tokens and the chunk itself, whose keys and
+// values were written through the slots first -- read through the block
+// table like decode ("Paged Attention as a Memory Manager", §How the Kernel
+// Executes Paged Attention: at prefill each new sequence gets its logical
+// blocks in order; "Paged Attention: Virtual Memory for the KV Cache", §The
+// fix borrowed from operating systems).  Query token t of a chunk of L tokens
+// in a context of P sits at position P - L + t and sees positions 0 .. its
+// own: textbook causal attention (the pages give no formula), i.e. for each
+// token exactly the decode result at that length.
+//
+// Work decomposition.  One workgroup per (sequence, kv head, block of
+// 64 / group query tokens); its four waves each own 16 matrix-core columns,
+// the (query token, query head) pairs of 16 / group tokens of the kv head's
+// group.  The workgroup streams the 16-token K/V tiles of the positions its
+// tokens can see through a 4-slot LDS ring filled by direct global->LDS
+// loads, each wave loading a quarter of every tile, so every K/V byte read
+// serves 64 columns.  Per tile and wave: S^T = K Q^T with
+// v_mfma_f32_16x16x32, a causal limit per column, the running-max softmax of
+// the decode kernel (reference maximum refreshed when it grows by more than
+// 2^8), P split into a 16-bit high part and the rounded remainder for two
+// v_mfma_f32_16x16x16 products into O^T.  No split of the context: a
+// workgroup covers its tokens' whole prefix, and many workgroups run at once.
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+
+namespace {
+
+// Workgroup barrier without the memory fence of __syncthreads, which would
+// wait for every outstanding load of the wave (the ring's prefetches
+// included); each wave waits for its own loads with an explicit count first.
+// The clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// LDS reads of the ring and the block ids.  As volatile LDS accesses the
+// compiler keeps them where they are (after the explicit waits and the
+// barrier) and does not add a wait for every direct load still in flight.
+template <class V>
+__device__ __forceinline__ V ring_read(const uint8_t* p) {
+  return *(const volatile __attribute__((address_space(3))) V*)(p);
+}
+
+template <class T, int D, int BS, int G>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  using bits = typename T::bits;
+  using MF = MfmaOps<T>;
+  using v4 = typename MF::v4;
+  using el = typename MF::e;
+  constexpr int TQ = 16 / G;           // query tokens per wave
+  constexpr int TQW = 4 * TQ;          // per workgroup
+  constexpr int NS = D / 32;           // QK slices of 32 dims
+  constexpr int NT = D / 16;           // PV row tiles of 16 dims
+  constexpr int KI = D / 32;           // 1 KiB loads per K (and per V) tile
+  constexpr int LPW = 2 * KI / 4;      // loads per wave per tile
+  constexpr int NSL = 4;               // ring slots
+  constexpr int IDCAP = 512;           // tiles whose block ids are staged at once
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(LPW >= 1 && LPW * (NSL - 1) < 64, "loads per wave");
+  // the ring is the dynamic LDS array, a separate object from the block ids,
+  // so the compiler can tell that its direct loads never write s_ids; reads
+  // of a landed slot are ordered by the explicit waits below
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
+  constexpr int SLOT = 2 * KI * 1024;
+  __shared__ int2 s_ids[IDCAP];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q = lane >> 4;
+  const int c = lane & 15;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = a.num_q_heads;
+  const int s = blockIdx.y / Hkv;
+  const int h = blockIdx.y % Hkv;
+  const int qs = a.query_start[s];
+  const int P = min(max(a.ctx[s], 0), a.max_ctx);
+  const int L = min(max(a.query_start[s + 1] - qs, 0), P);
+  const int tq0 = blockIdx.x * TQW;
+  if (tq0 >= L) return;                          // (whole workgroup)
+  const int p0 = P - L;                          // position of the chunk's first token
+  const int kmax = p0 + min(L, tq0 + TQW);       // positions the workgroup's tokens see
+  const int nt = (kmax + 15) / 16;
+
+  // this lane's column: token j of the wave, head gc of the group
+  const int tw0 = tq0 + wave * TQ;
+  const int j = c / G, gc = c % G;
+  const bool col_valid = tw0 + j < L;
+  const int tok = min(tw0 + j, L - 1);           // (a spare column repeats the last token)
+  const int lim = p0 + tok + 1;                  // causal limit of the column (exclusive)
+  const int64_t qrow = (int64_t(qs) + tok) * Hq + int64_t(h) * G + gc;
+  const bits* qp = static_cast<const bits*>(a.q) + qrow * D;
+  u32x4 qop[NS];
+#pragma unroll
+  for (int m = 0; m < NS; ++m) qop[m] = *reinterpret_cast<const u32x4*>(qp + (4 * m + q) * 8);
+  // the query loads complete here, in a wait the compiler knows about
+  // (vmcnt 0; expcnt and lgkmcnt at their maxima): otherwise it waits for
+  // every load in flight before each tile's first product
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  const int32_t* row = a.tables + int64_t(s) * a.table_stride;
+  const bits* kpool = static_cast<const bits*>(a.k);
+  const bits* vpool = static_cast<const bits*>(a.v);
+  // block ids of tiles [from, from + IDCAP) (the whole workgroup)
+  int id_base = 0;
+  auto stage_ids = [&](int from) {
+    const int n = min(IDCAP, nt - from);
+    for (int i = threadIdx.x; i < n; i += 256) {
+      const int t = from + i;
+      int2 ids;
+      if constexpr (BS == 16) {
+        ids.x = ids.y = row[t];
+      } else if constexpr (BS == 32) {
+        ids.x = ids.y = row[t >> 1];
+      } else {
+        ids.x = row[2 * t];
+        ids.y = 16 * t + 8 < kmax ? row[2 * t + 1] : ids.x;
+      }
+      s_ids[i] = ids;
+    }
+    id_base = from;
+  };
+  // this wave's quarter of the loads of tile t into its slot
+  auto issue = [&](int t) {
+    uint8_t* sl = ring + (t % NSL) * SLOT;
+    const int b0 = uniform(ring_read<int32_t>(reinterpret_cast<const uint8_t*>(&s_ids[t - id_base].x)));
+    const int b1 = uniform(ring_read<int32_t>(reinterpret_cast<const uint8_t*>(&s_ids[t - id_base].y)));
+#pragma unroll
+    for (int ii = 0; ii < LPW; ++ii) {
+      const int i = wave * LPW + ii;             // load i of the tile's 2 KI
+      if (i < KI) {
+        const int u = i * 64 + lane;
+        const int jj = u >> 4, tt = u & 15;
+        int blk, tk;
+        if constexpr (BS == 16) {
+          blk = b0;
+          tk = tt;
+        } else if constexpr (BS == 32) {
+          blk = b0;
+          tk = 16 * (t & 1) + tt;
+        } else {
+          blk = tt < 8 ? b0 : b1;
+          tk = tt & 7;
+        }
+        const int64_t e = ((int64_t(blk) * Hkv + h) * (D / 8) + jj) * (BS * 8) + tk * 8;
+        dma16(kpool + e, sl + i * 1024);
+      } else {
+        const int u = (i - KI) * 64 + lane;
+        const int d = u >> 1, hh = u & 1;
+        int blk, tk0;
+        if constexpr (BS == 16) {
+          blk = b0;
+          tk0 = 8 * hh;
+        } else if constexpr (BS == 32) {
+          blk = b0;
+          tk0 = 16 * (t & 1) + 8 * hh;
+        } else {
+          blk = hh ? b1 : b0;
+          tk0 = 0;
+        }
+        const int64_t e = ((int64_t(blk) * Hkv + h) * D + d) * BS + tk0;
+        dma16(vpool + e, sl + i * 1024);
+      }
+    }
+  };
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf, l_lane = 0.f;
+
+  stage_ids(0);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NSL - 1; ++i)
+    if (i < nt) issue(i);
+  for (int t = 0; t < nt; ++t) {
+    // this wave's loads of tile t have landed once at most its loads of the
+    // newer tiles are outstanding; the barrier then covers every wave's share
+    // (and every wave is done with tile t - 1, whose slot is refilled next)
+    switch (min(nt - 1, t + NSL - 2) - t) {
+      case 0: vm_wait<0>(); break;
+      case 1: vm_wait<LPW>(); break;
+      default: vm_wait<2 * LPW>(); break;
+    }
+    wg_barrier();
+    const int tn = t + NSL - 1;
+    if (tn < nt) {
+      if (tn >= id_base + IDCAP) {
+        // next window of block ids (every slot's loads have landed: the
+        // compiler waits for the table reads before the LDS writes)
+        stage_ids(tn);
+        lgkm_wait0();
+        wg_barrier();
+      }
+      issue(tn);
+    }
+    // ---- tile t: S^T = K Q^T, causal mask per column, online softmax, PV
+    const uint8_t* sl = ring + (t % NSL) * SLOT;
+    u32x4 kr[NS];
+    u32x2 vr[NT];
+#pragma unroll
+    for (int m = 0; m < NS; ++m) kr[m] = ring_read<u32x4>(sl + ((4 * m + q) * 16 + c) * 16);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) vr[n] = ring_read<u32x2>(sl + KI * 1024 + (16 * n + c) * 32 + 8 * q);
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NS; ++m) sc = MF::qk(kr[m], qop[m], sc);
+    const int kp0 = 16 * t + 4 * q;
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = kp0 + i < lim ? sc[i] * a.scale_log2 : kNegInf;
+    float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mt = xor16<OpMax>(mt);
+    mt = xor32<OpMax>(mt);
+    // (tile 0 holds position 0, which every column sees: m_ref is finite
+    // from then on and masked terms give exp2(-inf) = 0)
+    const bool need = mt > m_ref + 8.f;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? (m_ref == kNegInf ? 0.f : fast_exp2(m_ref - mt)) : 1.f;
+      m_ref = need ? mt : m_ref;
+      l_lane *= alpha;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_ref);
+    l_lane += (p[0] + p[1]) + (p[2] + p[3]);
+    v4 phi, plo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const el hi = static_cast<el>(p[i]);
+      phi[i] = hi;
+      plo[i] = static_cast<el>(p[i] - static_cast<float>(hi));
+    }
+    if (16 * t + 16 > kmax) {
+      // positions past the workgroup's last token may hold anything (NaN
+      // poison included): select zeros
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        uint32_t w0 = vr[n][0], w1 = vr[n][1];
+        if (kp0 + 0 >= kmax) w0 &= 0xFFFF0000u;
+        if (kp0 + 1 >= kmax) w0 &= 0x0000FFFFu;
+        if (kp0 + 2 >= kmax) w1 &= 0xFFFF0000u;
+        if (kp0 + 3 >= kmax) w1 &= 0x0000FFFFu;
+        vr[n] = u32x2{w0, w1};
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      acc[n] = MF::pv(vr[n], phi, acc[n]);
+      acc[n] = MF::pv(vr[n], plo, acc[n]);
+    }
+  }
+
+  float l = xor16<OpSum>(l_lane);
+  l = xor32<OpSum>(l);
+  if (col_valid) {
+    const float inv = 1.f / l;
+    const int64_t o = qrow * D + 4 * q;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const f32x4 v = acc[n] * inv;
+      if (a.out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o + 16 * n) = v;
+      } else {
+        const uint32_t lo = T::from_f32(v[0]) | (T::from_f32(v[1]) << 16);
+        const uint32_t hi = T::from_f32(v[2]) | (T::from_f32(v[3]) << 16);
+        *reinterpret_cast<u32x2*>(static_cast<bits*>(a.out) + o + 16 * n) = u32x2{lo, hi};
+      }
+    }
+  }
+}
+
+template <class T, int D, int BS, int G>
+hipError_t launch_g(const PrefillArgs& a, int32_t max_query_len, hipStream_t stream) {
+  const int tpw = 4 * (16 / G);
+  const size_t lds = 4 * 2 * (D / 32) * 1024;   // the tile ring: 4 slots of K and V
+  dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads), block(256);
+  hipLaunchKernelGGL((prefill_kernel<T, D, BS, G>), grid, block, lds, stream, a);
+  return hipGetLastError();
+}
+
+template <class T, int D, int BS>
+hipError_t launch_b(const PrefillArgs& a, int32_t group, int32_t max_query_len, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_g<T, D, BS, 1>(a, max_query_len, stream);
+    case 2: return launch_g<T, D, BS, 2>(a, max_query_len, stream);
+    case 4: return launch_g<T, D, BS, 4>(a, max_query_len, stream);
+    case 8: return launch_g<T, D, BS, 8>(a, max_query_len, stream);
+    case 16: return launch_g<T, D, BS, 16>(a, max_query_len, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class T, int D>
+hipError_t launch_d(const PrefillArgs& a, int32_t bs, int32_t group, int32_t max_query_len, hipStream_t stream) {
+  switch (bs) {
+    case 8: return launch_b<T, D, 8>(a, group, max_query_len, stream);
+    case 16: return launch_b<T, D, 16>(a, group, max_query_len, stream);
+    case 32: return launch_b<T, D, 32>(a, group, max_query_len, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class T>
+hipError_t launch_t(const PrefillArgs& a, int32_t d, int32_t bs, int32_t group, int32_t max_query_len,
+                    hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_d<T, 64>(a, bs, group, max_query_len, stream);
+    case 128: return launch_d<T, 128>(a, bs, group, max_query_len, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int32_t dtype, int32_t d, int32_t bs, int32_t group,
+                          int32_t max_query_len, hipStream_t stream) {
+  if (max_query_len <= 0 || a.num_seqs <= 0) return hipSuccess;
+  switch (dtype) {
+    case 1: return launch_t<F16>(a, d, bs, group, max_query_len, stream);
+    case 2: return launch_t<BF16>(a, d, bs, group, max_query_len, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

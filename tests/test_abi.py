@@ -342,3 +342,23 @@ def test_stream_plan_rejects_bad_input():
         pa.pa_stream_plan(np.array([0, 5, 3], dtype=np.int32), 2, 4)      # decreasing prefix
     with pytest.raises(pa.PAError):
         pa.pa_stream_plan(np.array([0, 5], dtype=np.int32), 2, 2000)      # grid beyond the limit
+
+
+def _prefill_args(**over):
+    a = dict(out=16, out_dtype=pa.PA_F32, q=16, k=16, v=16, kv_dtype=pa.PA_BF16, tables=16, stride=256,
+             qs=16, ctx=16, max_q=512, max_ctx=4096, B=64, Hq=32, Hkv=8, D=128, BS=16, N=1000, scale=0.1,
+             stream=0)
+    a.update(over)
+    return [a[k] for k in ["out", "out_dtype", "q", "k", "v", "kv_dtype", "tables", "stride", "qs", "ctx",
+                           "max_q", "max_ctx", "B", "Hq", "Hkv", "D", "BS", "N", "scale", "stream"]]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kv_dtype=pa.PA_F32), 4), (dict(D=96), 4), (dict(Hq=24, Hkv=8), 4), (dict(Hq=12, Hkv=8), 1),
+    (dict(out_dtype=pa.PA_F16), 1), (dict(max_q=5000), 1), (dict(stride=10), 1), (dict(q=8), 1),
+    (dict(qs=0), 1), (dict(B=10000), 4),
+])
+def test_prefill_rejects_bad_arguments(over, status):
+    """Host validation of pa_prefill, before any launch."""
+    assert pa.lib.pa_prefill(*_prefill_args(**over)) == status
+    assert pa.lib.pa_last_error()

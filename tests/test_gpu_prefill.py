@@ -1,0 +1,110 @@
+"""Paged prefill (pa_prefill) against the CPU oracle on an MI355X: chunks of
+new tokens attend causally over their sequences' paged context.  Outputs
+(fp32) must be within 2e-3 of the float64 oracle for 16-bit caches."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+# dtype, head_dim, block size, q heads, kv heads, context lengths, chunk lengths
+CASES = {
+    "gqa4_bf16_bs16": ("bf16", 128, 16, 32, 8, [300, 17, 1, 2049, 64], [300, 5, 1, 100, 64]),
+    "mha_f16_bs8": ("f16", 64, 8, 8, 8, [40, 129, 7], [40, 33, 7]),
+    "gqa8_bf16_bs32": ("bf16", 128, 32, 64, 8, [1000, 260], [250, 1]),
+    "gqa16_bf16_d64": ("bf16", 64, 16, 16, 1, [77, 33], [77, 20]),
+    "gqa2_f16_bs16": ("f16", 128, 16, 8, 4, [513, 1], [512, 1]),
+    "long_context_bf16": ("bf16", 128, 16, 32, 8, [9000, 300], [64, 300]),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_prefill_matches_oracle(case):
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    dtype, d, bs, hq, hkv, ctx, chunk = CASES[case]
+    say("prefill", case)
+    w = W.tiny(num_seqs=len(ctx), dtype=dtype, seed=41, ctx=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+               block_size=bs)
+    dev = runner.run_script(w, decode=False)
+    eng = dev.engine
+    seqs = list(range(len(ctx)))
+    tab, ctx_now = eng.bm.export(seqs, eng.stride)
+    assert list(ctx_now) == list(ctx)
+    rng = np.random.default_rng([41, len(ctx)])
+    T = int(sum(chunk))
+    q = W.round_to_dtype(rng.standard_normal((T, hq, d), dtype=np.float32), dtype)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    tdt = runner.TORCH_DTYPE[dtype]
+    q_dev = torch.from_numpy(q).to("cuda").to(tdt)
+    out = torch.full((T, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    scale = 1.0 / d ** 0.5
+    pa.pa_prefill(out, q_dev, eng.k_cache, eng.v_cache, torch.from_numpy(np.ascontiguousarray(tab)).to("cuda"),
+                  torch.from_numpy(qs).to("cuda"), torch.from_numpy(np.asarray(ctx, np.int32)).to("cuda"),
+                  max(chunk), max(ctx), scale)
+    # half-precision output: the fp32 result rounded to the cache dtype
+    out_h = torch.empty((T, hq, d), dtype=tdt, device="cuda")
+    pa.pa_prefill(out_h, q_dev, eng.k_cache, eng.v_cache, torch.from_numpy(np.ascontiguousarray(tab)).to("cuda"),
+                  torch.from_numpy(qs).to("cuda"), torch.from_numpy(np.asarray(ctx, np.int32)).to("cuda"),
+                  max(chunk), max(ctx), scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = 0.0
+    for i, (n, L) in enumerate(zip(ctx, chunk)):
+        rows = w.row_of(i, np.arange(n))
+        ref = oracle.prefill_attention(q[qs[i]: qs[i + 1]], w.k_rows[rows], w.v_rows[rows], scale)
+        err = max(err, float(np.max(np.abs(got[qs[i]: qs[i + 1]] - ref))))
+    say(case, "max abs error", err)
+    assert err <= 2e-3
+    assert torch.equal(out_h, out.to(tdt))
+
+
+def test_prefill_of_one_token_is_decode():
+    """A one-token chunk is a decode step: pa_prefill agrees with the oracle's
+    decode over the whole context, and so does pa_decode on the same row."""
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    ctx = [1, 300, 4000]
+    w = W.tiny(num_seqs=3, dtype="bf16", seed=5, ctx=ctx, num_q_heads=32, num_kv_heads=8, head_dim=128,
+               block_size=16)
+    dev = runner.run_script(w)
+    eng = dev.engine
+    dec = dev.decodes[-1]
+    q_dev = dev.q_dev[dec.q_index][torch.tensor(dec.seqs, device="cuda")].contiguous()
+    out = torch.empty((3, 32, 128), dtype=torch.float32, device="cuda")
+    pa.pa_prefill(out, q_dev, eng.k_cache, eng.v_cache, torch.from_numpy(np.ascontiguousarray(dec.tables)).to("cuda"),
+                  torch.arange(4, dtype=torch.int32, device="cuda"),
+                  torch.from_numpy(np.asarray(dec.ctx, np.int32)).to("cuda"), 1, max(ctx), 1.0 / 128 ** 0.5)
+    torch.cuda.synchronize()
+    ref = oracle.run_scenario(w).decodes[-1].out
+    assert float(np.max(np.abs(out.cpu().numpy() - ref))) <= 2e-3
+    assert float(torch.max(torch.abs(out - dec.out))) <= 2e-3
+
+
+def test_prefill_rejects_bad_arguments():
+    import paged_kv_cache_332_amd as pa
+    k = torch.zeros((4, 2, 8, 16, 8), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros((4, 2, 64, 16), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((3, 8, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((3, 8, 64), dtype=torch.float32, device="cuda")
+    tab = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    qs = torch.tensor([0, 3], dtype=torch.int32, device="cuda")
+    cl = torch.tensor([3], dtype=torch.int32, device="cuda")
+    with pytest.raises(pa.PAError):
+        pa.pa_prefill(out, q, k, v, tab, qs, cl, 5, 3, 0.1)       # chunk longer than the context bound
+    with pytest.raises(pa.PAError):
+        pa.pa_prefill(out, q, k, v, tab, qs, cl, 3, 100, 0.1)     # table stride too short for the bound
+    with pytest.raises(pa.PAError):
+        pa.pa_prefill(out, q, k.float(), v.float(), tab, qs, cl, 3, 3, 0.1)  # fp32 cache

@@ -229,3 +229,49 @@ def test_c4_construction(name):
         assert len(src) == 1 and tabs[63, 127] == next(iter(src))       # last sharer in place
         assert all(r.bm.refcount(int(b)) == 64 for b in tabs[0, :127])
     assert r.decodes[-1].ctx.tolist() == w.ctx.tolist()
+
+
+# ----------------------------------------------------------------- prefill
+def _masked_prefill(Q, K, V, scale):
+    """Independent formulation: the whole L x n score matrix per query head,
+    an explicit causal mask, a row softmax and one product with V."""
+    Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
+    L, Hq, D = Q.shape
+    n, Hkv, _ = K.shape
+    g = Hq // Hkv
+    pos = n - L + np.arange(L)
+    out = np.zeros_like(Q)
+    for r in range(Hq):
+        S = Q[:, r, :] @ K[:, r // g, :].T * scale            # [L, n]
+        S[np.arange(n)[None, :] > pos[:, None]] = -np.inf
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        out[:, r, :] = (P / P.sum(axis=1, keepdims=True)) @ V[:, r // g, :]
+    return out
+
+
+@pytest.mark.parametrize("L,n,hq,hkv", [(1, 1, 2, 1), (5, 5, 4, 2), (3, 9, 8, 2), (7, 20, 4, 4)])
+def test_prefill_oracle_matches_masked_matrix(L, n, hq, hkv):
+    """Row by row decode over growing prefixes equals the masked score matrix
+    (a chunk at the end of its context; the whole prompt when L = n)."""
+    rng = np.random.default_rng([L, n, hq])
+    D = 8
+    Q = rng.standard_normal((L, hq, D))
+    K = rng.standard_normal((n, hkv, D))
+    V = rng.standard_normal((n, hkv, D))
+    got = oracle.prefill_attention(Q, K, V, 0.35)
+    assert np.allclose(got, _masked_prefill(Q, K, V, 0.35), rtol=0, atol=1e-12)
+
+
+def test_prefill_first_token_sees_only_itself():
+    """The first token of a fresh prompt attends to position 0 alone: its
+    output is V[0] exactly, whatever the scores; the last row equals decode
+    over the whole context."""
+    rng = np.random.default_rng(3)
+    Q = rng.standard_normal((6, 4, 8)) * 50
+    K = rng.standard_normal((6, 2, 8))
+    V = rng.standard_normal((6, 2, 8))
+    out = oracle.prefill_attention(Q, K, V, 1.0)
+    assert np.array_equal(out[0], np.repeat(V[0], 2, axis=0))
+    assert np.array_equal(out[-1], oracle.decode_attention(Q[-1], K, V, 1.0))
+    with pytest.raises(ValueError):
+        oracle.prefill_attention(Q, K[:3], V[:3], 1.0)
