@@ -50,6 +50,9 @@ def parse():
                          "between kernels costs the stream ~4 us, so sparse timing keeps the step intact)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", type=int, default=8, help="passes timed after evicting the Infinity Cache")
+    ap.add_argument("--prefill", type=int, default=0, metavar="L",
+                    help="measure pa_prefill instead: the last min(L, ctx) tokens of every sequence of the "
+                         "config as one chunk each (prints its own JSON line)")
     ap.add_argument("--burst", type=int, default=16,
                     help="back-to-back pass launches timed for the roofline's launch duration")
     ap.add_argument("--no-balance", action="store_true",
@@ -142,6 +145,62 @@ def cpu_baseline(w, budget_s: float):
 W_ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 
 
+def prefill_bench(args, w, cfg, pa, runner, torch):
+    """pa_prefill on the config's pools: every sequence's last min(L, ctx)
+    tokens as its chunk, causal over its whole context.  FLOPs count 4 Hq D
+    per (query token, visible key): QK^T and PV, multiply and add."""
+    dtype = runner.TORCH_DTYPE[cfg.dtype]
+    dev = runner.run_script(w, decode=False)
+    eng = dev.engine
+    seqs = list(range(cfg.num_seqs))
+    tab, ctx = eng.bm.export(seqs, eng.stride)
+    ctx = np.asarray(ctx, dtype=np.int64)
+    chunk = np.minimum(args.prefill, ctx)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    T = int(qs[-1])
+    g = torch.Generator(device="cuda").manual_seed(7)
+    q = torch.randn((T, cfg.num_q_heads, cfg.head_dim), generator=g, device="cuda").to(dtype)
+    out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    tab_d = torch.from_numpy(np.ascontiguousarray(tab)).to("cuda")
+    qs_d = torch.from_numpy(qs).to("cuda")
+    ctx_d = torch.from_numpy(ctx.astype(np.int32)).to("cuda")
+    scale = 1.0 / cfg.head_dim ** 0.5
+    run = lambda: pa.pa_prefill(out, q, eng.k_cache, eng.v_cache, tab_d, qs_d, ctx_d, int(chunk.max()),
+                                int(ctx.max()), scale)
+    for _ in range(args.warmup):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # visible keys per query token: its position + 1
+    keys = sum(int(((c - L + 1) + c) * L // 2) for c, L in zip(ctx, chunk))
+    flops = 4.0 * cfg.num_q_heads * cfg.head_dim * keys
+    # K/V tiles each workgroup streams (16-token tiles up to its last token)
+    tpw = 4 * (16 // (cfg.num_q_heads // cfg.num_kv_heads))
+    tiles = 0
+    for c, L in zip(ctx, chunk):
+        p0 = c - L
+        for b in range(0, int(L), tpw):
+            tiles += -(-(p0 + min(L, b + tpw)) // 16)
+    kv_bytes = tiles * cfg.num_kv_heads * 2 * 16 * cfg.head_dim * W_ELEM[cfg.dtype]
+    tflops = flops / (us * 1e-6) / 1e12
+    print(json.dumps({
+        "metric": "paged prefill TFLOP/s", "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 4), "higher_is_better": True,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": args.config, "batch": cfg.num_seqs, "chunk": int(args.prefill),
+                   "query_tokens": T, "ctx_mean": round(float(ctx.mean()), 1)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "kv_bytes_streamed": int(kv_bytes),
+                     "kv_GBps": round(kv_bytes / (us * 1e-6) / 1e9, 1)},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -174,6 +233,9 @@ def main():
     seqs = list(range(cfg.num_seqs))
     # spare blocks for the tokens the warm-up and timed steps append
     extra_blocks = cfg.num_seqs * (-(-total_steps // cfg.block_size) + 1)
+    if args.prefill:
+        prefill_bench(args, w, cfg, pa, runner, torch)
+        return
     dev = runner.run_script(w, partition_size=part, kernel=kernel, extra_context=total_steps,
                             extra_blocks=extra_blocks)
     eng: PagedKVEngine = dev.engine
