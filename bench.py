@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--prefill", type=int, default=0, metavar="L",
                     help="measure pa_prefill instead: the last min(L, ctx) tokens of every sequence of the "
                          "config as one chunk each (prints its own JSON line)")
+    ap.add_argument("--swap", type=float, default=0.0, metavar="FRAC",
+                    help="measure preemption by swap instead: every k-th sequence (FRAC of the batch) copied "
+                         "to pinned host memory and back with pa_swap_blocks (prints its own JSON line)")
     ap.add_argument("--burst", type=int, default=16,
                     help="back-to-back pass launches timed for the roofline's launch duration")
     ap.add_argument("--no-balance", action="store_true",
@@ -201,6 +204,65 @@ def prefill_bench(args, w, cfg, pa, runner, torch):
     }), flush=True)
 
 
+def swap_bench(args, w, cfg, pa, runner, torch):
+    """pa_swap_blocks on the config's pools: the blocks of every k-th sequence
+    (k = round(1 / FRAC)) moved to pinned host memory and back, each direction
+    timed on its own with HIP events.  The copy runs over the host link, so a
+    plain DMA copy of the same bytes (torch's pinned copy) is timed beside it
+    as the link's practical rate; peak = 64 GB/s per direction (PCIe 5.0 x16)."""
+    dev = runner.run_script(w, decode=False)
+    eng = dev.engine
+    k = max(1, int(round(1.0 / args.swap)))
+    victims = list(range(0, cfg.num_seqs, k))
+    tab, ctx = eng.bm.export(victims, eng.stride)
+    blocks = np.concatenate([tab[i, : -(-int(c) // cfg.block_size)] for i, c in enumerate(ctx)]).astype(np.int32)
+    n = int(blocks.size)
+    per_block = eng.k_cache[0].numel()
+    tdt = eng.k_cache.dtype
+    host_k = torch.empty((n, per_block), dtype=tdt).pin_memory()
+    host_v = torch.empty((n, per_block), dtype=tdt).pin_memory()
+    ids = torch.from_numpy(blocks).to("cuda")
+    nbytes = 2 * n * per_block * eng.k_cache.element_size()
+    steps = max(1, min(args.steps, 20))
+    ref_k = eng.k_cache[ids.long()].clone()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    us_out = timed(lambda: pa.pa_swap_blocks(eng.k_cache, eng.v_cache, host_k, host_v, ids, to_host=True))
+    us_in = timed(lambda: pa.pa_swap_blocks(eng.k_cache, eng.v_cache, host_k, host_v, ids, to_host=False))
+    bits = torch.int32 if ref_k.element_size() == 4 else torch.int16      # unwritten slots hold NaN
+    assert torch.equal(eng.k_cache[ids.long()].view(bits), ref_k.view(bits)), "swap round trip changed the pool"
+    # the host link's rate for one contiguous copy of the same bytes
+    flat_d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    flat_h = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    us_dma_out = timed(lambda: flat_h.copy_(flat_d, non_blocking=True))
+    us_dma_in = timed(lambda: flat_d.copy_(flat_h, non_blocking=True))
+    gbps = lambda us: round(nbytes / (us * 1e-6) / 1e9, 2)
+    peak = 64.0
+    print(json.dumps({
+        "metric": "swap GB/s", "value": gbps(us_out), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": 2, "ms_per_step": round(us_out / 1e3, 4), "higher_is_better": True, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.config, "sequences_swapped": len(victims), "blocks": n,
+                   "bytes_each_way": int(nbytes)},
+        "swap_out": {"us": round(us_out, 1), "GBps": gbps(us_out)},
+        "swap_in": {"us": round(us_in, 1), "GBps": gbps(us_in)},
+        "dma_copy": {"out_GBps": gbps(us_dma_out), "in_GBps": gbps(us_dma_in)},
+        "roofline": {"bound": "host-link", "achieved": gbps(us_out), "peak": peak, "unit": "GB/s",
+                     "frac": round(gbps(us_out) / peak, 4), "frac_in": round(gbps(us_in) / peak, 4)},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -235,6 +297,9 @@ def main():
     extra_blocks = cfg.num_seqs * (-(-total_steps // cfg.block_size) + 1)
     if args.prefill:
         prefill_bench(args, w, cfg, pa, runner, torch)
+        return
+    if args.swap:
+        swap_bench(args, w, cfg, pa, runner, torch)
         return
     dev = runner.run_script(w, partition_size=part, kernel=kernel, extra_context=total_steps,
                             extra_blocks=extra_blocks)

@@ -235,6 +235,22 @@ pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t 
 /* Free blocks: the headroom a server can admit against ([VM] §What it buys
  * in practice). */
 int32_t pa_bm_num_free(const pa_bm* bm);
+/* Preemption by swap ([VM] §What it does not fix: when memory runs out a
+ * sequence is evicted and its blocks swapped out, to be brought back later).
+ * pa_bm_swap_out releases the sequence's blocks like pa_bm_free_seq and keeps
+ * its length: blocks_out (room for ceil(len / BS)) receives its table in
+ * logical order and *num_blocks_out the count, so the caller can copy them
+ * out (pa_swap_blocks, to_host = 1) on the stream before anything reuses
+ * them.  A shared block stays resident for its other sharers; the swapped
+ * sequence gets a private copy back.
+ * pa_bm_swap_in gives a swapped-out sequence fresh blocks (all-or-nothing,
+ * PA_ERR_OOM leaves everything unchanged) and returns them in logical order
+ * for the copy back (to_host = 0).  pa_bm_swapped_len is the length of a
+ * swapped-out sequence, or -1. */
+pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq, int32_t* blocks_out, int32_t* num_blocks_out);
+pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq, int32_t* blocks_out, int32_t* num_blocks_out);
+int32_t pa_bm_swapped_len(const pa_bm* bm, int64_t seq);
+
 /* Admission that keeps headroom ([VM] §What it buys in practice: memory is
  * handed out in small increments, so a server can admit without committing to
  * a request's worst case and can tell how close it is to the ceiling):
@@ -257,6 +273,20 @@ int32_t pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap);
 /* out[5] = {free blocks, referenced blocks, shared blocks (count > 1),
  *           copy-on-write pairs issued so far, slack tokens in last blocks} */
 pa_status pa_bm_stats(const pa_bm* bm, int64_t* out);
+
+/* Copies whole blocks (every kv head, K and V) between the pools and host
+ * memory for preemption by swap: blocks[i] (pool block id) <-> slot i of
+ * host_k / host_v, each [num_blocks_moved][num_kv_heads * head_dim *
+ * block_size] elements in the pools' in-block layout.  to_host: 1 pool ->
+ * host, 0 host -> pool.  host_k, host_v and blocks must be pinned host memory
+ * (or device memory); 16-byte aligned buffers.  An id outside
+ * [0, num_blocks) moves nothing (its host slot is left as it was).
+ * Asynchronous on `stream`: the copy out must be enqueued before any work
+ * that reuses the blocks, and the host must not read host_k / host_v before
+ * it completes. */
+pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_v, const int32_t* blocks,
+                         int32_t num_blocks_moved, int32_t to_host, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * pa_prefill — causal attention of new tokens over their sequences' paged

@@ -35,6 +35,18 @@ same written policy, so integer results are unique):
 * a call that cannot get the blocks it needs raises ``OutOfBlocks`` and
   changes nothing; unknown or duplicate sequence ids raise ``InvalidOp`` and
   change nothing.
+
+Preemption by swap ("Paged Attention: Virtual Memory for the KV Cache",
+§What it does not fix: once memory runs out a sequence must be evicted, its
+blocks moved off the device and brought back later):
+
+* ``swap_out`` releases the sequence's blocks exactly like ``free_seq`` and
+  keeps its length; it returns the table (logical order) so the caller can
+  copy the blocks to host memory before anything reuses them;
+* ``swap_in`` takes ceil(len / BS) fresh blocks in logical order (all or
+  nothing) for the copy back; a block that was shared comes back private;
+* a swapped-out id is neither live nor free: ``add_seq`` and ``fork`` reject
+  it, and only ``swap_in`` brings it back.
 """
 from __future__ import annotations
 
@@ -68,6 +80,7 @@ class BlockManagerModel:
         self.rc = [0] * num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
+        self.swapped: Dict[int, int] = {}
         self.cow_count = 0
 
     # -- queries -------------------------------------------------------------
@@ -102,7 +115,7 @@ class BlockManagerModel:
         return b
 
     def add_seq(self, seq: int, n: int) -> List[int]:
-        if seq in self.tables or n < 0:
+        if seq in self.tables or seq in self.swapped or n < 0:
             raise InvalidOp("sequence exists or negative length")
         need = -(-n // self.BS)
         if need > len(self.free):
@@ -149,7 +162,7 @@ class BlockManagerModel:
         return slots, pairs
 
     def fork(self, parent: int, child: int) -> None:
-        if parent not in self.tables or child in self.tables:
+        if parent not in self.tables or child in self.tables or child in self.swapped:
             raise InvalidOp("bad fork")
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
@@ -164,6 +177,29 @@ class BlockManagerModel:
             if self.rc[b] == 0:
                 self.free.append(b)
         del self.lens[seq]
+
+    def swap_out(self, seq: int) -> List[int]:
+        if seq not in self.tables:
+            raise InvalidOp("unknown sequence")
+        table = list(self.tables[seq])
+        self.swapped[seq] = self.lens[seq]
+        self.free_seq(seq)
+        return table
+
+    def swap_in(self, seq: int) -> List[int]:
+        if seq not in self.swapped:
+            raise InvalidOp("not swapped out")
+        n = self.swapped[seq]
+        need = -(-n // self.BS)
+        if need > len(self.free):
+            raise OutOfBlocks()
+        del self.swapped[seq]
+        self.tables[seq] = [self._pop() for _ in range(need)]
+        self.lens[seq] = n
+        return list(self.tables[seq])
+
+    def swapped_len(self, seq: int) -> int:
+        return self.swapped.get(seq, -1)
 
     def export(self, seqs: Sequence[int], stride: int):
         """int32 tables [n][stride] padded with -1, int32 context lengths [n]."""

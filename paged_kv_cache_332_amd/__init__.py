@@ -23,7 +23,7 @@ __all__ = [
     "PA_PHASE_PASS", "PA_PHASE_MERGE", "PA_PHASE_ALL",
     "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
     "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version", "pa_step",
-    "pa_decode_stream_grid", "step_record_words", "pa_stream_plan", "pa_prefill", "pa_step_layer",
+    "pa_decode_stream_grid", "step_record_words", "pa_stream_plan", "pa_prefill", "pa_swap_blocks", "pa_step_layer",
     "STEP_KV", "STEP_PASS", "STEP_MERGE", "STEP_ALL",
 ]
 
@@ -71,6 +71,10 @@ _sig("pa_bm_free_seq", _i32, _vp, _i64)
 _sig("pa_bm_export", _i32, _vp, _pi64, _i32, _i32, _pi32, _pi32)
 _sig("pa_bm_num_free", _i32, _vp)
 _sig("pa_bm_admit", _i32, _vp, _i64, _i32, _i32, _pi32)
+_sig("pa_bm_swap_out", _i32, _vp, _i64, _pi32, _pi32)
+_sig("pa_bm_swap_in", _i32, _vp, _i64, _pi32, _pi32)
+_sig("pa_bm_swapped_len", _i32, _vp, _i64)
+_sig("pa_swap_blocks", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
 _sig("pa_bm_occupancy", _i32, _vp, _pi64)
 _sig("pa_bm_refcount", _i32, _vp, _i32)
 _sig("pa_bm_seq_len", _i32, _vp, _i64)
@@ -200,6 +204,23 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
               partition_size: int = 0, workspace=None, stream=None) -> None:
     pa_decode_variant(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                       partition_size, workspace, stream, PA_KERNEL_AUTO)
+
+
+def pa_swap_blocks(k_cache, v_cache, host_k, host_v, blocks, to_host: bool, stream=None) -> None:
+    """Whole blocks between the pools and pinned host tensors ([n][Hkv*D*BS]
+    elements each); ``blocks`` is an int32 tensor, pinned or on the device."""
+    import torch
+    n_, hkv, d, bs = _pool_dims(k_cache, v_cache)
+    per_block = hkv * d * bs
+    if blocks.dtype != torch.int32 or not blocks.is_contiguous():
+        raise PAError("pa_swap_blocks: blocks must be a contiguous int32 tensor")
+    for name, h in (("host_k", host_k), ("host_v", host_v)):
+        if h.dtype != k_cache.dtype or not h.is_contiguous() or h.numel() < blocks.numel() * per_block:
+            raise PAError(f"pa_swap_blocks: {name} must be a contiguous {k_cache.dtype} tensor of at least "
+                          f"{blocks.numel()} x {per_block} elements")
+    _check(lib.pa_swap_blocks(k_cache.data_ptr(), v_cache.data_ptr(), host_k.data_ptr(), host_v.data_ptr(),
+                              blocks.data_ptr(), int(blocks.numel()), 1 if to_host else 0, hkv, d, bs, n_,
+                              torch_dtype_code(k_cache.dtype), _stream(stream)))
 
 
 def pa_prefill(out, q, k_cache, v_cache, block_tables, query_start, context_lens, max_query_len: int,
@@ -335,6 +356,26 @@ class BlockManager:
         out = np.empty(max(num_tokens, 0), dtype=np.int32)
         _check(lib.pa_bm_admit(self._h, int(seq), int(num_tokens), int(reserve_blocks), out.ctypes.data_as(_pi32)))
         return out
+
+    def swap_out(self, seq: int) -> np.ndarray:
+        """Release the sequence's blocks, keeping its length; returns its table
+        (copy the blocks out before they are reused)."""
+        n = max(0, -(-max(self.seq_len(seq), 0) // self.block_size))
+        out = np.empty(max(n, 1), dtype=np.int32)
+        cnt = ctypes.c_int32(0)
+        _check(lib.pa_bm_swap_out(self._h, int(seq), out.ctypes.data_as(_pi32), ctypes.byref(cnt)))
+        return out[: cnt.value].copy()
+
+    def swap_in(self, seq: int) -> np.ndarray:
+        """Fresh blocks for a swapped-out sequence, in logical order."""
+        n = max(0, -(-max(self.swapped_len(seq), 0) // self.block_size))
+        out = np.empty(max(n, 1), dtype=np.int32)
+        cnt = ctypes.c_int32(0)
+        _check(lib.pa_bm_swap_in(self._h, int(seq), out.ctypes.data_as(_pi32), ctypes.byref(cnt)))
+        return out[: cnt.value].copy()
+
+    def swapped_len(self, seq: int) -> int:
+        return int(lib.pa_bm_swapped_len(self._h, int(seq)))
 
     def occupancy(self) -> Tuple[int, int, int, int]:
         """(slots of held blocks, tokens, unused slots in last blocks, free slots)."""

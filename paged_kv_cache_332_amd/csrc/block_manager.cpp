@@ -26,6 +26,7 @@ struct pa_bm {
   std::vector<int32_t> free_stack;  // back() is the next block handed out
   std::vector<int32_t> refcount;
   std::unordered_map<int64_t, Seq> seqs;
+  std::unordered_map<int64_t, int32_t> swapped;  // lengths of sequences held on the host
   int64_t cow_count = 0;
 
   int32_t take() {
@@ -71,7 +72,8 @@ void pa_bm_destroy(pa_bm* bm) { delete bm; }
 
 pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t num_tokens, int32_t* slots_out) {
   if (!bm || num_tokens < 0) return pa::fail(PA_ERR_INVALID, "pa_bm_add_seq: bad arguments");
-  if (bm->seqs.count(seq)) return pa::fail(PA_ERR_INVALID, "pa_bm_add_seq: sequence %lld exists", (long long)seq);
+  if (bm->seqs.count(seq) || bm->swapped.count(seq))
+    return pa::fail(PA_ERR_INVALID, "pa_bm_add_seq: sequence %lld exists", (long long)seq);
   int64_t need = (static_cast<int64_t>(num_tokens) + bm->block_size - 1) / bm->block_size;
   if (need > static_cast<int64_t>(bm->free_stack.size()))
     return pa::fail(PA_ERR_OOM, "pa_bm_add_seq: need %lld blocks, %zu free", (long long)need,
@@ -169,7 +171,7 @@ pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t*
 pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   if (!bm) return pa::fail(PA_ERR_INVALID, "pa_bm_fork: null manager");
   auto it = bm->seqs.find(parent);
-  if (it == bm->seqs.end() || bm->seqs.count(child))
+  if (it == bm->seqs.end() || bm->seqs.count(child) || bm->swapped.count(child))
     return pa::fail(PA_ERR_INVALID, "pa_bm_fork: unknown parent %lld or existing child %lld",
                     (long long)parent, (long long)child);
   pa_bm::Seq s = it->second;
@@ -192,6 +194,55 @@ pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq) {
   }
   bm->seqs.erase(it);
   return PA_OK;
+}
+
+pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq, int32_t* blocks_out, int32_t* num_blocks_out) {
+  if (!bm || !num_blocks_out) return pa::fail(PA_ERR_INVALID, "pa_bm_swap_out: bad arguments");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end())
+    return pa::fail(PA_ERR_INVALID, "pa_bm_swap_out: unknown sequence %lld", (long long)seq);
+  const std::vector<int32_t>& t = it->second.table;
+  if (!t.empty() && !blocks_out) return pa::fail(PA_ERR_INVALID, "pa_bm_swap_out: bad arguments");
+  for (int32_t b : t) {
+    if (bm->refcount[b] <= 0)
+      return pa::fail(PA_ERR_INVALID, "pa_bm_swap_out: refcount underflow on block %d", b);
+  }
+  std::copy(t.begin(), t.end(), blocks_out);
+  *num_blocks_out = static_cast<int32_t>(t.size());
+  // released like pa_bm_free_seq: the caller copies the blocks out on the
+  // same stream before anything can reuse them
+  for (int32_t b : t) {
+    if (--bm->refcount[b] == 0) bm->free_stack.push_back(b);
+  }
+  bm->swapped[seq] = it->second.len;
+  bm->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq, int32_t* blocks_out, int32_t* num_blocks_out) {
+  if (!bm || !num_blocks_out) return pa::fail(PA_ERR_INVALID, "pa_bm_swap_in: bad arguments");
+  auto it = bm->swapped.find(seq);
+  if (it == bm->swapped.end() || bm->seqs.count(seq))
+    return pa::fail(PA_ERR_INVALID, "pa_bm_swap_in: sequence %lld is not swapped out", (long long)seq);
+  const int32_t len = it->second;
+  const int64_t need = (static_cast<int64_t>(len) + bm->block_size - 1) / bm->block_size;
+  if (need > 0 && !blocks_out) return pa::fail(PA_ERR_INVALID, "pa_bm_swap_in: bad arguments");
+  if (need > static_cast<int64_t>(bm->free_stack.size()))
+    return pa::fail(PA_ERR_OOM, "pa_bm_swap_in: need %lld blocks, %zu free", (long long)need, bm->free_stack.size());
+  pa_bm::Seq s;
+  s.len = len;
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(bm->take());
+  std::copy(s.table.begin(), s.table.end(), blocks_out);
+  *num_blocks_out = static_cast<int32_t>(need);
+  bm->seqs.emplace(seq, std::move(s));
+  bm->swapped.erase(it);
+  return PA_OK;
+}
+
+int32_t pa_bm_swapped_len(const pa_bm* bm, int64_t seq) {
+  if (!bm) return -1;
+  auto it = bm->swapped.find(seq);
+  return it == bm->swapped.end() ? -1 : it->second;
 }
 
 pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t stride,

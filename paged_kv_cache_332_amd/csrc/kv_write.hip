@@ -138,6 +138,36 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* k_new, cons
   return hipGetLastError();
 }
 
+// Whole blocks (all kv heads, K and V) between the pools and host memory the
+// device can address: block blocks[i] <-> host slot i ([n][units] 16-byte
+// units per pool).  Grid (n, 2, chunks): y selects K or V.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(u32x4* __restrict__ kc, u32x4* __restrict__ vc,
+                                                          u32x4* __restrict__ hk, u32x4* __restrict__ hv,
+                                                          const int32_t* __restrict__ blocks, int64_t units,
+                                                          int32_t num_blocks, int32_t to_host) {
+  const int64_t i = blockIdx.x;
+  const int64_t b = blocks[i];
+  if (b < 0 || b >= num_blocks) return;  // an id outside the pool moves nothing
+  u32x4* dev = (blockIdx.y ? vc : kc) + b * units;
+  u32x4* host = (blockIdx.y ? hv : hk) + i * units;
+  for (int64_t u = int64_t(blockIdx.z) * blockDim.x + threadIdx.x; u < units; u += int64_t(gridDim.z) * blockDim.x) {
+    if (to_host) host[u] = dev[u];
+    else dev[u] = host[u];
+  }
+}
+
+hipError_t launch_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_v, const int32_t* blocks,
+                              int32_t n, int64_t block_bytes, int32_t num_blocks, int32_t to_host,
+                              hipStream_t stream) {
+  const int64_t units = block_bytes / 16;
+  const int32_t chunks = static_cast<int32_t>(std::min<int64_t>(16, (units + 255) / 256));
+  dim3 grid(n, 2, chunks), block(256);
+  hipLaunchKernelGGL(swap_blocks_kernel, grid, block, 0, stream, static_cast<u32x4*>(k_cache),
+                     static_cast<u32x4*>(v_cache), static_cast<u32x4*>(host_k), static_cast<u32x4*>(host_v), blocks,
+                     units, num_blocks, to_host);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                               int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,
                               hipStream_t stream) {

@@ -23,6 +23,23 @@ int elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
 bool valid_dtype(pa_dtype d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The pointer itself if the device can address it: device memory, or pinned
+// host memory mapped at the same address on the device (one unified address
+// space); nullptr otherwise.
+void* device_address(const void* p) {
+  hipPointerAttribute_t attr{};
+  void* dev = nullptr;
+  if (hipPointerGetAttributes(&attr, p) == hipSuccess) {
+    if (attr.type == hipMemoryTypeHost && attr.devicePointer && attr.devicePointer == attr.hostPointer) {
+      dev = const_cast<void*>(p);
+    } else if (attr.type == hipMemoryTypeDevice) {
+      dev = const_cast<void*>(p);
+    }
+  }
+  (void)hipGetLastError();  // a plain host pointer leaves an error behind
+  return dev;
+}
+
 pa_status check_cache_shape(const char* fn, int32_t num_kv_heads, int32_t head_dim,
                             int32_t block_size, int32_t num_blocks, pa_dtype dtype) {
   if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID, "%s: unknown dtype %d", fn, int(dtype));
@@ -100,6 +117,29 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
                         pa::launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, num_kv_heads, head_dim,
                                                block_size, pa::elem_bytes(dtype),
                                                static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_v, const int32_t* blocks,
+                         int32_t num_blocks_moved, int32_t to_host, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream) {
+  const char* fn = "pa_swap_blocks";
+  if (pa_status st = pa::check_cache_shape(fn, num_kv_heads, head_dim, block_size, num_blocks, dtype)) return st;
+  if (num_blocks_moved < 0 || (to_host != 0 && to_host != 1))
+    return pa::fail(PA_ERR_INVALID, "%s: bad arguments", fn);
+  if (num_blocks_moved == 0) return PA_OK;
+  if (!k_cache || !v_cache || !host_k || !host_v || !blocks) return pa::fail(PA_ERR_INVALID, "%s: null pointer", fn);
+  if (!pa::aligned16(k_cache) || !pa::aligned16(v_cache) || !pa::aligned16(host_k) || !pa::aligned16(host_v))
+    return pa::fail(PA_ERR_INVALID, "%s: caches and host buffers must be 16-byte aligned", fn);
+  // the host buffers and the list must be addressable by the device: pinned
+  // host memory (its device address is used) or device memory
+  void* hk = pa::device_address(host_k);
+  void* hv = pa::device_address(host_v);
+  const int32_t* bl = static_cast<const int32_t*>(pa::device_address(blocks));
+  if (!hk || !hv || !bl)
+    return pa::fail(PA_ERR_INVALID, "%s: host buffers and the block list must be pinned host or device memory", fn);
+  const int64_t block_bytes = int64_t(num_kv_heads) * head_dim * block_size * pa::elem_bytes(dtype);
+  return pa::hip_status(fn, pa::launch_swap_blocks(k_cache, v_cache, hk, hv, bl, num_blocks_moved, block_bytes,
+                                                   num_blocks, to_host, static_cast<hipStream_t>(stream)));
 }
 
 int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,

@@ -99,6 +99,11 @@ hipError_t launch_step_stage(const int32_t* rec_host, int32_t* rec_dev, int64_t 
                              void* v_cache, const void* k_new, const void* v_new, int32_t hkv, int32_t d,
                              int32_t bs, int32_t elem_bytes, const int32_t* slots_host, hipStream_t stream);
 
+// block_bytes = bytes of one block of one pool (all kv heads), a multiple of
+// 16; ids outside [0, num_blocks) are skipped
+hipError_t launch_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_v, const int32_t* blocks,
+                              int32_t n, int64_t block_bytes, int32_t num_blocks, int32_t to_host,
+                              hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                               int32_t hkv, int32_t d, int32_t bs, int32_t elem_bytes,
                               hipStream_t stream);

@@ -206,6 +206,8 @@ def bm_invariants(bm):
     for b in free:
         assert refs[b] == 0
     assert len(free) + sum(1 for r in refs if r > 0) == N
+    # a swapped-out sequence holds no block and is not live
+    assert not set(getattr(bm, "swapped", {})) & set(bm.tables)
 
 
 # ------------------------------------------------------------------- cache
@@ -262,3 +264,58 @@ def check_copy_blocks(Cache):
     assert np.array_equal(k1[3], k0[1]) and np.array_equal(v1[3], v0[1])
     others = [b for b in range(6) if b != 3]
     assert np.array_equal(k1[others], k0[others]) and np.array_equal(v1[others], v0[others])
+
+
+def check_bm_swap(BM, OutOfBlocks, InvalidOp):
+    """Preemption by swap, hand-traced on tiny pools (LIFO free stack, blocks
+    released in logical order, fresh blocks taken in logical order)."""
+    bm = BM(6, 4)
+    assert bm.add_seq(0, 10)[:5] == [0, 1, 2, 3, 4]           # table [0, 1, 2]
+    assert bm.swap_out(0) == [0, 1, 2]
+    assert bm.num_free() == 6 and bm.swapped == {0: 10}
+    for bad in (lambda: bm.add_seq(0, 1), lambda: bm.swap_out(0), lambda: bm.append([0])):
+        try:
+            bad()
+            raise AssertionError("a swapped-out id must be rejected")
+        except InvalidOp:
+            pass
+    bm.add_seq(1, 1)                                          # takes block 2 (top of the stack)
+    try:
+        bm.fork(1, 0)
+        raise AssertionError("fork onto a swapped-out id must be rejected")
+    except InvalidOp:
+        pass
+    assert bm.swap_in(0) == [1, 0, 3]                         # next three on the stack
+    assert bm.lens[0] == 10 and bm.swapped == {}
+    assert bm.tables[0] == [1, 0, 3]
+
+    # a shared block stays resident for its other sharer; it comes back private
+    bm = BM(5, 4)
+    bm.add_seq(1, 8)                                          # [0, 1]
+    bm.fork(1, 2)
+    assert bm.swap_out(1) == [0, 1]
+    assert [bm.refcount(b) for b in range(5)] == [1, 1, 0, 0, 0] and bm.num_free() == 3
+    assert bm.swap_in(1) == [2, 3]
+    assert [bm.refcount(b) for b in range(5)] == [1, 1, 1, 1, 0]
+    assert bm.tables[2] == [0, 1]
+
+    # all or nothing when the pool is short
+    bm = BM(3, 4)
+    bm.add_seq(1, 12)                                         # [0, 1, 2]
+    bm.swap_out(1)                                            # stack bottom..top = 0, 1, 2
+    bm.add_seq(2, 5)                                          # [2, 1]
+    snap = (list(bm.free), [bm.refcount(b) for b in range(3)], dict(bm.swapped))
+    try:
+        bm.swap_in(1)
+        raise AssertionError("swap_in must fail without three free blocks")
+    except OutOfBlocks:
+        pass
+    assert snap == (list(bm.free), [bm.refcount(b) for b in range(3)], dict(bm.swapped))
+    bm.free_seq(2)
+    assert bm.swap_in(1) == [1, 2, 0]
+
+    # an empty sequence swaps without blocks
+    bm = BM(2, 4)
+    bm.add_seq(5, 0)
+    assert bm.swap_out(5) == [] and bm.swapped == {5: 0}
+    assert bm.swap_in(5) == [] and bm.lens[5] == 0

@@ -42,6 +42,7 @@ class CppBM:
         self.N, self.BS = num_blocks, block_size
         self.m = pa.BlockManager(num_blocks, block_size, order)
         self._seqs = set()
+        self._swapped = set()
 
     def _wrap(self, fn, *a):
         try:
@@ -67,6 +68,22 @@ class CppBM:
     def free_seq(self, seq):
         self._wrap(self.m.free_seq, seq)
         self._seqs.discard(seq)
+
+    def swap_out(self, seq):
+        out = [int(b) for b in self._wrap(self.m.swap_out, seq)]
+        self._seqs.discard(seq)
+        self._swapped.add(seq)
+        return out
+
+    def swap_in(self, seq):
+        out = [int(b) for b in self._wrap(self.m.swap_in, seq)]
+        self._swapped.discard(seq)
+        self._seqs.add(seq)
+        return out
+
+    @property
+    def swapped(self):
+        return {s: self.m.swapped_len(s) for s in self._swapped}
 
     def export(self, seqs, stride):
         return self._wrap(self.m.export, list(seqs), stride)
@@ -106,6 +123,10 @@ def test_cpp_block_manager_golden():
     P.check_bm_golden(CppBM, OutOfBlocks)
 
 
+def test_cpp_block_manager_swap():
+    P.check_bm_swap(CppBM, OutOfBlocks, InvalidOp)
+
+
 def test_cpp_create_rejects_bad_order():
     with pytest.raises(pa.PAError):
         pa.BlockManager(4, 16, [0, 1, 1, 2])
@@ -118,11 +139,12 @@ def _same_state(cpp: CppBM, model: BlockManagerModel):
     assert cpp.rc == model.rc
     assert cpp.tables == {s: t for s, t in model.tables.items()}
     assert cpp.lens == model.lens
+    assert cpp.swapped == model.swapped
     assert tuple(cpp.stats()) == tuple(model.stats())
 
 
 @settings(max_examples=80, deadline=None)
-@given(st.lists(st.tuples(st.integers(0, 4), st.integers(0, 7), st.integers(0, 40)), max_size=50),
+@given(st.lists(st.tuples(st.integers(0, 6), st.integers(0, 7), st.integers(0, 40)), max_size=50),
        st.sampled_from([1, 4, 8, 16]), st.integers(0, 2**31 - 1))
 def test_cpp_matches_model_on_random_ops(ops, bs, seed):
     order = list(np.random.default_rng(seed).permutation(20))
@@ -139,6 +161,10 @@ def test_cpp_matches_model_on_random_ops(ops, bs, seed):
                     r = bm.fork(seq, (seq + n) % 8)
                 elif kind == 3:
                     r = bm.free_seq(seq)
+                elif kind == 5:
+                    r = bm.swap_out(seq)
+                elif kind == 6:
+                    r = bm.swap_in(seq)
                 else:
                     r = bm.append([seq])
                 results.append(("ok", r))
@@ -362,3 +388,23 @@ def test_prefill_rejects_bad_arguments(over, status):
     """Host validation of pa_prefill, before any launch."""
     assert pa.lib.pa_prefill(*_prefill_args(**over)) == status
     assert pa.lib.pa_last_error()
+
+
+def _swap_args(**over):
+    a = dict(k=16, v=16, hk=16, hv=16, blocks=16, n=4, to_host=1, Hkv=8, D=128, BS=16, N=1000, dtype=pa.PA_BF16,
+             stream=0)
+    a.update(over)
+    return [a[k] for k in ["k", "v", "hk", "hv", "blocks", "n", "to_host", "Hkv", "D", "BS", "N", "dtype", "stream"]]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(to_host=2), 1), (dict(n=-1), 1), (dict(D=96), 4), (dict(BS=12), 4), (dict(N=0), 1), (dict(dtype=7), 1),
+    (dict(hk=0), 1), (dict(hv=8), 1),
+    (dict(), 1),              # pointers the device cannot address (no device here)
+    (dict(n=0, hk=0), 0),     # nothing to move
+])
+def test_swap_blocks_rejects_bad_arguments(over, status):
+    """Host validation of pa_swap_blocks, before any launch."""
+    assert pa.lib.pa_swap_blocks(*_swap_args(**over)) == status
+    if status:
+        assert pa.lib.pa_last_error()

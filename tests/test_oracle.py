@@ -69,6 +69,37 @@ def test_bm_errors_change_nothing():
     assert snap == (list(bm.free), list(bm.rc), {k: list(v) for k, v in bm.tables.items()}, dict(bm.lens))
 
 
+def test_bm_swap_pins():
+    P.check_bm_swap(BlockManagerModel, OutOfBlocks, InvalidOp)
+
+
+def test_swap_round_trip_restores_the_sequence():
+    """Swap a sequence out (blocks copied to host arrays), let another
+    sequence take and overwrite its blocks, swap it back into fresh blocks:
+    its gathered K/V and its decode output are unchanged."""
+    rng = np.random.default_rng(3)
+    H, D, BS, N = 2, 16, 4, 8
+    cache = PagedCacheModel(N, H, D, BS, "bf16")
+    bm = BlockManagerModel(N, BS, rng.permutation(N))
+    k = W.round_to_dtype(rng.standard_normal((11, H, D), dtype=np.float32), "bf16")
+    v = W.round_to_dtype(rng.standard_normal((11, H, D), dtype=np.float32), "bf16")
+    cache.write(bm.add_seq(0, 11), k, v)
+    q = rng.standard_normal((H, D))
+    k0, v0 = cache.gather(bm.table(0), 11)
+    ref = A.decode_attention(q, k0, v0, 0.25)
+    blocks = bm.swap_out(0)
+    host_k, host_v = cache.k[blocks].copy(), cache.v[blocks].copy()
+    other = bm.add_seq(1, N * BS)                              # every block, overwritten
+    cache.write(other, np.ones((N * BS, H, D), np.float32), -np.ones((N * BS, H, D), np.float32))
+    bm.free_seq(1)
+    fresh = bm.swap_in(0)
+    assert fresh != blocks
+    cache.k[fresh], cache.v[fresh] = host_k, host_v
+    k1, v1 = cache.gather(bm.table(0), 11)
+    assert np.array_equal(k1, k0) and np.array_equal(v1, v0)
+    assert np.array_equal(A.decode_attention(q, k1, v1, 0.25), ref)
+
+
 def test_bm_interchangeable_blocks_after_churn():
     """Every free block is interchangeable: after any churn an allocation of
     k blocks succeeds exactly when k <= num_free."""
@@ -91,7 +122,7 @@ def test_bm_interchangeable_blocks_after_churn():
 
 
 @settings(max_examples=60, deadline=None)
-@given(st.lists(st.tuples(st.integers(0, 4), st.integers(0, 7), st.integers(0, 40)), max_size=60),
+@given(st.lists(st.tuples(st.integers(0, 6), st.integers(0, 7), st.integers(0, 40)), max_size=60),
        st.sampled_from([1, 4, 8]))
 def test_bm_random_ops_keep_invariants(ops, bs):
     bm = BlockManagerModel(24, bs, list(reversed(range(24))))
@@ -105,6 +136,10 @@ def test_bm_random_ops_keep_invariants(ops, bs):
                 bm.fork(seq, (seq + n) % 8)
             elif kind == 3:
                 bm.free_seq(seq)
+            elif kind == 5:
+                bm.swap_out(seq)
+            elif kind == 6:
+                bm.swap_in(seq)
             else:
                 bm.append([seq])
         except (OutOfBlocks, InvalidOp):

@@ -92,6 +92,25 @@ def test_block_manager_mutant_is_caught(name, old, new):
     assert _fails([lambda: P.check_bm_golden(m.BlockManagerModel, m.OutOfBlocks)]), name
 
 
+SWAP_MUTANTS = [
+    ("swap_out keeps its blocks", "        self.swapped[seq] = self.lens[seq]\n        self.free_seq(seq)",
+     "        self.swapped[seq] = self.lens[seq]\n        del self.tables[seq], self.lens[seq]"),
+    ("swapped id reused by add_seq", "if seq in self.tables or seq in self.swapped or n < 0:",
+     "if seq in self.tables or n < 0:"),
+    ("swap_in loses a token", "        n = self.swapped[seq]\n", "        n = max(self.swapped[seq] - 1, 0)\n"),
+    ("swap_in takes blocks in reverse", "        self.tables[seq] = [self._pop() for _ in range(need)]\n        self.lens[seq] = n\n        return list",
+     "        self.tables[seq] = [self._pop() for _ in range(need)][::-1]\n        self.lens[seq] = n\n        return list"),
+    ("swap_in not all-or-nothing", "            raise OutOfBlocks()\n        del self.swapped[seq]",
+     "            need = len(self.free)\n        del self.swapped[seq]"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", SWAP_MUTANTS, ids=[m[0] for m in SWAP_MUTANTS])
+def test_swap_mutant_is_caught(name, old, new):
+    m = _mutant("block_manager", old, new)
+    assert _fails([lambda: P.check_bm_swap(m.BlockManagerModel, m.OutOfBlocks, m.InvalidOp)]), name
+
+
 CACHE_MUTANTS = [
     ("V stored token-major", "self.v[blk, :, :, off] = vb", "self.v.reshape(self.N, self.H, self.BS, self.D)[blk, :, off, :] = vb"),
     ("K chunk transposed", "kx = kb.reshape(T, self.H, self.D // self.X, self.X)",
@@ -121,6 +140,7 @@ def test_unmutated_copy_passes_every_pin(module):
         P.check_split_merge(m.split_k, m.lse_merge, m.decode_attention)
     elif module == "block_manager":
         P.check_bm_golden(m.BlockManagerModel, m.OutOfBlocks)
+        P.check_bm_swap(m.BlockManagerModel, m.OutOfBlocks, m.InvalidOp)
     else:
         P.check_layout_golden(m.PagedCacheModel)
         P.check_copy_blocks(m.PagedCacheModel)
