@@ -251,6 +251,34 @@ pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq, int32_t* blocks_out, int32_t* n
 pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq, int32_t* blocks_out, int32_t* num_blocks_out);
 int32_t pa_bm_swapped_len(const pa_bm* bm, int64_t seq);
 
+/* Prefix caching across requests ([VM] §Sharing comes almost for free and
+ * §Why this matters: a prompt prefix many requests share is stored once).
+ * pa_bm_add_seq_cached is pa_bm_add_seq for a prompt given by its token ids
+ * (tokens host int32 [num_tokens]): it walks the prompt's full blocks from the
+ * start and reuses every cached block found, stopping at the first miss and
+ * never reusing the block that holds the last token.  slots_out (room for
+ * num_tokens, or NULL) gets every token's slot; *cached_tokens_out the number
+ * of leading tokens whose K/V is already in the pool (a multiple of the block
+ * size): the caller writes K/V and runs prefill for the rest only.  Its other
+ * full blocks are cached at once under the key (content id of the previous
+ * block, the block's token ids), compared exactly; their K/V must be written
+ * on the stream before any later work reads them.
+ * A cached block whose last reference goes is kept, evictable, instead of
+ * freed; a sequence's blocks become evictable from its last to its first.
+ * Fresh blocks come from the free stack, then from the evictable blocks,
+ * oldest first (an evicted block's key is dropped).  pa_bm_num_free,
+ * pa_bm_admit and out[0] of pa_bm_stats count the evictable blocks as free;
+ * pa_bm_free_list lists the free stack only.  All-or-nothing: PA_ERR_OOM
+ * changes nothing. */
+pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t num_tokens,
+                               int32_t* slots_out, int32_t* cached_tokens_out);
+/* out[4] = {cached blocks, evictable blocks, blocks reused so far, full blocks
+ * looked up so far} */
+pa_status pa_bm_cache_stats(const pa_bm* bm, int64_t* out);
+/* Forget every cached prefix: evictable blocks go on the free stack (oldest
+ * first), live cached blocks become plain blocks. */
+pa_status pa_bm_cache_clear(pa_bm* bm);
+
 /* Admission that keeps headroom ([VM] §What it buys in practice: memory is
  * handed out in small increments, so a server can admit without committing to
  * a request's worst case and can tell how close it is to the ceiling):

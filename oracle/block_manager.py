@@ -47,6 +47,31 @@ blocks moved off the device and brought back later):
   nothing) for the copy back; a block that was shared comes back private;
 * a swapped-out id is neither live nor free: ``add_seq`` and ``fork`` reject
   it, and only ``swap_in`` brings it back.
+
+Prefix caching across requests ("Paged Attention: Virtual Memory for the KV
+Cache", §Sharing comes almost for free and §Why this matters…: a prompt
+prefix that many requests share is stored once and reused; the pages give no
+keying or eviction rule, the readings below are this model's):
+
+* a full block of a sequence added with its token ids is cached under the key
+  (content id of the previous block, the block's BS token ids); the first
+  block's parent is content id 0 and every newly cached block gets the next
+  content id, so a key names the whole prefix up to the block's end, exactly
+  (no hash is trusted);
+* ``add_seq_cached(seq, tokens)`` walks the prompt's full blocks from the start
+  and reuses every block found, stopping at the first miss and never reusing
+  the block that holds the last token (at least one token is computed); it
+  returns the slots of all tokens and the number of reused tokens, whose K/V
+  the caller does not write again;
+* fresh full blocks of such a sequence are cached at once (the caller writes
+  their K/V on the stream before anything reads them); a key already cached
+  is not cached twice;
+* a cached block whose count drops to zero is not freed but becomes evictable,
+  in least-recently-released order; a sequence's blocks are released from its
+  last block to its first, so the end of a prefix is evicted before its start;
+* a fresh block comes from the free stack, and only when it is empty from the
+  evictable list (the oldest first, dropping its key); the blocks a call can
+  get are the free ones plus the evictable ones it does not itself reuse.
 """
 from __future__ import annotations
 
@@ -82,10 +107,23 @@ class BlockManagerModel:
         self.lens: Dict[int, int] = {}
         self.swapped: Dict[int, int] = {}
         self.cow_count = 0
+        # prefix cache
+        self.cache: Dict[Tuple[int, Tuple[int, ...]], Tuple[int, int]] = {}   # key -> (content id, block)
+        self.block_key: Dict[int, Tuple[int, Tuple[int, ...]]] = {}
+        self.evictable: List[int] = []                                       # oldest first
+        self.next_cid = 1
+        self.hit_blocks = 0
+        self.query_blocks = 0
 
     # -- queries -------------------------------------------------------------
     def num_free(self) -> int:
-        return len(self.free)
+        """Blocks a call can get: the free stack plus the evictable cached blocks."""
+        return len(self.free) + len(self.evictable)
+
+    def cache_stats(self) -> Tuple[int, int, int, int]:
+        """(cached blocks, evictable blocks, reused blocks so far, full
+        blocks looked up so far)."""
+        return len(self.block_key), len(self.evictable), self.hit_blocks, self.query_blocks
 
     def refcount(self, block: int) -> int:
         return self.rc[block]
@@ -106,19 +144,37 @@ class BlockManagerModel:
         used = sum(1 for c in self.rc if c > 0)
         shared = sum(1 for c in self.rc if c > 1)
         waste = sum(len(self.tables[s]) * self.BS - self.lens[s] for s in self.tables)
-        return len(self.free), used, shared, self.cow_count, waste
+        return self.num_free(), used, shared, self.cow_count, waste
 
     # -- operations ----------------------------------------------------------
     def _pop(self) -> int:
-        b = self.free.pop()
+        if self.free:
+            b = self.free.pop()
+        else:
+            b = self.evictable.pop(0)
+            del self.cache[self.block_key.pop(b)]
         self.rc[b] = 1
         return b
+
+    def _release(self, table: Sequence[int]) -> None:
+        """Drop one reference of each block, in logical order; a block that
+        reaches zero goes on the free stack, or, if cached, becomes evictable
+        (the sequence's cached blocks in reverse logical order)."""
+        cached = []
+        for b in table:
+            self.rc[b] -= 1
+            if self.rc[b] == 0:
+                if b in self.block_key:
+                    cached.append(b)
+                else:
+                    self.free.append(b)
+        self.evictable.extend(reversed(cached))
 
     def add_seq(self, seq: int, n: int) -> List[int]:
         if seq in self.tables or seq in self.swapped or n < 0:
             raise InvalidOp("sequence exists or negative length")
         need = -(-n // self.BS)
-        if need > len(self.free):
+        if need > self.num_free():
             raise OutOfBlocks()
         self.tables[seq] = [self._pop() for _ in range(need)]
         self.lens[seq] = n
@@ -142,7 +198,7 @@ class BlockManagerModel:
                 if c > 1:
                     need += 1
                     rc[last] = c - 1
-        if need > len(self.free):
+        if need > self.num_free():
             raise OutOfBlocks()
         slots, pairs = [], []
         for s in seqs:
@@ -172,11 +228,60 @@ class BlockManagerModel:
     def free_seq(self, seq: int) -> None:
         if seq not in self.tables:
             raise InvalidOp("unknown sequence")
-        for b in self.tables.pop(seq):
-            self.rc[b] -= 1
-            if self.rc[b] == 0:
-                self.free.append(b)
+        self._release(self.tables.pop(seq))
         del self.lens[seq]
+
+    def add_seq_cached(self, seq: int, tokens: Sequence[int]) -> Tuple[List[int], int]:
+        """add_seq with the prompt's token ids: reuses cached full blocks of
+        its prefix.  Returns (slots of all tokens, reused tokens)."""
+        tokens = [int(t) for t in tokens]
+        if seq in self.tables or seq in self.swapped:
+            raise InvalidOp("sequence exists")
+        n, BS = len(tokens), self.BS
+        nb = -(-n // BS)
+        full = n // BS
+        lookable = (n - 1) // BS if n else 0          # the block of the last token is computed
+        parent, hits = 0, []
+        for i in range(lookable):
+            key = (parent, tuple(tokens[i * BS:(i + 1) * BS]))
+            if key not in self.cache:
+                break
+            parent, b = self.cache[key]
+            hits.append(b)
+        revived = sum(1 for b in hits if self.rc[b] == 0)
+        if nb - len(hits) > self.num_free() - revived:
+            raise OutOfBlocks()
+        self.query_blocks += lookable
+        self.hit_blocks += len(hits)
+        for b in hits:
+            if self.rc[b] == 0:
+                self.evictable.remove(b)
+            self.rc[b] += 1
+        table = list(hits)
+        for i in range(len(hits), nb):
+            b = self._pop()
+            table.append(b)
+            if i < full:
+                key = (parent, tuple(tokens[i * BS:(i + 1) * BS]))
+                if key in self.cache:
+                    parent = self.cache[key][0]
+                else:
+                    cid = self.next_cid
+                    self.next_cid += 1
+                    self.cache[key] = (cid, b)
+                    self.block_key[b] = key
+                    parent = cid
+        self.tables[seq] = table
+        self.lens[seq] = n
+        return [self.slot(seq, t) for t in range(n)], len(hits) * BS
+
+    def cache_clear(self) -> None:
+        """Forget every cached prefix; evictable blocks go on the free stack,
+        oldest first."""
+        self.free.extend(self.evictable)
+        self.evictable = []
+        self.cache.clear()
+        self.block_key.clear()
 
     def swap_out(self, seq: int) -> List[int]:
         if seq not in self.tables:
@@ -191,7 +296,7 @@ class BlockManagerModel:
             raise InvalidOp("not swapped out")
         n = self.swapped[seq]
         need = -(-n // self.BS)
-        if need > len(self.free):
+        if need > self.num_free():
             raise OutOfBlocks()
         del self.swapped[seq]
         self.tables[seq] = [self._pop() for _ in range(need)]

@@ -74,6 +74,9 @@ _sig("pa_bm_admit", _i32, _vp, _i64, _i32, _i32, _pi32)
 _sig("pa_bm_swap_out", _i32, _vp, _i64, _pi32, _pi32)
 _sig("pa_bm_swap_in", _i32, _vp, _i64, _pi32, _pi32)
 _sig("pa_bm_swapped_len", _i32, _vp, _i64)
+_sig("pa_bm_add_seq_cached", _i32, _vp, _i64, _pi32, _i32, _pi32, _pi32)
+_sig("pa_bm_cache_stats", _i32, _vp, _pi64)
+_sig("pa_bm_cache_clear", _i32, _vp)
 _sig("pa_swap_blocks", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp)
 _sig("pa_bm_occupancy", _i32, _vp, _pi64)
 _sig("pa_bm_refcount", _i32, _vp, _i32)
@@ -376,6 +379,25 @@ class BlockManager:
 
     def swapped_len(self, seq: int) -> int:
         return int(lib.pa_bm_swapped_len(self._h, int(seq)))
+
+    def add_seq_cached(self, seq: int, tokens) -> Tuple[np.ndarray, int]:
+        """add_seq for a prompt given by its token ids, reusing cached full
+        blocks of its prefix; returns (slots of all tokens, reused tokens)."""
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        out = np.empty(max(tok.size, 1), dtype=np.int32)
+        hit = ctypes.c_int32(0)
+        _check(lib.pa_bm_add_seq_cached(self._h, int(seq), tok.ctypes.data_as(_pi32), int(tok.size),
+                                        out.ctypes.data_as(_pi32), ctypes.byref(hit)))
+        return out[: tok.size].copy(), int(hit.value)
+
+    def cache_stats(self) -> Tuple[int, int, int, int]:
+        """(cached blocks, evictable blocks, reused blocks so far, looked-up blocks so far)"""
+        out = np.zeros(4, dtype=np.int64)
+        _check(lib.pa_bm_cache_stats(self._h, out.ctypes.data_as(_pi64)))
+        return tuple(int(x) for x in out)
+
+    def cache_clear(self) -> None:
+        _check(lib.pa_bm_cache_clear(self._h))
 
     def occupancy(self) -> Tuple[int, int, int, int]:
         """(slots of held blocks, tokens, unused slots in last blocks, free slots)."""

@@ -11,15 +11,44 @@
 // diverges copies the block it is about to write (§Sharing comes almost for
 // free).  The allocation policy the pages leave open is stated in pa.h.
 #include <algorithm>
+#include <cstring>
+#include <iterator>
+#include <list>
 #include <unordered_map>
 #include <vector>
 
 #include "pa_internal.h"
 
+// A cached full block is named by the content id of the block before it (0 for
+// a prompt's first block) and its own token ids: the key names the whole
+// prefix up to the block's end, and lookups compare it exactly.
+struct PrefixKey {
+  uint64_t parent = 0;
+  std::vector<int32_t> tokens;
+  bool operator==(const PrefixKey& o) const { return parent == o.parent && tokens == o.tokens; }
+};
+// Bucket hash only (FNV-1a, 64 bit, over the parent id and the token bytes).
+struct PrefixKeyHash {
+  size_t operator()(const PrefixKey& k) const {
+    uint64_t h = 14695981039346656037ull;
+    auto mix = [&h](const void* p, size_t n) {
+      const unsigned char* c = static_cast<const unsigned char*>(p);
+      for (size_t i = 0; i < n; ++i) h = (h ^ c[i]) * 1099511628211ull;
+    };
+    mix(&k.parent, sizeof(k.parent));
+    mix(k.tokens.data(), k.tokens.size() * sizeof(int32_t));
+    return static_cast<size_t>(h);
+  }
+};
+
 struct pa_bm {
   struct Seq {
     std::vector<int32_t> table;
     int32_t len = 0;
+  };
+  struct CacheEntry {
+    uint64_t cid;
+    int32_t block;
   };
   int32_t num_blocks = 0;
   int32_t block_size = 1;
@@ -28,12 +57,47 @@ struct pa_bm {
   std::unordered_map<int64_t, Seq> seqs;
   std::unordered_map<int64_t, int32_t> swapped;  // lengths of sequences held on the host
   int64_t cow_count = 0;
+  // prefix cache
+  std::unordered_map<PrefixKey, CacheEntry, PrefixKeyHash> cache;
+  std::unordered_map<int32_t, PrefixKey> block_key;  // cached block -> its key
+  std::list<int32_t> evictable;                      // cached, unreferenced; front = oldest
+  std::unordered_map<int32_t, std::list<int32_t>::iterator> evictable_at;
+  uint64_t next_cid = 1;
+  int64_t hit_blocks = 0, query_blocks = 0;
 
+  // blocks a call can get: the free stack, then the evictable cached blocks
+  int64_t available() const { return static_cast<int64_t>(free_stack.size() + evictable.size()); }
   int32_t take() {
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+    } else {
+      b = evictable.front();
+      evictable.pop_front();
+      evictable_at.erase(b);
+      auto k = block_key.find(b);
+      cache.erase(k->second);
+      block_key.erase(k);
+    }
     refcount[b] = 1;
     return b;
+  }
+  // One reference of each block dropped in logical order; a block reaching
+  // zero goes on the free stack or, if cached, to the evictable list (the
+  // table's cached blocks from last to first, so a prefix's end goes first).
+  void release(const std::vector<int32_t>& table) {
+    std::vector<int32_t> cached;
+    for (int32_t b : table) {
+      if (--refcount[b] == 0) {
+        if (block_key.count(b)) cached.push_back(b);
+        else free_stack.push_back(b);
+      }
+    }
+    for (auto it = cached.rbegin(); it != cached.rend(); ++it) {
+      evictable.push_back(*it);
+      evictable_at[*it] = std::prev(evictable.end());
+    }
   }
   int32_t slot(const Seq& s, int32_t pos) const {
     return s.table[pos / block_size] * block_size + pos % block_size;
@@ -75,9 +139,9 @@ pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t num_tokens, int32_t* slo
   if (bm->seqs.count(seq) || bm->swapped.count(seq))
     return pa::fail(PA_ERR_INVALID, "pa_bm_add_seq: sequence %lld exists", (long long)seq);
   int64_t need = (static_cast<int64_t>(num_tokens) + bm->block_size - 1) / bm->block_size;
-  if (need > static_cast<int64_t>(bm->free_stack.size()))
-    return pa::fail(PA_ERR_OOM, "pa_bm_add_seq: need %lld blocks, %zu free", (long long)need,
-                    bm->free_stack.size());
+  if (need > bm->available())
+    return pa::fail(PA_ERR_OOM, "pa_bm_add_seq: need %lld blocks, %lld free", (long long)need,
+                    (long long)bm->available());
   pa_bm::Seq s;
   s.table.reserve(need);
   for (int64_t i = 0; i < need; ++i) s.table.push_back(bm->take());
@@ -91,7 +155,7 @@ pa_status pa_bm_add_seq(pa_bm* bm, int64_t seq, int32_t num_tokens, int32_t* slo
 pa_status pa_bm_admit(pa_bm* bm, int64_t seq, int32_t num_tokens, int32_t reserve_blocks, int32_t* slots_out) {
   if (!bm || num_tokens < 0 || reserve_blocks < 0) return pa::fail(PA_ERR_INVALID, "pa_bm_admit: bad arguments");
   const int64_t need = (static_cast<int64_t>(num_tokens) + bm->block_size - 1) / bm->block_size;
-  const int64_t free_blocks = static_cast<int64_t>(bm->free_stack.size());
+  const int64_t free_blocks = bm->available();
   if (need + reserve_blocks > free_blocks)
     return pa::fail(PA_ERR_OOM, "pa_bm_admit: need %lld blocks and a reserve of %d, %lld free", (long long)need,
                     reserve_blocks, (long long)free_blocks);
@@ -109,7 +173,7 @@ pa_status pa_bm_occupancy(const pa_bm* bm, int64_t* out) {
   out[0] = held * bm->block_size;
   out[1] = tokens;
   out[2] = slack;
-  out[3] = static_cast<int64_t>(bm->free_stack.size()) * bm->block_size;
+  out[3] = bm->available() * bm->block_size;
   return PA_OK;
 }
 
@@ -142,9 +206,9 @@ pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t*
       }
     }
   }
-  if (need > static_cast<int64_t>(bm->free_stack.size()))
-    return pa::fail(PA_ERR_OOM, "pa_bm_append_slots: need %lld blocks, %zu free", (long long)need,
-                    bm->free_stack.size());
+  if (need > bm->available())
+    return pa::fail(PA_ERR_OOM, "pa_bm_append_slots: need %lld blocks, %lld free", (long long)need,
+                    (long long)bm->available());
   int32_t ncow = 0;
   for (int32_t i = 0; i < n; ++i) {
     pa_bm::Seq& s = *ptr[i];
@@ -189,9 +253,7 @@ pa_status pa_bm_free_seq(pa_bm* bm, int64_t seq) {
     if (bm->refcount[b] <= 0)
       return pa::fail(PA_ERR_INVALID, "pa_bm_free_seq: refcount underflow on block %d", b);
   }
-  for (int32_t b : it->second.table) {
-    if (--bm->refcount[b] == 0) bm->free_stack.push_back(b);
-  }
+  bm->release(it->second.table);
   bm->seqs.erase(it);
   return PA_OK;
 }
@@ -211,9 +273,7 @@ pa_status pa_bm_swap_out(pa_bm* bm, int64_t seq, int32_t* blocks_out, int32_t* n
   *num_blocks_out = static_cast<int32_t>(t.size());
   // released like pa_bm_free_seq: the caller copies the blocks out on the
   // same stream before anything can reuse them
-  for (int32_t b : t) {
-    if (--bm->refcount[b] == 0) bm->free_stack.push_back(b);
-  }
+  bm->release(t);
   bm->swapped[seq] = it->second.len;
   bm->seqs.erase(it);
   return PA_OK;
@@ -227,8 +287,9 @@ pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq, int32_t* blocks_out, int32_t* nu
   const int32_t len = it->second;
   const int64_t need = (static_cast<int64_t>(len) + bm->block_size - 1) / bm->block_size;
   if (need > 0 && !blocks_out) return pa::fail(PA_ERR_INVALID, "pa_bm_swap_in: bad arguments");
-  if (need > static_cast<int64_t>(bm->free_stack.size()))
-    return pa::fail(PA_ERR_OOM, "pa_bm_swap_in: need %lld blocks, %zu free", (long long)need, bm->free_stack.size());
+  if (need > bm->available())
+    return pa::fail(PA_ERR_OOM, "pa_bm_swap_in: need %lld blocks, %lld free", (long long)need,
+                    (long long)bm->available());
   pa_bm::Seq s;
   s.len = len;
   for (int64_t i = 0; i < need; ++i) s.table.push_back(bm->take());
@@ -236,6 +297,92 @@ pa_status pa_bm_swap_in(pa_bm* bm, int64_t seq, int32_t* blocks_out, int32_t* nu
   *num_blocks_out = static_cast<int32_t>(need);
   bm->seqs.emplace(seq, std::move(s));
   bm->swapped.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t num_tokens,
+                               int32_t* slots_out, int32_t* cached_tokens_out) {
+  if (!bm || num_tokens < 0 || (num_tokens > 0 && !tokens) || !cached_tokens_out)
+    return pa::fail(PA_ERR_INVALID, "pa_bm_add_seq_cached: bad arguments");
+  if (bm->seqs.count(seq) || bm->swapped.count(seq))
+    return pa::fail(PA_ERR_INVALID, "pa_bm_add_seq_cached: sequence %lld exists", (long long)seq);
+  const int32_t BS = bm->block_size;
+  const int64_t nb = (static_cast<int64_t>(num_tokens) + BS - 1) / BS;
+  const int32_t full = num_tokens / BS;
+  // the block holding the last token is always computed
+  const int32_t lookable = num_tokens > 0 ? (num_tokens - 1) / BS : 0;
+  PrefixKey key;
+  key.tokens.resize(BS);
+  uint64_t parent = 0;
+  std::vector<int32_t> hits;
+  int64_t revived = 0;
+  for (int32_t i = 0; i < lookable; ++i) {
+    key.parent = parent;
+    std::memcpy(key.tokens.data(), tokens + static_cast<int64_t>(i) * BS, sizeof(int32_t) * BS);
+    auto f = bm->cache.find(key);
+    if (f == bm->cache.end()) break;
+    parent = f->second.cid;
+    hits.push_back(f->second.block);
+    revived += bm->refcount[f->second.block] == 0;
+  }
+  const int64_t need = nb - static_cast<int64_t>(hits.size());
+  if (need > bm->available() - revived)
+    return pa::fail(PA_ERR_OOM, "pa_bm_add_seq_cached: need %lld blocks, %lld free", (long long)need,
+                    (long long)(bm->available() - revived));
+  bm->query_blocks += lookable;
+  bm->hit_blocks += static_cast<int64_t>(hits.size());
+  pa_bm::Seq s;
+  s.len = num_tokens;
+  s.table.reserve(nb);
+  for (int32_t b : hits) {
+    if (bm->refcount[b] == 0) {
+      auto at = bm->evictable_at.find(b);
+      bm->evictable.erase(at->second);
+      bm->evictable_at.erase(at);
+    }
+    bm->refcount[b] += 1;
+    s.table.push_back(b);
+  }
+  for (int64_t i = static_cast<int64_t>(hits.size()); i < nb; ++i) {
+    const int32_t b = bm->take();
+    s.table.push_back(b);
+    if (i < full) {
+      key.parent = parent;
+      std::memcpy(key.tokens.data(), tokens + i * BS, sizeof(int32_t) * BS);
+      auto f = bm->cache.find(key);
+      if (f != bm->cache.end()) {
+        parent = f->second.cid;  // already cached under another block: this one stays private
+      } else {
+        const uint64_t cid = bm->next_cid++;
+        bm->cache.emplace(key, pa_bm::CacheEntry{cid, b});
+        bm->block_key.emplace(b, key);
+        parent = cid;
+      }
+    }
+  }
+  if (slots_out)
+    for (int32_t t = 0; t < num_tokens; ++t) slots_out[t] = bm->slot(s, t);
+  *cached_tokens_out = static_cast<int32_t>(hits.size()) * BS;
+  bm->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+pa_status pa_bm_cache_stats(const pa_bm* bm, int64_t* out) {
+  if (!bm || !out) return pa::fail(PA_ERR_INVALID, "pa_bm_cache_stats: bad arguments");
+  out[0] = static_cast<int64_t>(bm->block_key.size());
+  out[1] = static_cast<int64_t>(bm->evictable.size());
+  out[2] = bm->hit_blocks;
+  out[3] = bm->query_blocks;
+  return PA_OK;
+}
+
+pa_status pa_bm_cache_clear(pa_bm* bm) {
+  if (!bm) return pa::fail(PA_ERR_INVALID, "pa_bm_cache_clear: null manager");
+  for (int32_t b : bm->evictable) bm->free_stack.push_back(b);
+  bm->evictable.clear();
+  bm->evictable_at.clear();
+  bm->cache.clear();
+  bm->block_key.clear();
   return PA_OK;
 }
 
@@ -267,7 +414,7 @@ pa_status pa_bm_export(const pa_bm* bm, const int64_t* seqs, int32_t n, int32_t 
   return PA_OK;
 }
 
-int32_t pa_bm_num_free(const pa_bm* bm) { return bm ? static_cast<int32_t>(bm->free_stack.size()) : -1; }
+int32_t pa_bm_num_free(const pa_bm* bm) { return bm ? static_cast<int32_t>(bm->available()) : -1; }
 
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block) {
   if (!bm || block < 0 || block >= bm->num_blocks) return -1;
@@ -298,7 +445,7 @@ pa_status pa_bm_stats(const pa_bm* bm, int64_t* out) {
   }
   for (const auto& kv : bm->seqs)
     waste += static_cast<int64_t>(kv.second.table.size()) * bm->block_size - kv.second.len;
-  out[0] = static_cast<int64_t>(bm->free_stack.size());
+  out[0] = bm->available();
   out[1] = used;
   out[2] = shared;
   out[3] = bm->cow_count;

@@ -205,7 +205,18 @@ def bm_invariants(bm):
     assert refs == [bm.refcount(b) for b in range(N)]
     for b in free:
         assert refs[b] == 0
-    assert len(free) + sum(1 for r in refs if r > 0) == N
+    evictable = list(getattr(bm, "evictable", []))
+    assert len(free) + len(evictable) + sum(1 for r in refs if r > 0) == N
+    # cached blocks: the key map and the block map agree; an evictable block is
+    # cached and unreferenced; a block on the free stack is not cached
+    block_key = getattr(bm, "block_key", {})
+    for b, key in block_key.items():
+        assert bm.cache[key][1] == b
+    assert len(block_key) == len(getattr(bm, "cache", {}))
+    for b in evictable:
+        assert refs[b] == 0 and b in block_key
+    for b in free:
+        assert b not in block_key
     # a swapped-out sequence holds no block and is not live
     assert not set(getattr(bm, "swapped", {})) & set(bm.tables)
 
@@ -319,3 +330,65 @@ def check_bm_swap(BM, OutOfBlocks, InvalidOp):
     bm.add_seq(5, 0)
     assert bm.swap_out(5) == [] and bm.swapped == {5: 0}
     assert bm.swap_in(5) == [] and bm.lens[5] == 0
+
+
+def check_bm_prefix_cache(BM, OutOfBlocks, InvalidOp):
+    """Prefix caching, hand-traced on an 8-block pool of 4-token blocks
+    (identity order: the free stack hands out 0, 1, 2, ... first)."""
+    bm = BM(8, 4)
+    A = list(range(1, 11))                                    # tokens 1..10: two full blocks + 2
+    slots, hit = bm.add_seq_cached(1, A)
+    assert (slots, hit) == (list(range(10)), 0)               # blocks 0, 1, 2; blocks 0 and 1 cached
+    slots, hit = bm.add_seq_cached(2, A[:8] + [20, 21, 22])   # same first 8 tokens
+    assert hit == 8 and bm.tables[2] == [0, 1, 3] and slots[8:] == [12, 13, 14]
+    assert [bm.refcount(b) for b in (0, 1, 2, 3)] == [2, 2, 1, 1]
+    slots, hit = bm.add_seq_cached(3, A[:4])                  # one full block, holds the last token
+    assert hit == 0 and bm.tables[3] == [4]                   # never reused; its key is taken already
+    assert tuple(bm.cache_stats()) == (2, 0, 2, 4)
+    try:
+        bm.add_seq_cached(3, A)
+        raise AssertionError("a live id must be rejected")
+    except InvalidOp:
+        pass
+
+    bm.free_seq(1)                                            # block 2 -> free stack
+    bm.free_seq(2)                                            # 3 -> free stack; 1, 0 evictable
+    assert bm.num_free() == 7 and tuple(bm.cache_stats())[:2] == (2, 2)
+    slots, hit = bm.add_seq_cached(4, A[:9])                  # revives 0 and 1 from the evictable list
+    assert hit == 8 and bm.tables[4] == [0, 1, 3]
+    bm.free_seq(4)                                            # 1, 0 evictable again (1 oldest)
+    bm.add_seq(5, 24)                                         # 5 free + evicts block 1 (drops its key)
+    assert bm.tables[5] == [3, 2, 5, 6, 7, 1]
+    assert tuple(bm.cache_stats())[:2] == (1, 1)
+
+    snap = ([bm.refcount(b) for b in range(8)], bm.num_free(), tuple(bm.cache_stats()))
+    try:
+        bm.add_seq_cached(6, A[:9])                           # would revive 0 and need two more
+        raise AssertionError("expected OutOfBlocks")
+    except OutOfBlocks:
+        pass
+    try:
+        bm.add_seq_cached(6, A[:5])                           # the only evictable block is its own hit
+        raise AssertionError("expected OutOfBlocks")
+    except OutOfBlocks:
+        pass
+    assert snap == ([bm.refcount(b) for b in range(8)], bm.num_free(), tuple(bm.cache_stats()))
+    bm.free_seq(5)                                            # stack bottom..top: 3 2 5 6 7 1
+    slots, hit = bm.add_seq_cached(6, A[:9])
+    assert hit == 4 and bm.tables[6] == [0, 1, 7]             # block 1 cached again under a new id
+    slots, hit = bm.add_seq_cached(8, A[:8])                  # two full blocks: only the first is looked up
+    assert hit == 4 and bm.tables[8] == [0, 6]
+    assert tuple(bm.cache_stats()) == (2, 0, 2 + 2 + 1 + 1, 4 + 2 + 2 + 1)
+    # a block's tokens alone do not make a hit: tokens 5..8 are cached only
+    # after tokens 1..4
+    _, hit = bm.add_seq_cached(10, A[4:8] + [0])
+    assert hit == 0 and bm.tables[10] == [5, 2]
+    assert tuple(bm.cache_stats()) == (3, 0, 6, 10)
+
+    for seq in (6, 8, 3, 10):
+        bm.free_seq(seq)
+    assert tuple(bm.cache_stats())[:2] == (3, 3) and bm.num_free() == 8
+    bm.cache_clear()
+    assert tuple(bm.cache_stats())[:2] == (0, 0) and bm.num_free() == 8
+    _, hit = bm.add_seq_cached(9, A)
+    assert hit == 0

@@ -85,6 +85,17 @@ class CppBM:
     def swapped(self):
         return {s: self.m.swapped_len(s) for s in self._swapped}
 
+    def add_seq_cached(self, seq, tokens):
+        slots, hit = self._wrap(self.m.add_seq_cached, seq, tokens)
+        self._seqs.add(seq)
+        return [int(x) for x in slots], hit
+
+    def cache_stats(self):
+        return self.m.cache_stats()
+
+    def cache_clear(self):
+        self.m.cache_clear()
+
     def export(self, seqs, stride):
         return self._wrap(self.m.export, list(seqs), stride)
 
@@ -127,6 +138,62 @@ def test_cpp_block_manager_swap():
     P.check_bm_swap(CppBM, OutOfBlocks, InvalidOp)
 
 
+def test_cpp_block_manager_prefix_cache():
+    P.check_bm_prefix_cache(CppBM, OutOfBlocks, InvalidOp)
+
+
+def _prompt(kind, n, bs):
+    """Prompts from a few shared prefixes so that lookups hit, miss and
+    diverge part-way (token ids 0..3 only)."""
+    base = [(7 * i + kind) % 4 for i in range(64)]
+    fork = n % 5
+    return base[: max(0, n - fork)] + [(kind + j) % 4 for j in range(fork)]
+
+
+@settings(max_examples=120, deadline=None)
+@given(st.lists(st.tuples(st.integers(0, 8), st.integers(0, 9), st.integers(0, 40)), max_size=60),
+       st.sampled_from([1, 2, 4, 8]), st.integers(0, 2**31 - 1))
+def test_cpp_matches_model_with_prefix_cache(ops, bs, seed):
+    """Every operation, cached adds and evictions included, leaves the C++
+    manager and the model in the same state with the same results."""
+    order = list(np.random.default_rng(seed).permutation(16))
+    cpp, model = CppBM(16, bs, order), BlockManagerModel(16, bs, order)
+    for kind, seq, n in ops:
+        results = []
+        for bm in (cpp, model):
+            try:
+                if kind in (0, 7, 8):
+                    r = bm.add_seq_cached(seq, _prompt(kind % 2, n % 30, bs))
+                elif kind == 1:
+                    r = bm.append([s for s in sorted(model.tables) if (s + n) % 3 == 0])
+                elif kind == 2:
+                    r = bm.fork(seq, (seq + n) % 10)
+                elif kind == 3:
+                    r = bm.free_seq(seq)
+                elif kind == 4:
+                    r = bm.add_seq(seq, n % 20)
+                elif kind == 5:
+                    r = bm.swap_out(seq)
+                else:
+                    r = bm.swap_in(seq) if n % 7 else bm.cache_clear()
+                results.append(("ok", r))
+            except OutOfBlocks:
+                results.append(("oom", None))
+            except InvalidOp:
+                results.append(("invalid", None))
+        assert results[0][0] == results[1][0], (kind, results)
+        if results[0][0] == "ok" and results[0][1] is not None:
+            a, b = results[0][1], results[1][1]
+            if kind == 1:
+                assert list(a[0]) == list(b[0]) and [tuple(x) for x in a[1]] == [tuple(x) for x in b[1]]
+            elif kind in (0, 7, 8):
+                assert list(a[0]) == list(b[0]) and a[1] == b[1]
+            else:
+                assert list(a) == list(b)
+        _same_state(cpp, model)
+        P.bm_invariants(model)
+
+
 def test_cpp_create_rejects_bad_order():
     with pytest.raises(pa.PAError):
         pa.BlockManager(4, 16, [0, 1, 1, 2])
@@ -140,6 +207,8 @@ def _same_state(cpp: CppBM, model: BlockManagerModel):
     assert cpp.tables == {s: t for s, t in model.tables.items()}
     assert cpp.lens == model.lens
     assert cpp.swapped == model.swapped
+    assert tuple(cpp.cache_stats()) == tuple(model.cache_stats())
+    assert cpp.num_free() == model.num_free()
     assert tuple(cpp.stats()) == tuple(model.stats())
 
 

@@ -73,6 +73,48 @@ def test_bm_swap_pins():
     P.check_bm_swap(BlockManagerModel, OutOfBlocks, InvalidOp)
 
 
+def test_bm_prefix_cache_pins():
+    P.check_bm_prefix_cache(BlockManagerModel, OutOfBlocks, InvalidOp)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.tuples(st.integers(0, 5), st.integers(0, 7), st.integers(0, 40)), max_size=60),
+       st.sampled_from([1, 2, 4]))
+def test_prefix_cache_reuses_only_identical_prefixes(ops, bs):
+    """Brute force over the whole history: a reused block was first filled
+    by a sequence whose tokens up to that block's end equal the new prompt's
+    (the K/V a block holds is a function of that prefix), and the reuse stops
+    before the block of the last token."""
+    bm = BlockManagerModel(20, bs, list(reversed(range(20))))
+    filled = {}                  # block -> prefix of tokens it was filled under (None: uncached content)
+    prompts = [[(3 * i) % 5 for i in range(40)], [(3 * i) % 5 for i in range(6)] + [4] * 34]
+    for kind, seq, n in ops:
+        try:
+            if kind <= 2:
+                toks = prompts[kind % 2][: n % 30]
+                slots, hit = bm.add_seq_cached(seq, toks)
+                assert hit % bs == 0 and (hit < len(toks) or len(toks) == 0)
+                table = bm.table(seq)
+                for i, b in enumerate(table):
+                    pre = tuple(toks[: (i + 1) * bs])
+                    if i < hit // bs:
+                        assert filled[b] == pre
+                    else:
+                        filled[b] = pre if (i + 1) * bs <= len(toks) else None
+            elif kind == 3:
+                bm.free_seq(seq)
+            elif kind == 4:
+                bm.add_seq(seq, n % 20)
+                for b in bm.table(seq):
+                    filled[b] = None
+            else:
+                bm.append([seq])
+                filled[bm.table(seq)[-1]] = None
+        except (OutOfBlocks, InvalidOp):
+            pass
+        P.bm_invariants(bm)
+
+
 def test_swap_round_trip_restores_the_sequence():
     """Swap a sequence out (blocks copied to host arrays), let another
     sequence take and overwrite its blocks, swap it back into fresh blocks:

@@ -78,11 +78,11 @@ BM_MUTANTS = [
     ("FIFO free list", "self.free: List[int] = list(reversed(order))", "self.free: List[int] = list(order)"),
     ("copy even when unshared", "elif self.rc[t[-1]] > 1:", "elif self.rc[t[-1]] > 0:"),
     ("never copy-on-write", "elif self.rc[t[-1]] > 1:", "elif False:"),
-    ("free in reverse order", "for b in self.tables.pop(seq):", "for b in reversed(self.tables.pop(seq)):"),
+    ("free in reverse order", "        for b in table:\n            self.rc[b] -= 1", "        for b in reversed(table):\n            self.rc[b] -= 1"),
     ("slot off by one", "return t[pos // self.BS] * self.BS + pos % self.BS", "return t[pos // self.BS] * self.BS + (pos + 1) % self.BS"),
     ("block on full, not on first write", "            if pos % self.BS == 0:\n                t.append", "            if pos % self.BS == 1:\n                t.append"),
     ("fork forgets refcount", "        for b in self.tables[child]:\n            self.rc[b] += 1", "        pass"),
-    ("no all-or-nothing", "        if need > len(self.free):\n            raise OutOfBlocks()\n        self.tables[seq]", "        self.tables[seq]"),
+    ("no all-or-nothing", "        if need > self.num_free():\n            raise OutOfBlocks()\n        self.tables[seq]", "        self.tables[seq]"),
 ]
 
 
@@ -109,6 +109,24 @@ SWAP_MUTANTS = [
 def test_swap_mutant_is_caught(name, old, new):
     m = _mutant("block_manager", old, new)
     assert _fails([lambda: P.check_bm_swap(m.BlockManagerModel, m.OutOfBlocks, m.InvalidOp)]), name
+
+
+PREFIX_MUTANTS = [
+    ("key without parent", "key = (parent, tuple(tokens[i * BS:(i + 1) * BS]))", "key = (0, tuple(tokens[i * BS:(i + 1) * BS]))"),
+    ("reuses the last token's block", "lookable = (n - 1) // BS if n else 0", "lookable = n // BS"),
+    ("evicts the newest first", "b = self.evictable.pop(0)", "b = self.evictable.pop()"),
+    ("prefix start evicted first", "self.evictable.extend(reversed(cached))", "self.evictable.extend(cached)"),
+    ("evicted key kept", "del self.cache[self.block_key.pop(b)]", "self.block_key.pop(b)"),
+    ("revived hits counted as free", "if nb - len(hits) > self.num_free() - revived:", "if nb - len(hits) > self.num_free():"),
+    ("hits not counted", "        self.hit_blocks += len(hits)\n", ""),
+    ("cached blocks freed", "                if b in self.block_key:", "                if False:"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PREFIX_MUTANTS, ids=[m[0] for m in PREFIX_MUTANTS])
+def test_prefix_cache_mutant_is_caught(name, old, new):
+    m = _mutant("block_manager", old, new)
+    assert _fails([lambda: P.check_bm_prefix_cache(m.BlockManagerModel, m.OutOfBlocks, m.InvalidOp)]), name
 
 
 CACHE_MUTANTS = [
@@ -141,6 +159,7 @@ def test_unmutated_copy_passes_every_pin(module):
     elif module == "block_manager":
         P.check_bm_golden(m.BlockManagerModel, m.OutOfBlocks)
         P.check_bm_swap(m.BlockManagerModel, m.OutOfBlocks, m.InvalidOp)
+        P.check_bm_prefix_cache(m.BlockManagerModel, m.OutOfBlocks, m.InvalidOp)
     else:
         P.check_layout_golden(m.PagedCacheModel)
         P.check_copy_blocks(m.PagedCacheModel)
