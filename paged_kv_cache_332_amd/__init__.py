@@ -441,10 +441,11 @@ class BlockManager:
         return int(lib.pa_bm_num_seqs(self._h))
 
     def free_list(self) -> np.ndarray:
-        n = int(lib.pa_bm_num_free(self._h))
-        out = np.empty(n, dtype=np.int32)
-        lib.pa_bm_free_list(self._h, out.ctypes.data_as(_pi32), n)
-        return out
+        """The free stack, next allocation first (evictable cached blocks not included)."""
+        n = int(lib.pa_bm_num_free(self._h))      # an upper bound: it counts evictable blocks too
+        out = np.empty(max(n, 1), dtype=np.int32)
+        k = int(lib.pa_bm_free_list(self._h, out.ctypes.data_as(_pi32), n))
+        return out[:k].copy()
 
     def stats(self) -> Tuple[int, int, int, int, int]:
         out = np.zeros(5, dtype=np.int64)
