@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
   // sums live in separate static arrays, so the compiler can tell that their
   // reads never alias the ring's direct loads and adds no waits for them.
   __shared__ int2 s_tbl[4][kStreamTcap];
-  __shared__ int32_t s_ctx[kStreamMaxSeqs];
+  __shared__ int32_t s_ctx[kStreamMaxSeqs + 1];     // entry B is scratch
   __shared__ int32_t s_pre[kStreamMaxSeqs + 1];
   using bits = typename T::bits;
   using MF = MfmaOps<T>;
@@ -114,13 +114,86 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
   int32_t* ctxs = s_ctx;
   int32_t* pre = s_pre;                              // [B + 1] exclusive prefix of tiles
 
+  const bits* kpool = static_cast<const bits*>(a.k);
+  const bits* vpool = static_cast<const bits*>(a.v);
+  const bits* qbase = static_cast<const bits*>(a.q);
+
+  // issue the loads of one tile into slot s (ids = its block ids; with
+  // qload the item's query rows too: the tile starts the item or the wave)
+  auto issue = [&](const Cursor& cu, int s, int2 ids, bool qload) {
+    uint8_t* sl = slots + s * SB;
+    if (qload) {
+      // query rows of the item; lanes past G * D read row 0 again
+      const int64_t qrow = (int64_t(cu.seq) * Hq + int64_t(cu.kvh) * G) * D;
+#pragma unroll
+      for (int i = 0; i < QI; ++i) {
+        const int u = i * 64 + lane;
+        const int uu = u < G * D / 8 ? u : 0;
+        dma16(qbase + qrow + int64_t(uu) * 8, sl + 2 * KI * 1024 + i * 1024);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int u = i * 64 + lane;
+      const int j = u >> 4, t = u & 15;
+      int blk, tok;
+      if constexpr (BS == 16) {
+        blk = ids.x;
+        tok = t;
+      } else if constexpr (BS == 32) {
+        blk = ids.x;
+        tok = 16 * (cu.t & 1) + t;
+      } else {
+        blk = t < 8 ? ids.x : ids.y;
+        tok = t & 7;
+      }
+      const int64_t e = ((int64_t(blk) * Hkv + cu.kvh) * (D / 8) + j) * (BS * 8) + tok * 8;
+      dma16(kpool + e, sl + i * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int u = i * 64 + lane;
+      const int d = u >> 1, h = u & 1;
+      int blk, tok0;
+      if constexpr (BS == 16) {
+        blk = ids.x;
+        tok0 = 8 * h;
+      } else if constexpr (BS == 32) {
+        blk = ids.x;
+        tok0 = 16 * (cu.t & 1) + 8 * h;
+      } else {
+        blk = h ? ids.y : ids.x;
+        tok0 = 0;
+      }
+      const int64_t e = ((int64_t(blk) * Hkv + cu.kvh) * D + d) * BS + tok0;
+      dma16(vpool + e, sl + KI * 1024 + i * 1024);
+    }
+  };
+
+
+  // This wave's share of a host plan, read with no branch around it (a
+  // harmless read of the workspace without a plan) so that its latency
+  // overlaps the loads of the lengths and prefix sums below: the start-up
+  // is one round trip for all of them, not one per load.
+  const int64_t w = int64_t(blockIdx.x) * 4 + wave;
+  const int32_t* plan_src = sa.wave_start ? sa.wave_start + w : reinterpret_cast<const int32_t*>(sa.rec_ml);
+  const int32_t plan_a = plan_src[0];
+  const int32_t plan_b = plan_src[1];
+
   // ---- tiles per sequence and their prefix sums (whole workgroup) --------
   if (sa.pre_in) {
     for (int i = threadIdx.x; i <= B; i += 256) {
-      pre[i] = sa.pre_in[i];
-      if (i < B) ctxs[i] = min(max(a.ctx[i], 0), a.max_ctx);
+      // both loads issue before either is used (entry B of ctxs takes a
+      // copy of length 0 and is never read; B >= 1)
+      const int32_t pv = sa.pre_in[i];
+      const int32_t cv = a.ctx[i < B ? i : 0];
+      pre[i] = pv;
+      ctxs[i] = min(max(cv, 0), a.max_ctx);
     }
-    __syncthreads();
+    // the writes are done once lgkmcnt drains; a bare barrier does not wait
+    // for other loads in flight
+    lgkm_wait0();
+    wg_barrier();
   } else {
     int32_t* part = reinterpret_cast<int32_t*>(&s_tbl[0][0]);  // 512 ints of scratch
     const int per = (B + 255) / 256;
@@ -164,9 +237,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
     }
   }
 
-  const int64_t w = int64_t(blockIdx.x) * 4 + wave;
-  const int64_t ga = sa.wave_start ? int64_t(sa.wave_start[w]) : stream_wave_start(ntot, w, gridDim.x);
-  const int64_t gb = sa.wave_start ? int64_t(sa.wave_start[w + 1]) : stream_wave_start(ntot, w + 1, gridDim.x);
+  const int64_t ga = sa.wave_start ? int64_t(plan_a) : stream_wave_start(ntot, w, gridDim.x);
+  const int64_t gb = sa.wave_start ? int64_t(plan_b) : stream_wave_start(ntot, w + 1, gridDim.x);
   if (ga >= gb) {  // no workgroup barrier below this point
     if (sa.wave_time && lane == 0) {
       const int32_t t0 = static_cast<int32_t>(t_begin);
@@ -214,61 +286,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
     cu.t = uniform(cu.t);
     cu.nt = uniform(cu.nt);
     cu.ctx = uniform(cu.ctx);
-  };
-
-  const bits* kpool = static_cast<const bits*>(a.k);
-  const bits* vpool = static_cast<const bits*>(a.v);
-  const bits* qbase = static_cast<const bits*>(a.q);
-
-  // issue the loads of one tile into slot s (ids = its block ids)
-  auto issue = [&](const Cursor& cu, int s, int2 ids) {
-    uint8_t* sl = slots + s * SB;
-    if (cu.t == 0 || cu.g == ga) {
-      // query rows of the item; lanes past G * D read row 0 again
-      const int64_t qrow = (int64_t(cu.seq) * Hq + int64_t(cu.kvh) * G) * D;
-#pragma unroll
-      for (int i = 0; i < QI; ++i) {
-        const int u = i * 64 + lane;
-        const int uu = u < G * D / 8 ? u : 0;
-        dma16(qbase + qrow + int64_t(uu) * 8, sl + 2 * KI * 1024 + i * 1024);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int u = i * 64 + lane;
-      const int j = u >> 4, t = u & 15;
-      int blk, tok;
-      if constexpr (BS == 16) {
-        blk = ids.x;
-        tok = t;
-      } else if constexpr (BS == 32) {
-        blk = ids.x;
-        tok = 16 * (cu.t & 1) + t;
-      } else {
-        blk = t < 8 ? ids.x : ids.y;
-        tok = t & 7;
-      }
-      const int64_t e = ((int64_t(blk) * Hkv + cu.kvh) * (D / 8) + j) * (BS * 8) + tok * 8;
-      dma16(kpool + e, sl + i * 1024);
-    }
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int u = i * 64 + lane;
-      const int d = u >> 1, h = u & 1;
-      int blk, tok0;
-      if constexpr (BS == 16) {
-        blk = ids.x;
-        tok0 = 8 * h;
-      } else if constexpr (BS == 32) {
-        blk = ids.x;
-        tok0 = 16 * (cu.t & 1) + 8 * h;
-      } else {
-        blk = h ? ids.y : ids.x;
-        tok0 = 0;
-      }
-      const int64_t e = ((int64_t(blk) * Hkv + cu.kvh) * D + d) * BS + tok0;
-      dma16(vpool + e, sl + KI * 1024 + i * 1024);
-    }
   };
 
   // ---- per-item state -----------------------------------------------------
@@ -397,19 +414,40 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
     const int n = int(min(int64_t(tcap), gb - pa0));
     // block ids of each tile of the pass (BS 8: two blocks per tile; the
     // second is the first again when it holds no context token)
-    for (int i = lane; i < n; i += 64) {
-      const Cursor cu = locate(pa0 + i);
-      const int32_t* row = tables + int64_t(cu.seq) * a.table_stride;
-      int2 ids;
-      if constexpr (BS == 16) {
-        ids.x = ids.y = row[cu.t];
-      } else if constexpr (BS == 32) {
-        ids.x = ids.y = row[cu.t >> 1];
-      } else {
-        ids.x = row[2 * cu.t];
-        ids.y = 16 * cu.t + 8 < cu.ctx ? row[2 * cu.t + 1] : ids.x;
+    // all table reads of the pass are issued before the first is used (one
+    // round trip, not one per 64 tiles)
+    // (the values are only combined at the LDS writes, so no load waits for
+    // another)
+    constexpr int kIdIters = (tcap + 63) / 64;
+    int32_t idx[kIdIters], idy[kIdIters];
+    bool two[kIdIters];
+#pragma unroll
+    for (int j = 0; j < kIdIters; ++j) {
+      const int i = lane + 64 * j;
+      two[j] = false;
+      if (i < n) {
+        const Cursor cu = locate(pa0 + i);
+        const int32_t* row = tables + int64_t(cu.seq) * a.table_stride;
+        if constexpr (BS == 16) {
+          idx[j] = row[cu.t];
+        } else if constexpr (BS == 32) {
+          idx[j] = row[cu.t >> 1];
+        } else {
+          // the second block of the tile only when it holds a context token
+          // (else an in-range entry is read and not used)
+          two[j] = 16 * cu.t + 8 < cu.ctx;
+          idx[j] = row[2 * cu.t];
+          idy[j] = row[two[j] ? 2 * cu.t + 1 : 2 * cu.t];
+        }
       }
-      tbl[i] = ids;
+    }
+#pragma unroll
+    for (int j = 0; j < kIdIters; ++j) {
+      const int i = lane + 64 * j;
+      if (i < n) {
+        if constexpr (BS == 8) tbl[i] = int2{idx[j], two[j] ? idy[j] : idx[j]};
+        else tbl[i] = int2{idx[j], idx[j]};
+      }
     }
     lgkm_wait0();
     __builtin_amdgcn_wave_barrier();
@@ -421,7 +459,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
     for (int i = 0; i < NSLOT - 1; ++i) {
       if (i < n) {
         const int2 ids = tbl[i];
-        issue(ic, i, int2{uniform(ids.x), uniform(ids.y)});
+        issue(ic, i, int2{uniform(ids.x), uniform(ids.y)}, ic.t == 0 || ic.g == ga);
         advance(ic);
       }
     }
@@ -431,7 +469,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
         // the slot of tile k - 1: its LDS reads finished before its math ran
         lgkm_wait0();
         const int2 ids = tbl[kn];
-        issue(ic, kn % NSLOT, int2{uniform(ids.x), uniform(ids.y)});
+        issue(ic, kn % NSLOT, int2{uniform(ids.x), uniform(ids.y)}, ic.t == 0 || ic.g == ga);
         advance(ic);
         vm_wait<DPT*(NSLOT - 1)>();
       } else {

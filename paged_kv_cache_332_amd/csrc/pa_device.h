@@ -203,6 +203,12 @@ __device__ __forceinline__ void vm_wait() {
 
 __device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier without the memory fence of __syncthreads, which would
+// wait for every outstanding load of the wave (prefetches into LDS included);
+// each wave waits for its own accesses with an explicit count first.  The
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 }  // namespace pa

@@ -30,12 +30,6 @@ namespace pa {
 
 namespace {
 
-// Workgroup barrier without the memory fence of __syncthreads, which would
-// wait for every outstanding load of the wave (the ring's prefetches
-// included); each wave waits for its own loads with an explicit count first.
-// The clobber keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
 // LDS reads of the ring and the block ids.  As volatile LDS accesses the
 // compiler keeps them where they are (after the explicit waits and the
 // barrier) and does not add a wait for every direct load still in flight.
