@@ -188,7 +188,13 @@ def prefill_bench(args, w, cfg, pa, runner, torch):
     keys = sum(int(((c - L + 1) + c) * L // 2) for c, L in zip(ctx, chunk))
     flops = 4.0 * cfg.num_q_heads * cfg.head_dim * keys
     # K/V tiles each workgroup streams (16-token tiles up to its last token)
-    tpw = 4 * (16 // (cfg.num_q_heads // cfg.num_kv_heads))
+    # (the workgroup size the library picks: 2 column blocks per wave when the
+    # chunks keep at least 1024 such workgroups busy, else 1)
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    maxq = int(chunk.max())
+    tpw2 = 8 * (16 // G)
+    cb = 2 if maxq >= tpw2 and cfg.num_seqs * cfg.num_kv_heads * (-(-maxq // tpw2)) >= 1024 else 1
+    tpw = 4 * cb * (16 // G)
     tiles = 0
     for c, L in zip(ctx, chunk):
         p0 = c - L
@@ -202,6 +208,7 @@ def prefill_bench(args, w, cfg, pa, runner, torch):
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": args.config, "batch": cfg.num_seqs, "chunk": int(args.prefill),
                    "query_tokens": T, "ctx_mean": round(float(ctx.mean()), 1)},
+        "column_blocks_per_wave": cb,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4), "kv_bytes_streamed": int(kv_bytes),
                      "kv_GBps": round(kv_bytes / (us * 1e-6) / 1e9, 1)},

@@ -78,8 +78,18 @@ struct PrefillArgs {
   float scale_log2;              // scale * log2(e)
   int32_t out_f32;
 };
-// Query tokens one prefill workgroup takes (four waves of 16 / group columns).
-inline int32_t prefill_tokens_per_wg(int32_t group) { return 4 * (16 / group); }
+// Column blocks per prefill wave: 2 (32 columns, 2 x 16 / group tokens) when
+// the chunks are long enough to keep at least 1024 such workgroups, else 1.
+inline int32_t prefill_column_blocks(int32_t group, int32_t max_query_len, int32_t num_seqs, int32_t num_kv_heads) {
+  const int64_t tpw2 = 4 * 2 * (16 / group);
+  const int64_t wgs2 = int64_t(num_seqs) * num_kv_heads * ((max_query_len + tpw2 - 1) / tpw2);
+  return (max_query_len >= tpw2 && wgs2 >= 1024) ? 2 : 1;
+}
+// Query tokens one prefill workgroup takes (four waves of column blocks of
+// 16 / group tokens).
+inline int32_t prefill_tokens_per_wg(int32_t group, int32_t max_query_len, int32_t num_seqs, int32_t num_kv_heads) {
+  return 4 * prefill_column_blocks(group, max_query_len, num_seqs, num_kv_heads) * (16 / group);
+}
 hipError_t launch_prefill(const PrefillArgs& a, int32_t dtype, int32_t d, int32_t bs, int32_t group,
                           int32_t max_query_len, hipStream_t stream);
 

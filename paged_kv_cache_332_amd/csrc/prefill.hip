@@ -12,17 +12,21 @@
 // token exactly the decode result at that length.
 //
 // Work decomposition.  One workgroup per (sequence, kv head, block of
-// 64 / group query tokens); its four waves each own 16 matrix-core columns,
-// the (query token, query head) pairs of 16 / group tokens of the kv head's
-// group.  The workgroup streams the 16-token K/V tiles of the positions its
-// tokens can see through a 4-slot LDS ring filled by direct global->LDS
-// loads, each wave loading a quarter of every tile, so every K/V byte read
-// serves 64 columns.  Per tile and wave: S^T = K Q^T with
-// v_mfma_f32_16x16x32, a causal limit per column, the running-max softmax of
-// the decode kernel (reference maximum refreshed when it grows by more than
-// 2^8), P split into a 16-bit high part and the rounded remainder for two
-// v_mfma_f32_16x16x16 products into O^T.  No split of the context: a
-// workgroup covers its tokens' whole prefix, and many workgroups run at once.
+// 64 CB / group query tokens); its four waves each own CB blocks of 16
+// matrix-core columns, the (query token, query head) pairs of 16 / group
+// tokens of the kv head's group per block.  The workgroup streams the
+// 16-token K/V tiles of the positions its tokens can see through a 4-slot LDS
+// ring filled by direct global->LDS loads, each wave loading a quarter of
+// every tile, so every K/V byte read serves 64 CB columns (CB = 4 for long
+// chunks: the flops per byte streamed rise fourfold; CB = 1 keeps short
+// chunks spread over many workgroups).  Per tile, wave and column block:
+// S^T = K Q^T with v_mfma_f32_16x16x32 (the K operand read once for all
+// blocks), a causal limit per column, the running-max softmax of the decode
+// kernel (reference maximum refreshed when it grows by more than 2^8), P
+// split into a 16-bit high part and the rounded remainder for two
+// v_mfma_f32_16x16x16 products into O^T; a block none of whose columns sees
+// the tile skips it.  No split of the context: a workgroup covers its
+// tokens' whole prefix, and many workgroups run at once.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -38,13 +42,14 @@ __device__ __forceinline__ V ring_read(const uint8_t* p) {
   return *(const volatile __attribute__((address_space(3))) V*)(p);
 }
 
-template <class T, int D, int BS, int G>
+template <class T, int D, int BS, int G, int CB>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   using bits = typename T::bits;
   using MF = MfmaOps<T>;
   using v4 = typename MF::v4;
   using el = typename MF::e;
-  constexpr int TQ = 16 / G;           // query tokens per wave
+  constexpr int TB = 16 / G;           // query tokens per column block
+  constexpr int TQ = CB * TB;          // per wave
   constexpr int TQW = 4 * TQ;          // per workgroup
   constexpr int NS = D / 32;           // QK slices of 32 dims
   constexpr int NT = D / 16;           // PV row tiles of 16 dims
@@ -78,17 +83,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int kmax = p0 + min(L, tq0 + TQW);       // positions the workgroup's tokens see
   const int nt = (kmax + 15) / 16;
 
-  // this lane's column: token j of the wave, head gc of the group
+  // this lane's column in block cb: token cb TB + j of the wave, head gc of
+  // the group
   const int tw0 = tq0 + wave * TQ;
   const int j = c / G, gc = c % G;
-  const bool col_valid = tw0 + j < L;
-  const int tok = min(tw0 + j, L - 1);           // (a spare column repeats the last token)
-  const int lim = p0 + tok + 1;                  // causal limit of the column (exclusive)
-  const int64_t qrow = (int64_t(qs) + tok) * Hq + int64_t(h) * G + gc;
-  const bits* qp = static_cast<const bits*>(a.q) + qrow * D;
-  u32x4 qop[NS];
+  bool col_valid[CB];
+  int lim[CB];                                   // causal limit of the column (exclusive)
+  int64_t qrow[CB];
+  u32x4 qop[CB][NS];
 #pragma unroll
-  for (int m = 0; m < NS; ++m) qop[m] = *reinterpret_cast<const u32x4*>(qp + (4 * m + q) * 8);
+  for (int cb = 0; cb < CB; ++cb) {
+    col_valid[cb] = tw0 + cb * TB + j < L;
+    const int tok = min(tw0 + cb * TB + j, L - 1);  // (a spare column repeats the last token)
+    lim[cb] = p0 + tok + 1;
+    qrow[cb] = (int64_t(qs) + tok) * Hq + int64_t(h) * G + gc;
+    const bits* qp = static_cast<const bits*>(a.q) + qrow[cb] * D;
+#pragma unroll
+    for (int m = 0; m < NS; ++m) qop[cb][m] = *reinterpret_cast<const u32x4*>(qp + (4 * m + q) * 8);
+  }
+  // the last position any column of block cb sees (uniform over the wave)
+  int blk_last[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) blk_last[cb] = p0 + min(L, tw0 + (cb + 1) * TB) - 1;
   // the query loads complete here, in a wait the compiler knows about
   // (vmcnt 0; expcnt and lgkmcnt at their maxima): otherwise it waits for
   // every load in flight before each tile's first product
@@ -160,10 +176,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  f32x4 acc[NT];
+  f32x4 acc[CB][NT];
+  float m_ref[CB], l_lane[CB];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf, l_lane = 0.f;
+  for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[cb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref[cb] = kNegInf;
+    l_lane[cb] = 0.f;
+  }
 
   stage_ids(0);
   __syncthreads();
@@ -199,37 +220,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int m = 0; m < NS; ++m) kr[m] = ring_read<u32x4>(sl + ((4 * m + q) * 16 + c) * 16);
 #pragma unroll
     for (int n = 0; n < NT; ++n) vr[n] = ring_read<u32x2>(sl + KI * 1024 + (16 * n + c) * 32 + 8 * q);
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < NS; ++m) sc = MF::qk(kr[m], qop[m], sc);
     const int kp0 = 16 * t + 4 * q;
-    float sv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = kp0 + i < lim ? sc[i] * a.scale_log2 : kNegInf;
-    float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mt = xor16<OpMax>(mt);
-    mt = xor32<OpMax>(mt);
-    // (tile 0 holds position 0, which every column sees: m_ref is finite
-    // from then on and masked terms give exp2(-inf) = 0)
-    const bool need = mt > m_ref + 8.f;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? (m_ref == kNegInf ? 0.f : fast_exp2(m_ref - mt)) : 1.f;
-      m_ref = need ? mt : m_ref;
-      l_lane *= alpha;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_ref);
-    l_lane += (p[0] + p[1]) + (p[2] + p[3]);
-    v4 phi, plo;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const el hi = static_cast<el>(p[i]);
-      phi[i] = hi;
-      plo[i] = static_cast<el>(p[i] - static_cast<float>(hi));
-    }
     if (16 * t + 16 > kmax) {
       // positions past the workgroup's last token may hold anything (NaN
       // poison included): select zeros
@@ -244,26 +235,64 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
     }
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      acc[n] = MF::pv(vr[n], phi, acc[n]);
-      acc[n] = MF::pv(vr[n], plo, acc[n]);
+    for (int cb = 0; cb < CB; ++cb) {
+      // (tile 0 holds position 0, which every column sees, so no block
+      // skips it: m_ref is finite from then on and masked terms give
+      // exp2(-inf) = 0)
+      if (16 * t > blk_last[cb]) continue;
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < NS; ++m) sc = MF::qk(kr[m], qop[cb][m], sc);
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = kp0 + i < lim[cb] ? sc[i] * a.scale_log2 : kNegInf;
+      float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mt = xor16<OpMax>(mt);
+      mt = xor32<OpMax>(mt);
+      const bool need = mt > m_ref[cb] + 8.f;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? (m_ref[cb] == kNegInf ? 0.f : fast_exp2(m_ref[cb] - mt)) : 1.f;
+        m_ref[cb] = need ? mt : m_ref[cb];
+        l_lane[cb] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[cb][n] *= alpha;
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_ref[cb]);
+      l_lane[cb] += (p[0] + p[1]) + (p[2] + p[3]);
+      v4 phi, plo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const el hi = static_cast<el>(p[i]);
+        phi[i] = hi;
+        plo[i] = static_cast<el>(p[i] - static_cast<float>(hi));
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        acc[cb][n] = MF::pv(vr[n], phi, acc[cb][n]);
+        acc[cb][n] = MF::pv(vr[n], plo, acc[cb][n]);
+      }
     }
   }
 
-  float l = xor16<OpSum>(l_lane);
-  l = xor32<OpSum>(l);
-  if (col_valid) {
-    const float inv = 1.f / l;
-    const int64_t o = qrow * D + 4 * q;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const f32x4 v = acc[n] * inv;
-      if (a.out_f32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o + 16 * n) = v;
-      } else {
-        const uint32_t lo = T::from_f32(v[0]) | (T::from_f32(v[1]) << 16);
-        const uint32_t hi = T::from_f32(v[2]) | (T::from_f32(v[3]) << 16);
-        *reinterpret_cast<u32x2*>(static_cast<bits*>(a.out) + o + 16 * n) = u32x2{lo, hi};
+  for (int cb = 0; cb < CB; ++cb) {
+    float l = xor16<OpSum>(l_lane[cb]);
+    l = xor32<OpSum>(l);
+    if (col_valid[cb]) {
+      const float inv = 1.f / l;
+      const int64_t o = qrow[cb] * D + 4 * q;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const f32x4 v = acc[cb][n] * inv;
+        if (a.out_f32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o + 16 * n) = v;
+        } else {
+          const uint32_t lo = T::from_f32(v[0]) | (T::from_f32(v[1]) << 16);
+          const uint32_t hi = T::from_f32(v[2]) | (T::from_f32(v[3]) << 16);
+          *reinterpret_cast<u32x2*>(static_cast<bits*>(a.out) + o + 16 * n) = u32x2{lo, hi};
+        }
       }
     }
   }
@@ -271,10 +300,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
 template <class T, int D, int BS, int G>
 hipError_t launch_g(const PrefillArgs& a, int32_t max_query_len, hipStream_t stream) {
-  const int tpw = 4 * (16 / G);
+  const int cb = prefill_column_blocks(G, max_query_len, a.num_seqs, a.num_kv_heads);
+  const int tpw = 4 * cb * (16 / G);
   const size_t lds = 4 * 2 * (D / 32) * 1024;   // the tile ring: 4 slots of K and V
   dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads), block(256);
-  hipLaunchKernelGGL((prefill_kernel<T, D, BS, G>), grid, block, lds, stream, a);
+  if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2>), grid, block, lds, stream, a);
+  else hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1>), grid, block, lds, stream, a);
   return hipGetLastError();
 }
 

@@ -108,3 +108,63 @@ def test_prefill_rejects_bad_arguments():
         pa.pa_prefill(out, q, k, v, tab, qs, cl, 3, 100, 0.1)     # table stride too short for the bound
     with pytest.raises(pa.PAError):
         pa.pa_prefill(out, q, k.float(), v.float(), tab, qs, cl, 3, 3, 0.1)  # fp32 cache
+
+
+# dtype, head_dim, block size, q heads, kv heads, sequences, chunk, context range: batches large
+# enough for two column blocks per wave (the same sequence alone takes one)
+WIDE = {
+    "gqa4_bf16_bs16": ("bf16", 128, 16, 32, 8, 16, 512, (520, 1400)),
+    "mha_f16_bs8_d64": ("f16", 64, 8, 16, 16, 8, 1024, (1030, 1500)),
+    "gqa8_bf16_bs32": ("bf16", 128, 32, 64, 8, 8, 256, (300, 2000)),
+    "gqa16_bf16_d64": ("bf16", 64, 16, 16, 1, 8, 1024, (1024, 1300)),
+}
+
+
+@pytest.mark.parametrize("case", list(WIDE))
+def test_prefill_wide_workgroups_match_narrow(case):
+    """A batch large enough for two column blocks per wave gives, for every
+    sequence, the same bits as that sequence prefilled alone (one column
+    block per wave): both take the same tiles in the same order per column.
+    Sampled rows also match the oracle's decode at their positions."""
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    dtype, d, bs, hq, hkv, B, L, (lo, hi) = WIDE[case]
+    rng = np.random.default_rng([77, len(case)])
+    ctx = [int(x) for x in rng.integers(lo, hi, B)]
+    chunk = [L] * B
+    say("prefill wide vs narrow", case)
+    w = W.tiny(num_seqs=B, dtype=dtype, seed=78, ctx=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+               block_size=bs)
+    dev = runner.run_script(w, decode=False)
+    eng = dev.engine
+    tab, ctx_now = eng.bm.export(list(range(B)), eng.stride)
+    T = sum(chunk)
+    tdt = runner.TORCH_DTYPE[dtype]
+    q = W.round_to_dtype(rng.standard_normal((T, hq, d), dtype=np.float32), dtype)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    q_dev = torch.from_numpy(q).to("cuda").to(tdt)
+    scale = 1.0 / d ** 0.5
+    out = torch.full((T, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    pa.pa_prefill(out, q_dev, eng.k_cache, eng.v_cache, torch.from_numpy(np.ascontiguousarray(tab)).to("cuda"),
+                  torch.from_numpy(qs).to("cuda"), torch.from_numpy(np.asarray(ctx, np.int32)).to("cuda"),
+                  L, max(ctx), scale)
+    for i in range(B):
+        one = torch.full((chunk[i], hq, d), float("nan"), dtype=torch.float32, device="cuda")
+        pa.pa_prefill(one, q_dev[qs[i]: qs[i + 1]].contiguous(), eng.k_cache, eng.v_cache,
+                      torch.from_numpy(np.ascontiguousarray(tab[i: i + 1])).to("cuda"),
+                      torch.tensor([0, chunk[i]], dtype=torch.int32, device="cuda"),
+                      torch.tensor([ctx[i]], dtype=torch.int32, device="cuda"), chunk[i], ctx[i], scale)
+        torch.cuda.synchronize()
+        assert torch.equal(one.view(torch.int32), out[qs[i]: qs[i + 1]].view(torch.int32)), i
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = 0.0
+    for i in range(0, B, 3):
+        rows = w.row_of(i, np.arange(ctx[i]))
+        K, V = w.k_rows[rows], w.v_rows[rows]
+        for t in sorted({0, 1, 15, 16, 63, L // 2, L - 1}):
+            pos = ctx[i] - chunk[i] + t
+            ref = oracle.decode_attention(q[qs[i] + t], K[: pos + 1], V[: pos + 1], scale)
+            err = max(err, float(np.max(np.abs(got[qs[i] + t] - ref))))
+    say(case, "wide prefill sampled max abs error", err)
+    assert err <= 2e-3
