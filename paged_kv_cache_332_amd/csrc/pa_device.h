@@ -170,6 +170,10 @@ struct MfmaOps<BF16> {
   __device__ static f32x4 pv(u32x2 a, v4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4, a), b, c, 0, 0, 0);
   }
+  // the P.V product over 32 keys at the full rate of the 16x16x32 form
+  __device__ static f32x4 pv32(u32x4 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), b, c, 0, 0, 0);
+  }
 };
 
 template <>
@@ -183,6 +187,9 @@ struct MfmaOps<F16> {
   }
   __device__ static f32x4 pv(u32x2 a, v4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4, a), b, c, 0, 0, 0);
+  }
+  __device__ static f32x4 pv32(u32x4 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), b, c, 0, 0, 0);
   }
 };
 

@@ -15,18 +15,25 @@
 // 64 CB / group query tokens); its four waves each own CB blocks of 16
 // matrix-core columns, the (query token, query head) pairs of 16 / group
 // tokens of the kv head's group per block.  The workgroup streams the
-// 16-token K/V tiles of the positions its tokens can see through a 4-slot LDS
+// 16-token K/V tiles of the positions its tokens can see through a 6-slot LDS
 // ring filled by direct global->LDS loads, each wave loading a quarter of
-// every tile, so every K/V byte read serves 64 CB columns (CB = 4 for long
-// chunks: the flops per byte streamed rise fourfold; CB = 1 keeps short
-// chunks spread over many workgroups).  Per tile, wave and column block:
+// every tile, so every K/V byte read serves 64 CB columns (CB = 2 for long
+// chunks: twice the flops per byte streamed; CB = 1 keeps short chunks
+// spread over many workgroups).  Per tile, wave and column block:
 // S^T = K Q^T with v_mfma_f32_16x16x32 (the K operand read once for all
 // blocks), a causal limit per column, the running-max softmax of the decode
 // kernel (reference maximum refreshed when it grows by more than 2^8), P
-// split into a 16-bit high part and the rounded remainder for two
-// v_mfma_f32_16x16x16 products into O^T; a block none of whose columns sees
-// the tile skips it.  No split of the context: a workgroup covers its
-// tokens' whole prefix, and many workgroups run at once.
+// split into a 16-bit high part and the rounded remainder for two P V
+// products into O^T; a block none of whose columns sees the tiles skips
+// them.  No split of the context: a workgroup covers its tokens' whole
+// prefix, and many workgroups run at once.
+//
+// Tiles go in pairs: one softmax step covers 32 keys (one cross-lane
+// reduction and one rescale check per 32 keys), and P V is one
+// v_mfma_f32_16x16x32 per 16 value dims over both tiles (on gfx950 twice the
+// rate of the 16x16x16 form over one tile): key k = 8 q + i of the product
+// is key 4 q + i of the first tile for i < 4, of the second for i >= 4, in
+// both operands.  Registers are held to two waves per SIMD.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -42,11 +49,27 @@ __device__ __forceinline__ V ring_read(const uint8_t* p) {
   return *(const volatile __attribute__((address_space(3))) V*)(p);
 }
 
+// Wait until this wave's loads of the oldest tiles in flight have landed,
+// when k newer tiles (LPW loads each) may stay in flight (k uniform, at most
+// KMAX).
+template <int LPW, int KMAX>
+__device__ __forceinline__ void wait_oldest_tile(int k) {
+  if constexpr (KMAX > 0) {
+    if (k >= KMAX) {
+      vm_wait<KMAX * LPW>();
+      return;
+    }
+    wait_oldest_tile<LPW, KMAX - 1>(k);
+  } else {
+    vm_wait<0>();
+  }
+}
+
 template <class T, int D, int BS, int G, int CB>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
   using bits = typename T::bits;
   using MF = MfmaOps<T>;
-  using v4 = typename MF::v4;
+  using v8 = typename MF::v8;
   using el = typename MF::e;
   constexpr int TB = 16 / G;           // query tokens per column block
   constexpr int TQ = CB * TB;          // per wave
@@ -55,7 +78,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   constexpr int NT = D / 16;           // PV row tiles of 16 dims
   constexpr int KI = D / 32;           // 1 KiB loads per K (and per V) tile
   constexpr int LPW = 2 * KI / 4;      // loads per wave per tile
-  constexpr int NSL = 4;               // ring slots
+  constexpr int NSL = 6;               // ring slots: three pairs of tiles
   constexpr int IDCAP = 512;           // tiles whose block ids are staged at once
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   static_assert(LPW >= 1 && LPW * (NSL - 1) < 64, "loads per wave");
@@ -188,65 +211,93 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
   stage_ids(0);
   __syncthreads();
+  // tiles go in pairs (32 keys per softmax step): pair p computes from slots
+  // 2p, 2p + 1 (mod NSL) while pair p + 1 is in flight and pair p + 2 fills
+  // the slots of pair p - 1
 #pragma unroll
-  for (int i = 0; i < NSL - 1; ++i)
+  for (int i = 0; i < 4; ++i)
     if (i < nt) issue(i);
-  for (int t = 0; t < nt; ++t) {
-    // this wave's loads of tile t have landed once at most its loads of the
-    // newer tiles are outstanding; the barrier then covers every wave's share
-    // (and every wave is done with tile t - 1, whose slot is refilled next)
-    switch (min(nt - 1, t + NSL - 2) - t) {
-      case 0: vm_wait<0>(); break;
-      case 1: vm_wait<LPW>(); break;
-      default: vm_wait<2 * LPW>(); break;
-    }
+  for (int t = 0; t < nt; t += 2) {
+    // this wave's loads of tiles t and t + 1 have landed once at most its
+    // loads of the newer tiles are outstanding; the barrier then covers every
+    // wave's share (and every wave is done with the previous pair, whose
+    // slots are refilled next)
+    wait_oldest_tile<LPW, 2>(min(nt - 1, t + 3) - min(nt - 1, t + 1));
     wg_barrier();
-    const int tn = t + NSL - 1;
-    if (tn < nt) {
-      if (tn >= id_base + IDCAP) {
-        // next window of block ids (every slot's loads have landed: the
-        // compiler waits for the table reads before the LDS writes)
-        stage_ids(tn);
-        lgkm_wait0();
-        wg_barrier();
+#pragma unroll
+    for (int i = 4; i < 6; ++i) {
+      const int tn = t + i;
+      if (tn < nt) {
+        if (tn >= id_base + IDCAP) {
+          // next window of block ids (every slot's loads have landed: the
+          // compiler waits for the table reads before the LDS writes)
+          stage_ids(tn);
+          lgkm_wait0();
+          wg_barrier();
+        }
+        issue(tn);
       }
-      issue(tn);
     }
-    // ---- tile t: S^T = K Q^T, causal mask per column, online softmax, PV
-    const uint8_t* sl = ring + (t % NSL) * SLOT;
-    u32x4 kr[NS];
-    u32x2 vr[NT];
+    // ---- tiles t, t + 1: S^T = K Q^T per tile, causal mask per column,
+    // one online-softmax step over the 32 keys, P V over the 32 keys (a
+    // missing tile t + 1 reads a stale slot: every one of its scores is
+    // masked and its values are selected to zero)
+    const uint8_t* sa = ring + (t % NSL) * SLOT;
+    const uint8_t* sb = ring + ((t + 1) % NSL) * SLOT;
+    const int kp0 = 16 * t + 4 * q;              // keys kp0 .. + 3 (tile t), kp0 + 16 .. + 19 (tile t + 1)
+    f32x4 sc[CB][2];
 #pragma unroll
-    for (int m = 0; m < NS; ++m) kr[m] = ring_read<u32x4>(sl + ((4 * m + q) * 16 + c) * 16);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const uint8_t* sl = h2 ? sb : sa;
+      u32x4 kr[NS];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) vr[n] = ring_read<u32x2>(sl + KI * 1024 + (16 * n + c) * 32 + 8 * q);
-    const int kp0 = 16 * t + 4 * q;
-    if (16 * t + 16 > kmax) {
-      // positions past the workgroup's last token may hold anything (NaN
-      // poison included): select zeros
+      for (int m = 0; m < NS; ++m) kr[m] = ring_read<u32x4>(sl + ((4 * m + q) * 16 + c) * 16);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        sc[cb][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (16 * t > blk_last[cb]) continue;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) sc[cb][h2] = MF::qk(kr[m], qop[cb][m], sc[cb][h2]);
+      }
+    }
+    // V rows of both tiles, 8 keys per lane (k = 8 q + i: key kp0 + i of
+    // tile t for i < 4, of tile t + 1 for i >= 4), zeros past the
+    // workgroup's last position (which may hold anything, NaN poison
+    // included)
+    u32x4 vr[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const u32x2 va = ring_read<u32x2>(sa + KI * 1024 + (16 * n + c) * 32 + 8 * q);
+      const u32x2 vb = ring_read<u32x2>(sb + KI * 1024 + (16 * n + c) * 32 + 8 * q);
+      vr[n] = u32x4{va[0], va[1], vb[0], vb[1]};
+    }
+    if (16 * t + 32 > kmax) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        uint32_t w0 = vr[n][0], w1 = vr[n][1];
-        if (kp0 + 0 >= kmax) w0 &= 0xFFFF0000u;
-        if (kp0 + 1 >= kmax) w0 &= 0x0000FFFFu;
-        if (kp0 + 2 >= kmax) w1 &= 0xFFFF0000u;
-        if (kp0 + 3 >= kmax) w1 &= 0x0000FFFFu;
-        vr[n] = u32x2{w0, w1};
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const int k0 = kp0 + (w2 >> 1) * 16 + 2 * (w2 & 1);   // the two keys of 32-bit word w2
+          uint32_t x = vr[n][w2];
+          if (k0 >= kmax) x &= 0xFFFF0000u;
+          if (k0 + 1 >= kmax) x &= 0x0000FFFFu;
+          vr[n][w2] = x;
+        }
       }
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       // (tile 0 holds position 0, which every column sees, so no block
-      // skips it: m_ref is finite from then on and masked terms give
-      // exp2(-inf) = 0)
+      // skips the first pair: m_ref is finite from then on and masked terms
+      // give exp2(-inf) = 0)
       if (16 * t > blk_last[cb]) continue;
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      float sv[8];
 #pragma unroll
-      for (int m = 0; m < NS; ++m) sc = MF::qk(kr[m], qop[cb][m], sc);
-      float sv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = kp0 + i < lim[cb] ? sc[i] * a.scale_log2 : kNegInf;
-      float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = kp0 + i < lim[cb] ? sc[cb][0][i] * a.scale_log2 : kNegInf;
+        sv[4 + i] = kp0 + 16 + i < lim[cb] ? sc[cb][1][i] * a.scale_log2 : kNegInf;
+      }
+      float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
       mt = xor16<OpMax>(mt);
       mt = xor32<OpMax>(mt);
       const bool need = mt > m_ref[cb] + 8.f;
@@ -257,21 +308,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[cb][n] *= alpha;
       }
-      float p[4];
+      float p[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_ref[cb]);
-      l_lane[cb] += (p[0] + p[1]) + (p[2] + p[3]);
-      v4 phi, plo;
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sv[i] - m_ref[cb]);
+      l_lane[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      v8 phi, plo;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         const el hi = static_cast<el>(p[i]);
         phi[i] = hi;
         plo[i] = static_cast<el>(p[i] - static_cast<float>(hi));
       }
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        acc[cb][n] = MF::pv(vr[n], phi, acc[cb][n]);
-        acc[cb][n] = MF::pv(vr[n], plo, acc[cb][n]);
+        acc[cb][n] = MF::pv32(vr[n], phi, acc[cb][n]);
+        acc[cb][n] = MF::pv32(vr[n], plo, acc[cb][n]);
       }
     }
   }
@@ -302,7 +353,7 @@ template <class T, int D, int BS, int G>
 hipError_t launch_g(const PrefillArgs& a, int32_t max_query_len, hipStream_t stream) {
   const int cb = prefill_column_blocks(G, max_query_len, a.num_seqs, a.num_kv_heads);
   const int tpw = 4 * cb * (16 / G);
-  const size_t lds = 4 * 2 * (D / 32) * 1024;   // the tile ring: 4 slots of K and V
+  const size_t lds = 6 * 2 * (D / 32) * 1024;   // the tile ring: 6 slots of K and V
   dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads), block(256);
   if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2>), grid, block, lds, stream, a);
   else hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1>), grid, block, lds, stream, a);
