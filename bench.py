@@ -18,6 +18,7 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -433,6 +434,10 @@ def main():
     torch.cuda.synchronize()
     ctx_start = ctx0 + args.warmup
     host_s = []
+    # no garbage-collection pause inside the timed region (the loop allocates
+    # little; a collection there would stall the stream for milliseconds)
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     for i in range(args.steps):
         h0 = time.perf_counter()
@@ -440,6 +445,7 @@ def main():
         host_s.append(time.perf_counter() - h0)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     wts = eng.weights(cfg.num_seqs, cfg.num_q_heads)
     if wts is not None:
         print(f"[bench] workgroup weights by die: {wts[:8].tolist()}", file=sys.stderr, flush=True)
@@ -503,6 +509,7 @@ def main():
                    "kernel": args.kernel, "balance": eng.balance, "parallelism": "single GPU"},
         "tokens_per_s": round(cfg.num_seqs * args.steps / elapsed, 1),
         "host_us_per_step": round(float(np.median(host_s)) * 1e6, 1),
+        "host_us_per_step_max": round(float(np.max(host_s)) * 1e6, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "pa_decode pass (" + kname + ")",
                      "achieved": round(achieved, 2),
