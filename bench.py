@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # runs (scaled by a plain copy's counter readings); they describe the kernel
 # source they were taken with and are dropped once that source changes
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_c2_gqa_bf16_traffic.json")
+STREAM_HOST_MARKER = b"// ==== host side: launch configuration"
 STREAM_SRC = os.path.join(ROOT, "paged_kv_cache_332_amd", "csrc", "decode_stream.hip")
 METRIC = "paged decode KV read GB/s (% of HBM peak) + tokens/s, batch 64 GQA bf16"
 
@@ -98,6 +99,15 @@ def decode_bytes(ctx, cfg, esize, out_esize=4) -> int:
             + b * cfg.num_q_heads * cfg.head_dim * out_esize + tables + 4 * b)
 
 
+def stream_device_code_sha(hashlib) -> str:
+    """Hash of the stream kernel's device code: the source text before the
+    host-side marker (launch code below it does not change what a pass
+    reads or writes)."""
+    with open(STREAM_SRC, "rb") as f:
+        text = f.read()
+    return hashlib.sha256(text.split(STREAM_HOST_MARKER, 1)[0]).hexdigest()
+
+
 def measured_traffic(kernel_name: str, config: str):
     """HBM bytes per launch from the committed counter profile, or None when
     there is none for this kernel and workload or the kernel source has
@@ -109,9 +119,7 @@ def measured_traffic(kernel_name: str, config: str):
         rec = json.load(f)
     if rec.get("config") != config:
         return None
-    with open(STREAM_SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != stream_device_code_sha(hashlib):
         return None
     return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 

@@ -660,6 +660,8 @@ constexpr int stream_slot_bytes() {
 
 }  // namespace
 
+// ==== host side: launch configuration (no device code below this line) ====
+
 size_t stream_lds_bytes(int d, int gmax, int nslot) {
   const int qi = (gmax * d * 2 + 1023) / 1024;
   const size_t sb = size_t(2 * (d / 32) + qi) * 1024;
@@ -670,14 +672,9 @@ template <class T, int D, int BS, int GMAX, int NSLOT>
 static hipError_t launch_s(const StreamArgs& sa, size_t lds, int grid, int phases, hipStream_t stream) {
   auto kern = decode_stream_kernel<T, D, BS, GMAX, NSLOT>;
   // the dynamic size of an instantiation depends only on its template
-  // arguments; allow it once
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // arguments; allow it once per device
+  static std::atomic<uint64_t> allowed{0};
+  if (hipError_t e = allow_dynamic_lds(kern, lds, allowed)) return e;
   if (phases & 1) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, stream, sa);
     hipError_t e = hipGetLastError();

@@ -3,9 +3,25 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 namespace pa {
+
+// Lets `kern` take `lds` bytes of dynamic LDS (above the default limit) on the
+// current device; `done` (one per kernel instantiation) records the devices
+// already set, so the attribute call runs once per device and thread-safely.
+template <class K>
+inline hipError_t allow_dynamic_lds(K kern, size_t lds, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Arguments of the decode partition pass and the merge pass.
 struct DecodeArgs {
