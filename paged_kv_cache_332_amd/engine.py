@@ -29,32 +29,45 @@ _MAX_GRID = 1024     # the most workgroups the stream kernel launches
 XCDS = 8     # accelerator dies of the GPU; workgroup b of a launch runs on die b mod 8
 
 
-def rebalance(weights: np.ndarray, stamps: np.ndarray, rate: float = 0.5, groups: int = XCDS) -> np.ndarray:
-    """New stream-kernel workgroup weights from one completed step.
-
-    ``stamps`` holds, for the 4 waves of each workgroup in order, the start
-    and end of the wave (low 32 bits of a 100 MHz counter).  A workgroup's
-    finish time counts from the first start of any wave to the last end of
-    its own.  Workgroups are pooled in ``groups`` classes by index modulo
-    ``groups`` (the dies workgroups are dispatched to in turn, which run at
-    measurably different speeds; single workgroups only add noise).  Each
-    class's weight (its share of the tile list) moves towards what would have
-    let it finish with the others, w <- w * (mean / class mean) ** rate; the
-    result is scaled to a mean of 1024 and kept within 64..16384.  Results of
-    the decode do not depend on the weights, only the split of the work."""
-    g = weights.shape[0]
+def class_finish(stamps: np.ndarray, g: int, groups: int = XCDS) -> np.ndarray:
+    """Mean finish time of each class of workgroups (index modulo ``groups``)
+    in one completed step.  ``stamps`` holds, for the 4 waves of each of the
+    ``g`` workgroups in order, the start and end of the wave (low 32 bits of
+    a 100 MHz counter); a workgroup's finish counts from the first start of
+    any wave to the last end of its own."""
     t = np.asarray(stamps[: 8 * g], dtype=np.int64).reshape(g, 4, 2)
     rel = (t - t[0, 0, 0] + (1 << 31)) % (1 << 32) - (1 << 31)      # signed 32-bit differences
     finish = (rel[:, :, 1].max(axis=1) - rel[:, :, 0].min()).astype(np.float64)
     cls = np.arange(g) % groups
     cnt = np.bincount(cls, minlength=groups)
-    mean_c = np.bincount(cls, weights=finish, minlength=groups) / np.maximum(cnt, 1)
+    return np.bincount(cls, weights=finish, minlength=groups) / np.maximum(cnt, 1)
+
+
+def rebalance_classes(weights: np.ndarray, mean_c: np.ndarray, rate: float = 0.5,
+                      groups: int = XCDS) -> np.ndarray:
+    """New weights from class finish times (see rebalance)."""
+    g = weights.shape[0]
+    cls = np.arange(g) % groups
+    cnt = np.bincount(cls, minlength=groups)
     w_c = np.bincount(cls, weights=weights.astype(np.float64), minlength=groups) / np.maximum(cnt, 1)
     target = np.maximum(mean_c[cnt > 0].mean(), 1.0)
     f = w_c * (target / np.maximum(mean_c, 1.0)) ** rate
     f = f[cls]
     f *= 1024.0 / f.mean()
     return np.clip(np.rint(f), 64, 16384).astype(np.int32)
+
+
+def rebalance(weights: np.ndarray, stamps: np.ndarray, rate: float = 0.5, groups: int = XCDS) -> np.ndarray:
+    """New stream-kernel workgroup weights from one completed step.
+
+    Workgroups are pooled in ``groups`` classes by index modulo ``groups``
+    (the dies workgroups are dispatched to in turn, which run at measurably
+    different speeds; single workgroups only add noise).  Each class's weight
+    (its share of the tile list) moves towards what would have let it finish
+    with the others, w <- w * (mean / class mean) ** rate; the result is
+    scaled to a mean of 1024 and kept within 64..16384.  Results of the
+    decode do not depend on the weights, only the split of the work."""
+    return rebalance_classes(weights, class_finish(stamps, weights.shape[0], groups), rate, groups)
 
 
 class _Staging:
@@ -96,7 +109,7 @@ class PagedKVEngine:
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int, dtype,
                  order: Optional[Sequence[int]] = None, device: str = "cuda", poison: bool = True,
                  max_seqs: int = 256, max_context: int = 4096, ring: int = 8, guard_every: int = 4,
-                 balance: bool = True, balance_rate: float = 0.5):
+                 balance: bool = True, balance_rate: float = 0.2, balance_steps: int = 8):
         self.N, self.H, self.D, self.BS, self.dtype = num_blocks, num_kv_heads, head_dim, block_size, dtype
         self.device = torch.device(device)
         self.bm = BlockManager(num_blocks, block_size, order)
@@ -116,9 +129,10 @@ class PagedKVEngine:
         self._ws = torch.empty(0, dtype=torch.uint8, device=self.device)
         # workgroup weights of the stream kernel per (batch size, query heads),
         # fed back from the wave stamps of completed steps (see _balance)
-        self.balance, self.balance_rate = balance, balance_rate
+        self.balance, self.balance_rate, self.balance_steps = balance, balance_rate, balance_steps
         self._weights = {}
         self._wver = {}
+        self._wacc = {}
 
     # ------------------------------------------------------------- helpers
     def _next(self) -> _Staging:
@@ -133,15 +147,23 @@ class PagedKVEngine:
         return st
 
     def _balance(self, st: _Staging) -> None:
-        """Feedback from a completed step (see rebalance).  Stamps arrive a
-        ring's length of steps late, so only a step that ran with the current
-        weights updates them (at most once per lap): feedback from older
-        weights would correct the same error again and make the loop
-        oscillate."""
+        """Feedback from completed steps (see rebalance).  Stamps arrive a
+        ring's length of steps late, so only steps that ran with the current
+        weights count: feedback from older weights would correct the same
+        error again and make the loop oscillate.  A die's speed also varies
+        from step to step, so the class finish times of ``balance_steps``
+        such steps are averaged before one update."""
         (key, version), st.times_key = st.times_key, None
         w = self._weights.get(key)
-        if w is not None and version == self._wver.get(key):
-            w[:] = rebalance(w, st.times[: 8 * w.shape[0]].numpy(), self.balance_rate)
+        if w is None or version != self._wver.get(key):
+            return
+        acc = self._wacc.get(key)
+        if acc is None or acc[0] != version:
+            acc = self._wacc[key] = [version, np.zeros(XCDS), 0]
+        acc[1] += class_finish(st.times[: 8 * w.shape[0]].numpy(), w.shape[0])
+        acc[2] += 1
+        if acc[2] >= self.balance_steps:
+            w[:] = rebalance_classes(w, acc[1] / acc[2], self.balance_rate)
             self._wver[key] = version + 1
 
     def weights(self, num_seqs: int, num_q_heads: int) -> Optional[np.ndarray]:
