@@ -94,12 +94,17 @@ struct PrefillArgs {
   float scale_log2;              // scale * log2(e)
   int32_t out_f32;
 };
-// Column blocks per prefill wave: 2 (32 columns, 2 x 16 / group tokens) when
-// the chunks are long enough to keep at least 1024 such workgroups, else 1.
+// Column blocks per prefill wave (16 / group tokens each): more blocks
+// share each streamed tile and K operand among more columns, fewer keep
+// short chunks spread over enough workgroups.  3 when that still leaves at
+// least 4096 workgroups, 2 for at least 1024, else 1.
 inline int32_t prefill_column_blocks(int32_t group, int32_t max_query_len, int32_t num_seqs, int32_t num_kv_heads) {
-  const int64_t tpw2 = 4 * 2 * (16 / group);
-  const int64_t wgs2 = int64_t(num_seqs) * num_kv_heads * ((max_query_len + tpw2 - 1) / tpw2);
-  return (max_query_len >= tpw2 && wgs2 >= 1024) ? 2 : 1;
+  auto wgs = [&](int64_t cb) {
+    const int64_t tpw = 4 * cb * (16 / group);
+    return max_query_len < tpw ? int64_t(0) : int64_t(num_seqs) * num_kv_heads * ((max_query_len + tpw - 1) / tpw);
+  };
+  if (wgs(3) >= 4096) return 3;
+  return wgs(2) >= 1024 ? 2 : 1;
 }
 // Query tokens one prefill workgroup takes (four waves of column blocks of
 // 16 / group tokens).

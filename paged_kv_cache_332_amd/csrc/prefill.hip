@@ -355,7 +355,8 @@ hipError_t launch_g(const PrefillArgs& a, int32_t max_query_len, hipStream_t str
   const int tpw = 4 * cb * (16 / G);
   const size_t lds = 6 * 2 * (D / 32) * 1024;   // the tile ring: 6 slots of K and V
   dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads), block(256);
-  if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2>), grid, block, lds, stream, a);
+  if (cb == 3) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 3>), grid, block, lds, stream, a);
+  else if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2>), grid, block, lds, stream, a);
   else hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1>), grid, block, lds, stream, a);
   return hipGetLastError();
 }
