@@ -106,11 +106,6 @@ inline int32_t prefill_column_blocks(int32_t group, int32_t max_query_len, int32
   if (wgs(3) >= 4096) return 3;
   return wgs(2) >= 1024 ? 2 : 1;
 }
-// Query tokens one prefill workgroup takes (four waves of column blocks of
-// 16 / group tokens).
-inline int32_t prefill_tokens_per_wg(int32_t group, int32_t max_query_len, int32_t num_seqs, int32_t num_kv_heads) {
-  return 4 * prefill_column_blocks(group, max_query_len, num_seqs, num_kv_heads) * (16 / group);
-}
 hipError_t launch_prefill(const PrefillArgs& a, int32_t dtype, int32_t d, int32_t bs, int32_t group,
                           int32_t max_query_len, hipStream_t stream);
 

@@ -111,11 +111,12 @@ def test_prefill_rejects_bad_arguments():
 
 
 # dtype, head_dim, block size, q heads, kv heads, sequences, chunk, context range: batches large
-# enough for two column blocks per wave, three for the 32 x 768 case (the same sequence alone
-# takes one)
+# enough for two column blocks per wave, three for the *_three_blocks cases (the same sequence
+# alone takes one)
 WIDE = {
     "gqa4_bf16_bs16": ("bf16", 128, 16, 32, 8, 16, 512, (520, 1400)),
     "gqa4_bf16_bs16_three_blocks": ("bf16", 128, 16, 32, 8, 32, 768, (770, 1200)),
+    "mha_f16_bs8_d64_three_blocks": ("f16", 64, 8, 16, 16, 16, 3072, (3072, 3400)),
     "mha_f16_bs8_d64": ("f16", 64, 8, 16, 16, 8, 1024, (1030, 1500)),
     "gqa8_bf16_bs32": ("bf16", 128, 32, 64, 8, 8, 256, (300, 2000)),
     "gqa16_bf16_d64": ("bf16", 64, 16, 16, 1, 8, 1024, (1024, 1300)),
