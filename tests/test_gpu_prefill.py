@@ -172,3 +172,43 @@ def test_prefill_wide_workgroups_match_narrow(case):
             err = max(err, float(np.max(np.abs(got[qs[i] + t] - ref))))
     say(case, "wide prefill sampled max abs error", err)
     assert err <= 2e-3
+
+
+def test_prefill_empty_chunks_and_no_rows():
+    """Sequences with an empty chunk (no query rows) next to ones with rows,
+    and a call with no rows at all: only the real rows are written (the
+    rest of the output keeps its NaN fill), and they match the oracle."""
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    ctx = [40, 1, 300, 17]
+    chunk = [0, 1, 0, 17]
+    hq, hkv, d, bs = 8, 2, 64, 16
+    w = W.tiny(num_seqs=len(ctx), dtype="bf16", seed=61, ctx=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+               block_size=bs)
+    dev = runner.run_script(w, decode=False)
+    eng = dev.engine
+    tab, _ = eng.bm.export(list(range(len(ctx))), eng.stride)
+    rng = np.random.default_rng(62)
+    T = sum(chunk)
+    q = W.round_to_dtype(rng.standard_normal((T + 3, hq, d), dtype=np.float32), "bf16")
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    q_dev = torch.from_numpy(q).to("cuda").to(torch.bfloat16)
+    out = torch.full((T + 3, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    args = (torch.from_numpy(np.ascontiguousarray(tab)).to("cuda"), torch.from_numpy(qs).to("cuda"),
+            torch.from_numpy(np.asarray(ctx, np.int32)).to("cuda"))
+    pa.pa_prefill(out, q_dev, eng.k_cache, eng.v_cache, *args, max(chunk), max(ctx), 1.0 / d ** 0.5)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i, (n, L) in enumerate(zip(ctx, chunk)):
+        if L == 0:
+            continue
+        rows = w.row_of(i, np.arange(n))
+        ref = oracle.prefill_attention(q[qs[i]: qs[i + 1]], w.k_rows[rows], w.v_rows[rows], 1.0 / d ** 0.5)
+        assert float(np.max(np.abs(got[qs[i]: qs[i + 1]] - ref))) <= 2e-3
+    assert np.isnan(got[T:]).all()                       # rows past the last chunk untouched
+    # no rows at all: nothing is launched and nothing changes
+    before = out.clone()
+    zero = torch.zeros(len(ctx) + 1, dtype=torch.int32, device="cuda")
+    pa.pa_prefill(out, q_dev, eng.k_cache, eng.v_cache, args[0], zero, args[2], 0, max(ctx), 1.0 / d ** 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(out.isnan(), before.isnan()) and torch.equal(out.nan_to_num(), before.nan_to_num())
