@@ -51,6 +51,8 @@ def parse():
                     help="time the decode pass with HIP events on every k-th timed step (an event packet "
                          "between kernels costs the stream ~4 us, so sparse timing keeps the step intact)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the short prefill / prefix-cache / swap measurements added to the decode line")
     ap.add_argument("--cold", type=int, default=8, help="passes timed after evicting the Infinity Cache")
     ap.add_argument("--prefill", type=int, default=0, metavar="L",
                     help="measure pa_prefill instead: the last min(L, ctx) tokens of every sequence of the "
@@ -212,7 +214,7 @@ def prefill_bench(args, w, cfg, pa, runner, torch):
             tiles += -(-(p0 + min(L, b + tpw)) // 16)
     kv_bytes = tiles * cfg.num_kv_heads * 2 * 16 * cfg.head_dim * W_ELEM[cfg.dtype]
     tflops = flops / (us * 1e-6) / 1e12
-    print(json.dumps({
+    return {
         "metric": "paged prefill TFLOP/s", "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 4), "higher_is_better": True,
         "dtype": cfg.dtype, "data": "synthetic",
@@ -222,7 +224,7 @@ def prefill_bench(args, w, cfg, pa, runner, torch):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4), "kv_bytes_streamed": int(kv_bytes),
                      "kv_GBps": round(kv_bytes / (us * 1e-6) / 1e9, 1)},
-    }), flush=True)
+    }
 
 
 def swap_bench(args, w, cfg, pa, runner, torch):
@@ -270,7 +272,7 @@ def swap_bench(args, w, cfg, pa, runner, torch):
     us_dma_in = timed(lambda: flat_d.copy_(flat_h, non_blocking=True))
     gbps = lambda us: round(nbytes / (us * 1e-6) / 1e9, 2)
     peak = 64.0
-    print(json.dumps({
+    return {
         "metric": "swap GB/s", "value": gbps(us_out), "unit": "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": 2, "ms_per_step": round(us_out / 1e3, 4), "higher_is_better": True, "dtype": cfg.dtype,
         "data": "synthetic",
@@ -281,7 +283,7 @@ def swap_bench(args, w, cfg, pa, runner, torch):
         "dma_copy": {"out_GBps": gbps(us_dma_out), "in_GBps": gbps(us_dma_in)},
         "roofline": {"bound": "host-link", "achieved": gbps(us_out), "peak": peak, "unit": "GB/s",
                      "frac": round(gbps(us_out) / peak, 4), "frac_in": round(gbps(us_in) / peak, 4)},
-    }), flush=True)
+    }
 
 
 def prefix_cache_bench(args, cfg, pa, torch):
@@ -361,7 +363,7 @@ def prefix_cache_bench(args, cfg, pa, torch):
     for i, p in enumerate(prompts):
         write(eng.bm.add_seq(1000 + i, len(p)), 0)
     us_u, tf_u, T_u = run_prefill([1000 + i for i in range(B)], lens)
-    print(json.dumps({
+    return {
         "metric": "prefill speedup from the prefix cache", "value": round(us_u / us_c, 3), "unit": "x",
         "n_gpus": 1, "steps": max(1, min(args.steps, 20)), "warmup": 3, "ms_per_step": round(us_c / 1e3, 4),
         "higher_is_better": True, "dtype": cfg.dtype, "data": "synthetic",
@@ -372,7 +374,46 @@ def prefix_cache_bench(args, cfg, pa, torch):
         "uncached": {"ms": round(us_u / 1e3, 3), "query_tokens": T_u, "TFLOP/s": round(tf_u, 1)},
         "host_us_per_admission": {"shared_prefix_lap": round(host_us[0], 2),
                                   "readmission_median": round(float(np.median(host_us[1:])), 2)},
-    }), flush=True)
+    }
+
+
+def next_rows(args, w, cfg, pa, runner, torch):
+    """Short measurements of the rows beyond decode on the same workload's
+    shapes (each in full by its own flag): paged prefill of 512-token chunks
+    (--prefill 512), prefill with a shared 2048-token prefix served from the
+    cache (--prefix-cache 2048), preemption by swap of half the batch (--swap
+    0.5).  A failure is reported in place of the figures."""
+    out = {}
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup = 10, 8
+    for key, run in (("prefill_512", lambda: prefill_bench(_with(sub, prefill=512), w, cfg, pa, runner, torch)),
+                     ("prefix_cache_2048", lambda: prefix_cache_bench(_with(sub, prefix_cache=2048), cfg, pa, torch)),
+                     ("swap_half_batch", lambda: swap_bench(_with(sub, swap=0.5), w, cfg, pa, runner, torch))):
+        print(f"[bench] next row: {key}", file=sys.stderr, flush=True)
+        try:
+            r = run()
+        except Exception as e:  # reported, not fatal: the decode line above stands on its own
+            out[key] = {"error": f"{type(e).__name__}: {e}"}
+            continue
+        finally:
+            torch.cuda.empty_cache()
+        if key == "prefill_512":
+            out[key] = {"TFLOP/s": r["value"], "frac_of_bf16_peak": r["roofline"]["frac"], "ms": r["ms_per_step"],
+                        "query_tokens": r["config"]["query_tokens"], "column_blocks_per_wave": r["column_blocks_per_wave"]}
+        elif key == "prefix_cache_2048":
+            out[key] = {"speedup": r["value"], "cached_ms": r["cached"]["ms"], "uncached_ms": r["uncached"]["ms"],
+                        "reused_tokens": r["cached"]["reused_tokens"]}
+        else:
+            out[key] = {"out_GBps": r["swap_out"]["GBps"], "in_GBps": r["swap_in"]["GBps"],
+                        "frac_of_64GBps": r["roofline"]["frac"], "bytes_each_way": r["config"]["bytes_each_way"]}
+    return out
+
+
+def _with(ns, **kw):
+    n = argparse.Namespace(**vars(ns))
+    for k, v in kw.items():
+        setattr(n, k, v)
+    return n
 
 
 def main():
@@ -408,13 +449,13 @@ def main():
     # spare blocks for the tokens the warm-up and timed steps append
     extra_blocks = cfg.num_seqs * (-(-total_steps // cfg.block_size) + 1)
     if args.prefill:
-        prefill_bench(args, w, cfg, pa, runner, torch)
+        print(json.dumps(prefill_bench(args, w, cfg, pa, runner, torch)), flush=True)
         return
     if args.swap:
-        swap_bench(args, w, cfg, pa, runner, torch)
+        print(json.dumps(swap_bench(args, w, cfg, pa, runner, torch)), flush=True)
         return
     if args.prefix_cache:
-        prefix_cache_bench(args, cfg, pa, torch)
+        print(json.dumps(prefix_cache_bench(args, cfg, pa, torch)), flush=True)
         return
     dev = runner.run_script(w, partition_size=part, kernel=kernel, extra_context=total_steps,
                             extra_blocks=extra_blocks)
@@ -543,6 +584,10 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if not args.no_next and cfg.dtype != "f32":
+        del dev, eng
+        torch.cuda.empty_cache()
+        res["next_rows"] = next_rows(args, w, cfg, pa, runner, torch)
     print(json.dumps(res), flush=True)
 
 
