@@ -174,6 +174,20 @@ struct MfmaOps<BF16> {
   __device__ static f32x4 pv32(u32x4 a, v8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), b, c, 0, 0, 0);
   }
+  // p = hi + lo to about 2^-16 relative: hi is p with its low 16 bits cut
+  // off (a bf16 value, packed two a word by one byte permute), lo the exact
+  // remainder rounded to bf16
+  __device__ static void split(const float (&p)[8], v8& hi, v8& lo) {
+    u32x4 h;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x0 = __float_as_uint(p[2 * k]), x1 = __float_as_uint(p[2 * k + 1]);
+      h[k] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+      lo[2 * k] = static_cast<e>(p[2 * k] - __uint_as_float(x0 & 0xFFFF0000u));
+      lo[2 * k + 1] = static_cast<e>(p[2 * k + 1] - __uint_as_float(x1 & 0xFFFF0000u));
+    }
+    hi = __builtin_bit_cast(v8, h);
+  }
 };
 
 template <>
@@ -190,6 +204,14 @@ struct MfmaOps<F16> {
   }
   __device__ static f32x4 pv32(u32x4 a, v8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), b, c, 0, 0, 0);
+  }
+  // p = hi + lo: hi is p rounded to f16, lo the exact remainder rounded to f16
+  __device__ static void split(const float (&p)[8], v8& hi, v8& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      hi[i] = static_cast<e>(p[i]);
+      lo[i] = static_cast<e>(p[i] - static_cast<float>(hi[i]));
+    }
   }
 };
 

@@ -21,8 +21,11 @@
 // chunks: twice the flops per byte streamed; CB = 1 keeps short chunks
 // spread over many workgroups).  Per tile, wave and column block:
 // S^T = K Q^T with v_mfma_f32_16x16x32 (the K operand read once for all
-// blocks), a causal limit per column, the running-max softmax of the decode
-// kernel (reference maximum refreshed when it grows by more than 2^8), P
+// blocks), a causal limit per column (skipped where every key of the tiles
+// is visible to every column of the block), an online softmax over a lazy
+// reference maximum (the exponent folds the scale in as one fma; the
+// reference is raised to the column's exact maximum only when a lane's terms
+// of a step sum past 2^16, which leaves no maximum on the common path), P
 // split into a 16-bit high part and the rounded remainder for two P V
 // products into O^T; a block none of whose columns sees the tiles skips
 // them.  No split of the context: a workgroup covers its tokens' whole
@@ -124,10 +127,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int m = 0; m < NS; ++m) qop[cb][m] = *reinterpret_cast<const u32x4*>(qp + (4 * m + q) * 8);
   }
-  // the last position any column of block cb sees (uniform over the wave)
-  int blk_last[CB];
+  // the last position any column of block cb sees, and the causal limit of
+  // its first column, below which no key of the block is masked (both
+  // uniform over the wave)
+  int blk_last[CB], blk_open[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) blk_last[cb] = p0 + min(L, tw0 + (cb + 1) * TB) - 1;
+  for (int cb = 0; cb < CB; ++cb) {
+    blk_last[cb] = uniform(p0 + min(L, tw0 + (cb + 1) * TB) - 1);
+    blk_open[cb] = uniform(p0 + min(tw0 + cb * TB, L - 1) + 1);
+  }
+  // scores are taken raw and scaled inside the exponent, which needs a
+  // positive factor: a negative scale flips the sign of q (exact), a zero
+  // one zeroes q and scales by 1 (every score is 0 either way)
+  const float sraw = a.scale_log2;
+  const uint32_t qflip = sraw < 0.f ? 0x80008000u : 0u;
+  const uint32_t qkeep = sraw == 0.f ? 0u : 0xFFFFFFFFu;
+  const float sf = sraw == 0.f ? 1.f : fabsf(sraw);
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int m = 0; m < NS; ++m)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) qop[cb][m][w] = (qop[cb][m][w] & qkeep) ^ qflip;
   // the query loads complete here, in a wait the compiler knows about
   // (vmcnt 0; expcnt and lgkmcnt at their maxima): otherwise it waits for
   // every load in flight before each tile's first product
@@ -200,7 +221,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   };
 
   f32x4 acc[CB][NT];
-  float m_ref[CB], l_lane[CB];
+  float m_ref[CB], l_lane[CB];                   // (reference maximum: scaled, log2 units)
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
@@ -291,34 +312,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       // give exp2(-inf) = 0)
       if (16 * t > blk_last[cb]) continue;
       float sv[8];
+      if (16 * t + 32 <= blk_open[cb]) {
+        // every key of the pair is visible to every column of the block
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[i] = kp0 + i < lim[cb] ? sc[cb][0][i] * a.scale_log2 : kNegInf;
-        sv[4 + i] = kp0 + 16 + i < lim[cb] ? sc[cb][1][i] * a.scale_log2 : kNegInf;
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = sc[cb][0][i];
+          sv[4 + i] = sc[cb][1][i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = kp0 + i < lim[cb] ? sc[cb][0][i] : kNegInf;
+          sv[4 + i] = kp0 + 16 + i < lim[cb] ? sc[cb][1][i] : kNegInf;
+        }
       }
-      float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      mt = xor16<OpMax>(mt);
-      mt = xor32<OpMax>(mt);
-      const bool need = mt > m_ref[cb] + 8.f;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? (m_ref[cb] == kNegInf ? 0.f : fast_exp2(m_ref[cb] - mt)) : 1.f;
-        m_ref[cb] = need ? mt : m_ref[cb];
+      // exponents against the column's reference maximum as it stands; it
+      // is raised (to the column's exact maximum, over its four lanes) only
+      // when a lane's eight terms sum past 2^16 or are not finite (the first
+      // step, whose reference is -inf): no maximum at all on the common path
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb]));
+      float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      if (__builtin_amdgcn_ballot_w64(!(ps <= 65536.f))) {
+        float cm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        cm = xor16<OpMax>(cm);
+        cm = xor32<OpMax>(cm);
+        const float mn = cm * sf;
+        const bool up = mn > m_ref[cb];
+        const float alpha = up ? (m_ref[cb] == kNegInf ? 0.f : fast_exp2(m_ref[cb] - mn)) : 1.f;
+        m_ref[cb] = up ? mn : m_ref[cb];
         l_lane[cb] *= alpha;
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[cb][n] *= alpha;
-      }
-      float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sv[i] - m_ref[cb]);
-      l_lane[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb]));
+        ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      }
+      l_lane[cb] += ps;
       v8 phi, plo;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const el hi = static_cast<el>(p[i]);
-        phi[i] = hi;
-        plo[i] = static_cast<el>(p[i] - static_cast<float>(hi));
-      }
+      MF::split(p, phi, plo);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         acc[cb][n] = MF::pv32(vr[n], phi, acc[cb][n]);

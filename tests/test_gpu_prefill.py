@@ -212,3 +212,45 @@ def test_prefill_empty_chunks_and_no_rows():
     pa.pa_prefill(out, q_dev, eng.k_cache, eng.v_cache, args[0], zero, args[2], 0, max(ctx), 1.0 / d ** 0.5)
     torch.cuda.synchronize()
     assert torch.equal(out.isnan(), before.isnan()) and torch.equal(out.nan_to_num(), before.nan_to_num())
+
+
+# scales that take the kernel's other branches: a negative one (the sign of q
+# is flipped so that the factor inside the exponent is positive), zero (every
+# weight equal) and a large one (peaked rows whose reference maximum is
+# raised many times along the context)
+SCALES = {"negative": -0.125, "zero": 0.0, "large": 2.0}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("which", list(SCALES))
+def test_prefill_scale_sign_zero_and_large(dtype, which):
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    scale = SCALES[which]
+    ctx, chunk = [700, 40, 1], [300, 40, 1]
+    hq, hkv, d, bs = 16, 4, 128, 16
+    say("prefill scale", which, dtype)
+    w = W.tiny(num_seqs=len(ctx), dtype=dtype, seed=91, ctx=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+               block_size=bs)
+    dev = runner.run_script(w, decode=False)
+    eng = dev.engine
+    tab, _ = eng.bm.export(list(range(len(ctx))), eng.stride)
+    rng = np.random.default_rng([92, len(which)])
+    T = sum(chunk)
+    q = W.round_to_dtype(rng.standard_normal((T, hq, d), dtype=np.float32), dtype)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    q_dev = torch.from_numpy(q).to("cuda").to(runner.TORCH_DTYPE[dtype])
+    out = torch.full((T, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    pa.pa_prefill(out, q_dev, eng.k_cache, eng.v_cache, torch.from_numpy(np.ascontiguousarray(tab)).to("cuda"),
+                  torch.from_numpy(qs).to("cuda"), torch.from_numpy(np.asarray(ctx, np.int32)).to("cuda"),
+                  max(chunk), max(ctx), scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = 0.0
+    for i, n in enumerate(ctx):
+        rows = w.row_of(i, np.arange(n))
+        ref = oracle.prefill_attention(q[qs[i]: qs[i + 1]], w.k_rows[rows], w.v_rows[rows], scale)
+        err = max(err, float(np.max(np.abs(got[qs[i]: qs[i + 1]] - ref))))
+    say(which, dtype, "max abs error", err)
+    assert err <= 2e-3
