@@ -37,6 +37,8 @@
 // rate of the 16x16x16 form over one tile): key k = 8 q + i of the product
 // is key 4 q + i of the first tile for i < 4, of the second for i >= 4, in
 // both operands.  Registers are held to two waves per SIMD.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -230,6 +232,160 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     l_lane[cb] = 0.f;
   }
 
+  // one softmax step over tiles t, t + 1 (OPEN: every key of the pair is
+  // visible to every column of the wave, and the reference maxima are finite)
+  auto pair_step = [&](int t, auto open_tag) __attribute__((always_inline)) {
+    constexpr bool OPEN = decltype(open_tag)::value;
+    const uint8_t* sa = ring + (t % NSL) * SLOT;
+    const uint8_t* sb = ring + ((t + 1) % NSL) * SLOT;
+    const int kp0 = 16 * t + 4 * q;              // keys kp0 .. + 3 (tile t), kp0 + 16 .. + 19 (tile t + 1)
+    f32x4 sc[CB][2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const uint8_t* sl = h2 ? sb : sa;
+      u32x4 kr[NS];
+#pragma unroll
+      for (int m = 0; m < NS; ++m) kr[m] = ring_read<u32x4>(sl + ((4 * m + q) * 16 + c) * 16);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        sc[cb][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (!OPEN) {
+          if (16 * t > blk_last[cb]) continue;
+        }
+#pragma unroll
+        for (int m = 0; m < NS; ++m) sc[cb][h2] = MF::qk(kr[m], qop[cb][m], sc[cb][h2]);
+      }
+    }
+    // V rows of both tiles, 8 keys per lane (k = 8 q + i: key kp0 + i of
+    // tile t for i < 4, of tile t + 1 for i >= 4), zeros past the
+    // workgroup's last position (which may hold anything, NaN poison
+    // included)
+    u32x4 vr[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const u32x2 va = ring_read<u32x2>(sa + KI * 1024 + (16 * n + c) * 32 + 8 * q);
+      const u32x2 vb = ring_read<u32x2>(sb + KI * 1024 + (16 * n + c) * 32 + 8 * q);
+      vr[n] = u32x4{va[0], va[1], vb[0], vb[1]};
+    }
+    if constexpr (OPEN) {
+      // exponents against the reference maxima as they stand; a column's
+      // reference is raised to its exact maximum only when one of its terms
+      // would pass 2^13 (or is not a number)
+      float x[CB][8], xm[CB];
+      bool over = false;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[cb][i] = __builtin_fmaf(sc[cb][0][i], sf, -m_ref[cb]);
+          x[cb][4 + i] = __builtin_fmaf(sc[cb][1][i], sf, -m_ref[cb]);
+        }
+        xm[cb] = fmaxf(fmaxf(fmaxf(x[cb][0], x[cb][1]), fmaxf(x[cb][2], x[cb][3])),
+                       fmaxf(fmaxf(x[cb][4], x[cb][5]), fmaxf(x[cb][6], x[cb][7])));
+        over = over || !(xm[cb] <= 13.f);
+      }
+      if (__builtin_amdgcn_ballot_w64(over)) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          float cm = xor16<OpMax>(xm[cb]);
+          cm = xor32<OpMax>(cm);
+          const bool up = cm > 0.f;
+          const float mn = up ? m_ref[cb] + cm : m_ref[cb];
+          const float d = mn - m_ref[cb];
+          const float alpha = fast_exp2(-d);
+          m_ref[cb] = mn;
+          l_lane[cb] *= alpha;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[cb][n] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[cb][i] -= d;
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(x[cb][i]);
+        l_lane[cb] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+        v8 phi, plo;
+        MF::split(pv, phi, plo);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          acc[cb][n] = MF::pv32(vr[n], phi, acc[cb][n]);
+          acc[cb][n] = MF::pv32(vr[n], plo, acc[cb][n]);
+        }
+      }
+    } else {
+      if (16 * t + 32 > kmax) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) {
+            const int k0 = kp0 + (w2 >> 1) * 16 + 2 * (w2 & 1);   // the two keys of 32-bit word w2
+            uint32_t x = vr[n][w2];
+            if (k0 >= kmax) x &= 0xFFFF0000u;
+            if (k0 + 1 >= kmax) x &= 0x0000FFFFu;
+            vr[n][w2] = x;
+          }
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        // (tile 0 holds position 0, which every column sees, so no block
+        // skips the first pair: m_ref is finite from then on and masked terms
+        // give exp2(-inf) = 0)
+        if (16 * t > blk_last[cb]) continue;
+        float sv[8];
+        if (16 * t + 32 <= blk_open[cb]) {
+          // every key of the pair is visible to every column of the block
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sv[i] = sc[cb][0][i];
+            sv[4 + i] = sc[cb][1][i];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sv[i] = kp0 + i < lim[cb] ? sc[cb][0][i] : kNegInf;
+            sv[4 + i] = kp0 + 16 + i < lim[cb] ? sc[cb][1][i] : kNegInf;
+          }
+        }
+        // exponents against the column's reference maximum as it stands; it
+        // is raised (to the column's exact maximum, over its four lanes) only
+        // when a lane's eight terms sum past 2^16 or are not finite (the first
+        // step, whose reference is -inf): no maximum at all on the common path
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb]));
+        float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        if (__builtin_amdgcn_ballot_w64(!(ps <= 65536.f))) {
+          float cm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                           fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+          cm = xor16<OpMax>(cm);
+          cm = xor32<OpMax>(cm);
+          const float mn = cm * sf;
+          const bool up = mn > m_ref[cb];
+          const float alpha = up ? (m_ref[cb] == kNegInf ? 0.f : fast_exp2(m_ref[cb] - mn)) : 1.f;
+          m_ref[cb] = up ? mn : m_ref[cb];
+          l_lane[cb] *= alpha;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[cb][n] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb]));
+          ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        }
+        l_lane[cb] += ps;
+        v8 phi, plo;
+        MF::split(p, phi, plo);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          acc[cb][n] = MF::pv32(vr[n], phi, acc[cb][n]);
+          acc[cb][n] = MF::pv32(vr[n], plo, acc[cb][n]);
+        }
+      }
+    }
+  };
+
   stage_ids(0);
   __syncthreads();
   // tiles go in pairs (32 keys per softmax step): pair p computes from slots
@@ -238,7 +394,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (i < nt) issue(i);
-  for (int t = 0; t < nt; t += 2) {
+  // one pair: wait for its tiles, refill the slots of the pair before it,
+  // compute
+  auto advance = [&](int t, auto open_tag) __attribute__((always_inline)) {
     // this wave's loads of tiles t and t + 1 have landed once at most its
     // loads of the newer tiles are outstanding; the barrier then covers every
     // wave's share (and every wave is done with the previous pair, whose
@@ -259,107 +417,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         issue(tn);
       }
     }
-    // ---- tiles t, t + 1: S^T = K Q^T per tile, causal mask per column,
-    // one online-softmax step over the 32 keys, P V over the 32 keys (a
-    // missing tile t + 1 reads a stale slot: every one of its scores is
-    // masked and its values are selected to zero)
-    const uint8_t* sa = ring + (t % NSL) * SLOT;
-    const uint8_t* sb = ring + ((t + 1) % NSL) * SLOT;
-    const int kp0 = 16 * t + 4 * q;              // keys kp0 .. + 3 (tile t), kp0 + 16 .. + 19 (tile t + 1)
-    f32x4 sc[CB][2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const uint8_t* sl = h2 ? sb : sa;
-      u32x4 kr[NS];
-#pragma unroll
-      for (int m = 0; m < NS; ++m) kr[m] = ring_read<u32x4>(sl + ((4 * m + q) * 16 + c) * 16);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        sc[cb][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (16 * t > blk_last[cb]) continue;
-#pragma unroll
-        for (int m = 0; m < NS; ++m) sc[cb][h2] = MF::qk(kr[m], qop[cb][m], sc[cb][h2]);
-      }
-    }
-    // V rows of both tiles, 8 keys per lane (k = 8 q + i: key kp0 + i of
-    // tile t for i < 4, of tile t + 1 for i >= 4), zeros past the
-    // workgroup's last position (which may hold anything, NaN poison
-    // included)
-    u32x4 vr[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const u32x2 va = ring_read<u32x2>(sa + KI * 1024 + (16 * n + c) * 32 + 8 * q);
-      const u32x2 vb = ring_read<u32x2>(sb + KI * 1024 + (16 * n + c) * 32 + 8 * q);
-      vr[n] = u32x4{va[0], va[1], vb[0], vb[1]};
-    }
-    if (16 * t + 32 > kmax) {
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const int k0 = kp0 + (w2 >> 1) * 16 + 2 * (w2 & 1);   // the two keys of 32-bit word w2
-          uint32_t x = vr[n][w2];
-          if (k0 >= kmax) x &= 0xFFFF0000u;
-          if (k0 + 1 >= kmax) x &= 0x0000FFFFu;
-          vr[n][w2] = x;
-        }
-      }
-    }
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      // (tile 0 holds position 0, which every column sees, so no block
-      // skips the first pair: m_ref is finite from then on and masked terms
-      // give exp2(-inf) = 0)
-      if (16 * t > blk_last[cb]) continue;
-      float sv[8];
-      if (16 * t + 32 <= blk_open[cb]) {
-        // every key of the pair is visible to every column of the block
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[i] = sc[cb][0][i];
-          sv[4 + i] = sc[cb][1][i];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[i] = kp0 + i < lim[cb] ? sc[cb][0][i] : kNegInf;
-          sv[4 + i] = kp0 + 16 + i < lim[cb] ? sc[cb][1][i] : kNegInf;
-        }
-      }
-      // exponents against the column's reference maximum as it stands; it
-      // is raised (to the column's exact maximum, over its four lanes) only
-      // when a lane's eight terms sum past 2^16 or are not finite (the first
-      // step, whose reference is -inf): no maximum at all on the common path
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb]));
-      float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      if (__builtin_amdgcn_ballot_w64(!(ps <= 65536.f))) {
-        float cm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        cm = xor16<OpMax>(cm);
-        cm = xor32<OpMax>(cm);
-        const float mn = cm * sf;
-        const bool up = mn > m_ref[cb];
-        const float alpha = up ? (m_ref[cb] == kNegInf ? 0.f : fast_exp2(m_ref[cb] - mn)) : 1.f;
-        m_ref[cb] = up ? mn : m_ref[cb];
-        l_lane[cb] *= alpha;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[cb][n] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb]));
-        ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      }
-      l_lane[cb] += ps;
-      v8 phi, plo;
-      MF::split(p, phi, plo);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        acc[cb][n] = MF::pv32(vr[n], phi, acc[cb][n]);
-        acc[cb][n] = MF::pv32(vr[n], plo, acc[cb][n]);
-      }
-    }
-  }
+    pair_step(t, open_tag);
+  };
+  // Pairs past the first whose keys every column of the wave sees (those
+  // before the wave's first causal limit) take the open path: no causal
+  // mask, no skipped block, no zeroed values, and one rescale check for all
+  // blocks, so that each phase is one straight run of code in which the
+  // matrix products of one block overlap the vector work of the next.  The
+  // first pair (where the reference maxima are set) and those from the
+  // diagonal on take the general path: a causal limit per column, blocks
+  // past their last position skipped, and a missing tile t + 1 read from a
+  // stale slot with every score masked and every value selected to zero.
+  const int open_end = max(2, (blk_open[0] - 32) / 16 + 1);   // first t (even or odd) not open
+  int t = 0;
+  advance(t, std::false_type{});
+  for (t = 2; t < open_end; t += 2) advance(t, std::true_type{});
+  for (; t < nt; t += 2) advance(t, std::false_type{});
 
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
