@@ -66,6 +66,11 @@ def parse():
                          "and again with none (prints its own JSON line)")
     ap.add_argument("--burst", type=int, default=16,
                     help="back-to-back pass launches timed for the roofline's launch duration")
+    ap.add_argument("--pool-order", default="config", choices=["config", "identity"],
+                    help="initial free-list order: the config's own (seeded permutation) or identity, so that "
+                         "blocks taken in order are physically consecutive")
+    ap.add_argument("--l2-model", action="store_true",
+                    help="add the modelled L2 read requests of the last step's pass, by class")
     ap.add_argument("--no-balance", action="store_true",
                     help="equal workgroup shares in the stream kernel (no feedback from wave times)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -161,6 +166,74 @@ def cpu_baseline(w, budget_s: float):
 
 
 W_ELEM = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def l2_request_model(ctx, num_kv_heads, group, head_dim, esize, block_size, grid, weights, stride, pa):
+    """L2 read requests of one stream pass by class, modelled from the pass's
+    split (128-byte lines, one request per distinct line of a wave's load
+    instruction): K/V tile lines, block-table lines, query-row lines and the
+    start-up metadata (plan entries, lengths, tile prefix sums).  A line is a
+    compulsory miss the first time a die (XCD, workgroup b on die b mod 8)
+    touches it in the pass; the model counts those too.  Tiles are 16 tokens:
+    at block size 8 a tile takes two table entries (the second only when it
+    holds a context token, else the first block is read twice and its lanes
+    coalesce into half the lines); at 32 two tiles share one entry."""
+    line = 128
+    ctx = np.asarray(ctx, np.int64)
+    tiles = -(-ctx // 16)
+    pre = np.concatenate([[0], np.cumsum(tiles)]).astype(np.int64)
+    starts, _, _ = pa.pa_stream_plan(pre.astype(np.int32), num_kv_heads, grid, weights)
+    starts = starts.astype(np.int64)
+    B = len(ctx)
+    tcap = 224
+    tab_base = 16 * B                      # tables follow slots, pairs and lengths in the record
+    kv_lines_per_tile = 2 * 16 * head_dim * esize // line
+    q_lines = -(-group * head_dim * esize // line)
+    seen = [set() for _ in range(8)]
+    n_tab = n_tab_first = n_q = n_kv = 0
+
+    def count(die, addrs):
+        nonlocal n_tab, n_tab_first
+        ls = np.unique(addrs // line)
+        n_tab += len(ls)
+        for x in ls.tolist():
+            if x not in seen[die]:
+                seen[die].add(x)
+                n_tab_first += 1
+
+    for w in range(4 * grid):
+        ga, gb = int(starts[w]), int(starts[w + 1])
+        if ga >= gb:
+            continue
+        die = (w // 4) % 8
+        g = np.arange(ga, gb)
+        seq = np.searchsorted(num_kv_heads * pre, g, side="right") - 1
+        r = g - num_kv_heads * pre[seq]
+        nt = tiles[seq]
+        t = r % nt
+        row = tab_base + seq * stride * 4
+        if block_size == 8:
+            two = 16 * t + 8 < ctx[seq]
+            ax, ay = row + 2 * t * 4, row + np.where(two, 2 * t + 1, 2 * t) * 4
+            n_kv += int(np.sum(np.where(two, kv_lines_per_tile, kv_lines_per_tile // 2)))
+        else:
+            ax, ay = row + (t if block_size == 16 else t // 2) * 4, None
+            n_kv += (gb - ga) * kv_lines_per_tile
+        # query rows at every item start inside the share, and the first item
+        n_q += q_lines * int(np.count_nonzero((t == 0)[1:]) + 1)
+        for c0 in range(0, gb - ga, tcap):
+            for j in range(c0, min(c0 + tcap, gb - ga), 64):
+                e = min(j + 64, c0 + tcap, gb - ga)
+                count(die, ax[j:e])
+                if ay is not None:
+                    count(die, ay[j:e])
+    # start-up: each wave reads two plan words, each workgroup B + 1 prefix
+    # sums and B lengths (4-byte entries)
+    meta = 4 * grid + grid * (-(-(B + 1) * 4 // line) + -(-B * 4 // line))
+    meta_lines = -(-(4 * grid + 1) * 4 // line) + 8 * (-(-(B + 1) * 4 // line) + -(-B * 4 // line))
+    return {"line_bytes": line, "kv": int(n_kv), "table": int(n_tab), "table_first_touch_per_die": int(n_tab_first),
+            "query": int(n_q), "metadata": int(meta), "metadata_first_touch_per_die": int(min(meta, meta_lines)),
+            "total": int(n_kv + n_tab + n_q + meta)}
 
 
 def prefill_bench(args, w, cfg, pa, runner, torch):
@@ -437,6 +510,8 @@ def main():
     kernel = {"auto": pa.PA_KERNEL_AUTO, "valu": pa.PA_KERNEL_VALU, "mfma": pa.PA_KERNEL_MFMA,
               "stream": pa.PA_KERNEL_STREAM}[args.kernel]
     w = W.build(args.config)
+    if args.pool_order == "identity" and w.ops[0][0] == "create":
+        w.ops[0] = ("create", w.ops[0][1], None)
     dtype = runner.TORCH_DTYPE[cfg.dtype]
     esize = W_ELEM[cfg.dtype]
     print(f"[bench] {args.config}: {cfg.description}; replaying construction script", file=sys.stderr,
@@ -556,7 +631,8 @@ def main():
                    "ctx_mean": round(float(np.mean(step_ctx[0])), 1), "partition": part or
                    pa.pa_decode_default_partition(cfg.num_seqs, cfg.num_kv_heads, int(step_ctx[-1].max()),
                                                   cfg.block_size),
-                   "kernel": args.kernel, "balance": eng.balance, "parallelism": "single GPU"},
+                   "kernel": args.kernel, "balance": eng.balance, "pool_order": args.pool_order,
+                   "parallelism": "single GPU"},
         "tokens_per_s": round(cfg.num_seqs * args.steps / elapsed, 1),
         "host_us_per_step": round(float(np.median(host_s)) * 1e6, 1),
         "host_us_per_step_max": round(float(np.max(host_s)) * 1e6, 1),
@@ -581,6 +657,11 @@ def main():
                                          "event packets' own latency"}},
         "cpu_baseline": None,
     }
+    if args.l2_model and kname == "stream":
+        res["l2_request_model"] = l2_request_model(
+            step_ctx[-1], cfg.num_kv_heads, cfg.group, cfg.head_dim, esize, cfg.block_size,
+            pa.pa_decode_stream_grid(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim),
+            eng.weights(cfg.num_seqs, cfg.num_q_heads), eng.stride, pa)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

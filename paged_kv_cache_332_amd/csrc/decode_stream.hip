@@ -33,7 +33,9 @@
 // issue order.  Per tile a wave issues DPT = 2 D / 32 loads (K then V), plus
 // the query rows when the tile starts an item for that wave; waiting until at
 // most DPT (NSLOT - 1) loads are outstanding therefore guarantees the oldest
-// tile has landed (extra query loads only make the wait stricter).
+// tile has landed (extra query loads only make the wait stricter).  The K/V
+// loads carry the non-temporal cache policy: every K/V byte is read once per
+// pass, and with the default policy the pass ran about 12% slower.
 //
 // Slot layout (bf16/f16, 16-byte units):
 //   K  [D/8][16 tokens][8]   the MFMA A operand of S^T = K Q^T reads chunk
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
         tok = t & 7;
       }
       const int64_t e = ((int64_t(blk) * Hkv + cu.kvh) * (D / 8) + j) * (BS * 8) + tok * 8;
-      dma16(kpool + e, sl + i * 1024);
+      dma16_once(kpool + e, sl + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
         tok0 = 0;
       }
       const int64_t e = ((int64_t(blk) * Hkv + cu.kvh) * D + d) * BS + tok0;
-      dma16(vpool + e, sl + KI * 1024 + i * 1024);
+      dma16_once(vpool + e, sl + KI * 1024 + i * 1024);
     }
   };
 

@@ -223,6 +223,16 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, 0);
 }
 
+// The same load with the non-temporal cache policy (the "nt" bit of gfx950
+// memory instructions): the caches treat the line as streaming data that will
+// not be read again.  For bytes a launch reads exactly once (the K/V tiles of
+// a decode pass); lines that are read again (block tables, lengths, code)
+// then keep their place in L2.
+constexpr int kCpolNonTemporal = 2;
+__device__ __forceinline__ void dma16_once(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, kCpolNonTemporal);
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 // The memory clobber keeps LDS reads of the landed tile below the wait.
 template <int N>
