@@ -34,8 +34,10 @@
 // the query rows when the tile starts an item for that wave; waiting until at
 // most DPT (NSLOT - 1) loads are outstanding therefore guarantees the oldest
 // tile has landed (extra query loads only make the wait stricter).  The K/V
-// loads carry the non-temporal cache policy: every K/V byte is read once per
-// pass, and with the default policy the pass ran about 12% slower.
+// loads carry the non-temporal cache policy where a tile covers whole 128-byte
+// lines, which no later tile of the pass reads again (with the default policy
+// the pass ran about 12% slower); at block size 32 the V lines are shared by
+// two tiles and keep the default policy.
 //
 // Slot layout (bf16/f16, 16-byte units):
 //   K  [D/8][16 tokens][8]   the MFMA A operand of S^T = K Q^T reads chunk
@@ -120,10 +122,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
   const bits* vpool = static_cast<const bits*>(a.v);
   const bits* qbase = static_cast<const bits*>(a.q);
 
-  // issue the loads of one tile into slot s (ids = its block ids; with
+  // issue the loads of one tile into slot s (ids = its block ids, the second
+  // one's complement when the tile's blocks are shared and stay cached; with
   // qload the item's query rows too: the tile starts the item or the wave)
   auto issue = [&](const Cursor& cu, int s, int2 ids, bool qload) {
     uint8_t* sl = slots + s * SB;
+    const bool once = ids.y >= 0;
+    ids.y = once ? ids.y : ~ids.y;
     if (qload) {
       // query rows of the item; lanes past G * D read row 0 again
       const int64_t qrow = (int64_t(cu.seq) * Hq + int64_t(cu.kvh) * G) * D;
@@ -134,6 +139,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
         dma16(qbase + qrow + int64_t(uu) * 8, sl + 2 * KI * 1024 + i * 1024);
       }
     }
+    int64_t ek[KI], ev[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int u = i * 64 + lane;
@@ -149,8 +155,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
         blk = t < 8 ? ids.x : ids.y;
         tok = t & 7;
       }
-      const int64_t e = ((int64_t(blk) * Hkv + cu.kvh) * (D / 8) + j) * (BS * 8) + tok * 8;
-      dma16_once(kpool + e, sl + i * 1024);
+      ek[i] = ((int64_t(blk) * Hkv + cu.kvh) * (D / 8) + j) * (BS * 8) + tok * 8;
     }
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
@@ -167,8 +172,24 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
         blk = h ? ids.y : ids.x;
         tok0 = 0;
       }
-      const int64_t e = ((int64_t(blk) * Hkv + cu.kvh) * D + d) * BS + tok0;
-      dma16_once(vpool + e, sl + KI * 1024 + i * 1024);
+      ev[i] = ((int64_t(blk) * Hkv + cu.kvh) * D + d) * BS + tok0;
+    }
+    // one uniform branch per tile around the loads alone
+    if (once) {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) dma16_once(kpool + ek[i], sl + i * 1024);
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        // at block size 32 a tile holds half of each 64-byte V row and the
+        // next tile reads the other half of the same lines: those stay cached
+        if constexpr (BS == 32) dma16(vpool + ev[i], sl + KI * 1024 + i * 1024);
+        else dma16_once(vpool + ev[i], sl + KI * 1024 + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) dma16(kpool + ek[i], sl + i * 1024);
+#pragma unroll
+      for (int i = 0; i < KI; ++i) dma16(vpool + ev[i], sl + KI * 1024 + i * 1024);
     }
   };
 
@@ -412,6 +433,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
 
   // ---- passes of at most tcap tiles: stage block ids, then stream ---------
   const int32_t* tables = a.tables;
+  // (without shared counts the lengths are read instead and not used, so
+  // that no branch stands around the load)
+  const int32_t* shr_src = sa.shared ? sa.shared : a.ctx;
   for (int64_t pa0 = ga; pa0 < gb; pa0 += tcap) {
     const int n = int(min(int64_t(tcap), gb - pa0));
     // block ids of each tile of the pass (BS 8: two blocks per tile; the
@@ -420,35 +444,45 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(StreamArgs sa) {
     // round trip, not one per 64 tiles)
     // (the values are only combined at the LDS writes, so no load waits for
     // another)
+    // (the positions are found first and the loads issued after them: a
+    // load in flight across the search loop makes the compiler wait for it)
     constexpr int kIdIters = (tcap + 63) / 64;
-    int32_t idx[kIdIters], idy[kIdIters];
+    int32_t idx[kIdIters], idy[kIdIters], shr[kIdIters], bi[kIdIters], sq[kIdIters], tt[kIdIters];
     bool two[kIdIters];
 #pragma unroll
     for (int j = 0; j < kIdIters; ++j) {
       const int i = lane + 64 * j;
       two[j] = false;
+      sq[j] = 0;
+      tt[j] = 0;
       if (i < n) {
         const Cursor cu = locate(pa0 + i);
-        const int32_t* row = tables + int64_t(cu.seq) * a.table_stride;
-        if constexpr (BS == 16) {
-          idx[j] = row[cu.t];
-        } else if constexpr (BS == 32) {
-          idx[j] = row[cu.t >> 1];
-        } else {
-          // the second block of the tile only when it holds a context token
-          // (else an in-range entry is read and not used)
-          two[j] = 16 * cu.t + 8 < cu.ctx;
-          idx[j] = row[2 * cu.t];
-          idy[j] = row[two[j] ? 2 * cu.t + 1 : 2 * cu.t];
-        }
+        sq[j] = cu.seq;
+        tt[j] = cu.t;
+        // the second block of a tile at block size 8 only when it holds a
+        // context token (else an in-range entry is read and not used)
+        two[j] = BS == 8 && 16 * cu.t + 8 < cu.ctx;
+      }
+      // first block of the tile, against the sequence's shared blocks
+      bi[j] = BS == 16 ? tt[j] : BS == 32 ? tt[j] >> 1 : 2 * tt[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kIdIters; ++j) {
+      const int i = lane + 64 * j;
+      shr[j] = 0;
+      if (i < n) {
+        const int32_t* row = tables + int64_t(sq[j]) * a.table_stride;
+        shr[j] = shr_src[sq[j]];
+        idx[j] = row[bi[j]];
+        if constexpr (BS == 8) idy[j] = row[two[j] ? bi[j] + 1 : bi[j]];
       }
     }
 #pragma unroll
     for (int j = 0; j < kIdIters; ++j) {
       const int i = lane + 64 * j;
       if (i < n) {
-        if constexpr (BS == 8) tbl[i] = int2{idx[j], two[j] ? idy[j] : idx[j]};
-        else tbl[i] = int2{idx[j], idx[j]};
+        const int32_t y = BS == 8 && two[j] ? idy[j] : idx[j];
+        tbl[i] = int2{idx[j], sa.shared && bi[j] < shr[j] ? ~y : y};
       }
     }
     lgkm_wait0();

@@ -307,6 +307,7 @@ pa_status decode_impl(void* out, pa_dtype out_dtype, const void* q, const void* 
         sa.cut_workers = extras->cut_workers;
         sa.num_cut = extras->num_cut;
         sa.wave_time = extras->wave_time;
+        sa.shared = extras->shared;
       }
       return pa::hip_status(fn, pa::launch_decode_stream(sa, kv_dtype, head_dim, block_size, sp.gmax, sp.nslot,
                                                           sp.lds, sp.grid, phases, s));

@@ -20,6 +20,7 @@ struct StreamExtras {
   const int32_t* cut_workers;  // the waves of each cut item, in order
   int32_t num_cut;
   int32_t* wave_time;          // [grid * 4][2] wave start and end stamps, 10 ns units (written)
+  const int32_t* shared;       // [B] leading blocks of each sequence that other sequences also hold
 };
 
 pa_status decode_impl(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,

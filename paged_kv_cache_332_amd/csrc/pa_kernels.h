@@ -59,6 +59,8 @@ struct StreamArgs {
   int32_t num_cut;
   int32_t* wave_time;            // [grid * 4][2] start and end of each wave (low 32 bits of the
                                  // 100 MHz real-time counter), or null
+  const int32_t* shared;         // [B] leading blocks of each sequence that other sequences also
+                                 // hold (read again in the same pass), or null: none
 };
 
 // Stream kernel limits: tiles whose block ids a wave stages per pass, the

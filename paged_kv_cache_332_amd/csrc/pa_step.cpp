@@ -60,20 +60,23 @@ size_t plan_entries(int64_t grid) { return size_t(4 * grid + 1 + 3) / 4 * 4; }
 size_t record_words(int64_t n, int64_t stride, int64_t hkv, int64_t grid) {
   // (the plan: wave starts padded to 4 words, an 8-word entry per cut item,
   // at most two cut items per wave in the full wave list)
-  const size_t w = size_t(n) * (5 + stride + 8 * hkv) + 1 + kHeaderWords + 3 + (grid ? 12 * grid + 4 : 0);
+  const size_t w = size_t(n) * (6 + stride + 8 * hkv) + 1 + kHeaderWords + 3 + (grid ? 12 * grid + 4 : 0);
   return (w + 3) / 4 * 4;
 }
 
-// Where the parts of a record for n sequences start.  The header holds the
+// Where the parts of a record for n sequences start: slots [n], copy-on-write
+// pairs [n][2], lengths [n], tables [n][stride], tile prefix sums [n + 1],
+// shared leading blocks [n], header, plan.  The header holds the
 // copy-on-write pair count, the stream grid the plan was made for (0: no
 // plan), the cut-item count and the words in use.
 struct Layout {
-  size_t pre, header, plan;
+  size_t pre, shared, header, plan;
 };
 Layout layout(int64_t n, int64_t stride) {
   Layout l;
   l.pre = size_t(4 * n + n * stride);
-  l.header = l.pre + size_t(n) + 1;
+  l.shared = l.pre + size_t(n) + 1;
+  l.header = l.shared + size_t(n);
   l.plan = (l.header + kHeaderWords + 3) / 4 * 4;  // 16-byte aligned, as are the entries
   return l;
 }
@@ -132,7 +135,7 @@ pa_status run_device(const char* fn, const int32_t* stage_host, const int32_t* h
   }
   const int32_t* d_ctx = stage_dev + 3 * n;
   const int32_t* d_tables = stage_dev + 4 * n;
-  pa::StreamExtras ex{stage_dev + lo.pre, nullptr, nullptr, nullptr, 0, d_times};
+  pa::StreamExtras ex{stage_dev + lo.pre, nullptr, nullptr, nullptr, 0, d_times, stage_dev + lo.shared};
   if (grid > 0) {
     const int32_t* plan = stage_dev + lo.plan;
     ex.wave_start = plan;
@@ -303,6 +306,17 @@ pa_status pa_step(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* stage_host
   int32_t* pre = stage_host + lo.pre;
   pre[0] = 0;
   for (int32_t i = 0; i < n; ++i) pre[i + 1] = pre[i] + (ctx[i] + 15) / 16;
+  // blocks at the front of each table that other sequences also hold (a
+  // forked or cached prefix): the pass reads them more than once, so their
+  // loads keep the caching policy; the walk stops at the first private block
+  int32_t* shared = stage_host + lo.shared;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t* row = tables + int64_t(i) * table_stride;
+    const int32_t nb = (ctx[i] + block_size - 1) / block_size;
+    int32_t j = 0;
+    while (j < nb && pa_bm_refcount(bm, row[j]) > 1) ++j;
+    shared[i] = j;
+  }
   int32_t ncut = 0;
   const bool planned = grid > 0 && int64_t(num_kv_heads) * pre[n] < (int64_t(1) << 31);
   const size_t plan_words =

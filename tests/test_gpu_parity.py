@@ -390,3 +390,39 @@ def test_step_layer_reuses_the_record(kern):
     say("negated V: max |out2 + out0|", err)
     assert err <= 1e-6 and float(out0.abs().max()) > 0.1
     assert torch.equal(kb.view(torch.int16), eng.k_cache.view(torch.int16))
+
+
+@pytest.mark.parametrize("prefix,bs", [(13, 8), (40, 16), (64, 32)])
+def test_step_marks_shared_prefix_blocks(prefix, bs):
+    """Forked sequences decoded through pa_step (the path that tells the pass
+    which leading blocks other sequences share, so that their loads stay
+    cached): the step record's counts equal the oracle model's (blocks with
+    refcount above one at the front of each table, after the step's
+    copy-on-write), and the outputs equal those of unshared copies bit for
+    bit and the oracle within tolerance."""
+    pa, runner = _pa()
+    from scenarios import fork_workload
+    res = []
+    for share in (True, False):
+        w = fork_workload(prefix, [3, 3, 3, 3], share, block_size=bs, num_kv_heads=2, num_q_heads=8,
+                          head_dim=128)
+        say("step over shared prefix", prefix, bs, share)
+        dev = runner.run_script(w, use_step=True)
+        res.append(dev.decodes[-1].out.cpu())
+        ref = oracle.run_scenario(w)
+        check_run(w, dev, ref, label=f"step prefix {prefix} share {share}")
+        eng = dev.engine
+        st = eng._ring[(eng._ri - 1) % len(eng._ring)]
+        n = len(ref.decodes[-1].seqs)
+        at = 4 * n + n * eng.stride + n + 1
+        got = st.h[at: at + n].numpy()
+        want = []
+        for s in ref.decodes[-1].seqs:
+            t = ref.bm.table(s)[: -(-ref.bm.length(s) // bs)]
+            k = 0
+            while k < len(t) and ref.bm.refcount(t[k]) > 1:
+                k += 1
+            want.append(k)
+        assert list(got) == want, (list(got), want)
+        assert (max(want) > 0) == share
+    assert torch.equal(res[0], res[1])
