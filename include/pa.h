@@ -142,6 +142,11 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
  * Errors: PA_ERR_INVALID (bad sizes, workspace too small, out_dtype not F32
  * or kv_dtype), PA_ERR_UNSUPPORTED (shape outside the supported set),
  * PA_ERR_HIP (launch failure).
+ * Cache policy: with a 16-bit cache the K/V tiles are read with the
+ * non-temporal load policy (a byte is read once per call).  A block that
+ * several sequences of the call share is then fetched once per sharer;
+ * pa_step, which knows the refcounts, keeps the caching policy for those.
+ * Results do not depend on the policy.
  * ---------------------------------------------------------------------- */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, int32_t partition_size);
@@ -351,9 +356,13 @@ pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k
  *   2. pa_bm_export of the grown tables and context lengths;
  *   3. the step record, laid out in int32 words as
  *      [slots n | copy pairs 2n | context lengths n | tables n * table_stride
- *       | tile prefix sums n + 1 | header 4 | stream plan (16-byte aligned)]
- *      (the header: copy-on-write pairs, the stream grid of the plan or 0,
- *      cut items, words in use)
+ *       | tile prefix sums n + 1 | shared blocks n | header 4
+ *       | stream plan (16-byte aligned)]
+ *      (shared blocks: how many blocks at the front of each table other
+ *      sequences also hold, i.e. have a refcount above one; the stream pass
+ *      reads their tiles with the caching load policy, every other K/V tile
+ *      with the non-temporal one; the header: copy-on-write pairs, the
+ *      stream grid of the plan or 0, cut items, words in use)
  *      (rounded up to a multiple of 4 words), goes from stage_host (pinned
  *      host memory, 16-byte aligned) to stage_dev (device memory): when the
  *      runtime maps stage_host into the device's address space, a kernel on
