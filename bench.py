@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_c2_gqa_bf16_traffic.json")
 STREAM_HOST_MARKER = b"// ==== host side: launch configuration"
 STREAM_SRC = os.path.join(ROOT, "paged_kv_cache_332_amd", "csrc", "decode_stream.hip")
+STREAM_HEADERS = [os.path.join(ROOT, "paged_kv_cache_332_amd", "csrc", h) for h in ("pa_device.h", "pa_kernels.h")]
 METRIC = "paged decode KV read GB/s (% of HBM peak) + tokens/s, batch 64 GQA bf16"
 
 
@@ -109,10 +110,13 @@ def decode_bytes(ctx, cfg, esize, out_esize=4) -> int:
 def stream_device_code_sha(hashlib) -> str:
     """Hash of the stream kernel's device code: the source text before the
     host-side marker (launch code below it does not change what a pass
-    reads or writes)."""
+    reads or writes), followed by the device headers it includes."""
     with open(STREAM_SRC, "rb") as f:
-        text = f.read()
-    return hashlib.sha256(text.split(STREAM_HOST_MARKER, 1)[0]).hexdigest()
+        text = f.read().split(STREAM_HOST_MARKER, 1)[0]
+    for h in STREAM_HEADERS:
+        with open(h, "rb") as f:
+            text += f.read()
+    return hashlib.sha256(text).hexdigest()
 
 
 def measured_traffic(kernel_name: str, config: str):
