@@ -181,7 +181,10 @@ def l2_request_model(ctx, num_kv_heads, group, head_dim, esize, block_size, grid
     touches it in the pass; the model counts those too.  Tiles are 16 tokens:
     at block size 8 a tile takes two table entries (the second only when it
     holds a context token, else the first block is read twice and its lanes
-    coalesce into half the lines); at 32 two tiles share one entry."""
+    coalesce into half the lines); at 32 two tiles share one entry.  The
+    constants mirror the kernel and the step record: tiles staged per table
+    read (224) and the tables' offset in the record (after 4 words per
+    sequence)."""
     line = 128
     ctx = np.asarray(ctx, np.int64)
     tiles = -(-ctx // 16)
