@@ -299,6 +299,12 @@ pa_status pa_bm_admit(pa_bm* bm, int64_t seq, int32_t num_tokens, int32_t reserv
 pa_status pa_bm_occupancy(const pa_bm* bm, int64_t* out);
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);      /* -1 if out of range */
 int32_t pa_bm_seq_len(const pa_bm* bm, int64_t seq);         /* -1 if unknown */
+/* Blocks at the front of the sequence's table that are also held elsewhere
+ * (refcount above one: a fork, a sharer not yet diverged, a cached prefix
+ * another prompt reuses); -1 if unknown.  Kept per sequence and walked again
+ * only after some block starts or stops being shared ([VM] §Sharing comes
+ * almost for free).  pa_step records it for the decode pass's load policy. */
+int32_t pa_bm_shared_blocks(const pa_bm* bm, int64_t seq);
 int32_t pa_bm_num_seqs(const pa_bm* bm);
 /* Free list, next allocation first; writes min(cap, num_free) ids, returns
  * num_free. */

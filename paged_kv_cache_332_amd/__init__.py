@@ -81,6 +81,7 @@ _sig("pa_swap_blocks", _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i
 _sig("pa_bm_occupancy", _i32, _vp, _pi64)
 _sig("pa_bm_refcount", _i32, _vp, _i32)
 _sig("pa_bm_seq_len", _i32, _vp, _i64)
+_sig("pa_bm_shared_blocks", _i32, _vp, _i64)
 _sig("pa_bm_num_seqs", _i32, _vp)
 _sig("pa_bm_free_list", _i32, _vp, _pi32, _i32)
 _sig("pa_bm_stats", _i32, _vp, _pi64)
@@ -436,6 +437,11 @@ class BlockManager:
 
     def seq_len(self, seq: int) -> int:
         return int(lib.pa_bm_seq_len(self._h, int(seq)))
+
+    def shared_blocks(self, seq: int) -> int:
+        """Blocks at the front of the sequence's table held elsewhere too
+        (refcount above one); -1 if unknown."""
+        return int(lib.pa_bm_shared_blocks(self._h, int(seq)))
 
     def num_seqs(self) -> int:
         return int(lib.pa_bm_num_seqs(self._h))

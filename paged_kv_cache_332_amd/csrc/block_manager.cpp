@@ -45,6 +45,10 @@ struct pa_bm {
   struct Seq {
     std::vector<int32_t> table;
     int32_t len = 0;
+    // blocks at the front of the table with refcount > 1, valid while
+    // shared_epoch equals the manager's share_epoch
+    mutable int32_t shared_len = 0;
+    mutable uint64_t shared_epoch = 0;
   };
   struct CacheEntry {
     uint64_t cid;
@@ -64,6 +68,28 @@ struct pa_bm {
   std::unordered_map<int32_t, std::list<int32_t>::iterator> evictable_at;
   uint64_t next_cid = 1;
   int64_t hit_blocks = 0, query_blocks = 0;
+  // advanced whenever a block starts or stops being shared (its refcount
+  // crosses between 1 and 2), which can change any table's shared prefix
+  uint64_t share_epoch = 1;
+
+  // refcount[b] += d, noting a change of the block's shared state
+  void rc_add(int32_t b, int32_t d) {
+    const int32_t before = refcount[b];
+    refcount[b] = before + d;
+    if ((before > 1) != (before + d > 1)) ++share_epoch;
+  }
+  // The number of blocks at the front of s's table that other holders share
+  // (walked again only after a sharing change anywhere).
+  int32_t shared_prefix(const Seq& s) const {
+    if (s.shared_epoch != share_epoch) {
+      int32_t j = 0;
+      const int32_t nb = static_cast<int32_t>(s.table.size());
+      while (j < nb && refcount[s.table[j]] > 1) ++j;
+      s.shared_len = j;
+      s.shared_epoch = share_epoch;
+    }
+    return s.shared_len;
+  }
 
   // blocks a call can get: the free stack, then the evictable cached blocks
   int64_t available() const { return static_cast<int64_t>(free_stack.size() + evictable.size()); }
@@ -89,7 +115,8 @@ struct pa_bm {
   void release(const std::vector<int32_t>& table) {
     std::vector<int32_t> cached;
     for (int32_t b : table) {
-      if (--refcount[b] == 0) {
+      rc_add(b, -1);
+      if (refcount[b] == 0) {
         if (block_key.count(b)) cached.push_back(b);
         else free_stack.push_back(b);
       }
@@ -218,8 +245,11 @@ pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t*
     } else if (bm->refcount[s.table.back()] > 1) {
       int32_t old = s.table.back();
       int32_t fresh = bm->take();
-      bm->refcount[old] -= 1;
+      bm->rc_add(old, -1);
       s.table.back() = fresh;
+      // the copy is private: a cached shared prefix ends before it at most
+      const int32_t at = static_cast<int32_t>(s.table.size()) - 1;
+      if (s.shared_len > at) s.shared_len = at;
       cow_pairs_out[2 * ncow] = old;
       cow_pairs_out[2 * ncow + 1] = fresh;
       ++ncow;
@@ -239,7 +269,7 @@ pa_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
     return pa::fail(PA_ERR_INVALID, "pa_bm_fork: unknown parent %lld or existing child %lld",
                     (long long)parent, (long long)child);
   pa_bm::Seq s = it->second;
-  for (int32_t b : s.table) bm->refcount[b] += 1;
+  for (int32_t b : s.table) bm->rc_add(b, 1);
   bm->seqs.emplace(child, std::move(s));
   return PA_OK;
 }
@@ -340,7 +370,7 @@ pa_status pa_bm_add_seq_cached(pa_bm* bm, int64_t seq, const int32_t* tokens, in
       bm->evictable.erase(at->second);
       bm->evictable_at.erase(at);
     }
-    bm->refcount[b] += 1;
+    bm->rc_add(b, 1);
     s.table.push_back(b);
   }
   for (int64_t i = static_cast<int64_t>(hits.size()); i < nb; ++i) {
@@ -425,6 +455,12 @@ int32_t pa_bm_seq_len(const pa_bm* bm, int64_t seq) {
   if (!bm) return -1;
   auto it = bm->seqs.find(seq);
   return it == bm->seqs.end() ? -1 : it->second.len;
+}
+
+int32_t pa_bm_shared_blocks(const pa_bm* bm, int64_t seq) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? -1 : bm->shared_prefix(it->second);
 }
 
 int32_t pa_bm_num_seqs(const pa_bm* bm) { return bm ? static_cast<int32_t>(bm->seqs.size()) : -1; }

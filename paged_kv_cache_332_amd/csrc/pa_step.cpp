@@ -308,15 +308,9 @@ pa_status pa_step(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* stage_host
   for (int32_t i = 0; i < n; ++i) pre[i + 1] = pre[i] + (ctx[i] + 15) / 16;
   // blocks at the front of each table that other sequences also hold (a
   // forked or cached prefix): the pass reads them more than once, so their
-  // loads keep the caching policy; the walk stops at the first private block
+  // loads keep the caching policy
   int32_t* shared = stage_host + lo.shared;
-  for (int32_t i = 0; i < n; ++i) {
-    const int32_t* row = tables + int64_t(i) * table_stride;
-    const int32_t nb = (ctx[i] + block_size - 1) / block_size;
-    int32_t j = 0;
-    while (j < nb && pa_bm_refcount(bm, row[j]) > 1) ++j;
-    shared[i] = j;
-  }
+  for (int32_t i = 0; i < n; ++i) shared[i] = pa_bm_shared_blocks(bm, seqs[i]);
   int32_t ncut = 0;
   const bool planned = grid > 0 && int64_t(num_kv_heads) * pre[n] < (int64_t(1) << 31);
   const size_t plan_words =

@@ -210,6 +210,15 @@ def _same_state(cpp: CppBM, model: BlockManagerModel):
     assert tuple(cpp.cache_stats()) == tuple(model.cache_stats())
     assert cpp.num_free() == model.num_free()
     assert tuple(cpp.stats()) == tuple(model.stats())
+    # the shared prefix the C++ manager keeps per sequence (and walks again
+    # only after a sharing change) against its definition on the model's
+    # state: leading table entries whose refcount is above one
+    for s, t in model.tables.items():
+        k = 0
+        while k < len(t) and model.rc[t[k]] > 1:
+            k += 1
+        assert cpp.m.shared_blocks(s) == k, (s, t, cpp.m.shared_blocks(s), k)
+    assert cpp.m.shared_blocks(10 ** 6) == -1
 
 
 @settings(max_examples=80, deadline=None)
@@ -485,3 +494,31 @@ def test_swap_blocks_rejects_bad_arguments(over, status):
     assert pa.lib.pa_swap_blocks(*_swap_args(**over)) == status
     if status:
         assert pa.lib.pa_last_error()
+
+
+def test_shared_blocks_follow_forks_copies_and_frees():
+    """Hand-traced sharing changes (block size 4, a 10-token prompt in blocks
+    0..2, the last one partly filled): the leading shared blocks of every
+    table after forks, a copy-on-write by one of three sharers (the partly
+    filled block stays shared by the other two), the last sharer's in-place
+    write, and frees that leave a single holder."""
+    bm = pa.BlockManager(16, 4)
+    bm.add_seq(0, 10)
+    assert bm.shared_blocks(0) == 0
+    bm.fork(0, 1)
+    bm.fork(0, 2)
+    assert [bm.shared_blocks(s) for s in (0, 1, 2)] == [3, 3, 3]
+    _, pairs = bm.append_slots([1])           # copies block 2; two sharers remain
+    assert len(pairs) == 1
+    assert [bm.shared_blocks(s) for s in (0, 1, 2)] == [3, 2, 3]
+    _, pairs = bm.append_slots([0])           # copies again; sequence 2 now holds block 2 alone
+    assert len(pairs) == 1
+    assert [bm.shared_blocks(s) for s in (0, 1, 2)] == [2, 2, 2]
+    _, pairs = bm.append_slots([2])           # the last holder writes in place
+    assert len(pairs) == 0
+    assert [bm.shared_blocks(s) for s in (0, 1, 2)] == [2, 2, 2]
+    bm.free_seq(1)
+    assert [bm.shared_blocks(s) for s in (0, 2)] == [2, 2]
+    bm.free_seq(2)
+    assert bm.shared_blocks(0) == 0
+    assert bm.shared_blocks(2) == -1
