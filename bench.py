@@ -149,24 +149,38 @@ def cpu_baseline(w, budget_s: float):
     d = ref.decodes[-1]
     cfg = w.cfg
     q = w.q_sets[d.q_index]
-    done_bytes, seqs = 0, 0
-    t0 = time.perf_counter()
-    j = 0
-    while time.perf_counter() - t0 < budget_s:
-        i = j % len(d.seqs)
-        K, V = ref.cache.gather(d.tables[i], int(d.ctx[i]))
-        oracle.decode_attention(q[d.seqs[i]], K, V, cfg.scale)
-        done_bytes += kv_bytes(np.array([d.ctx[i]]), cfg.num_kv_heads, cfg.head_dim,
-                               W_ELEM[cfg.dtype])
-        seqs += 1
-        j += 1
-    el = time.perf_counter() - t0
-    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": f"{seqs} sequences of the final decode step ({done_bytes / 1e6:.0f} MB of K/V) "
-                      f"gathered through the table and attended in float64 in {el:.1f} s; "
-                      f"host has {os.cpu_count()} cpus, affinity {len(os.sched_getaffinity(0))}",
-            "tokens_per_s": round(seqs / el, 3)}
+
+    def run(budget):
+        done_bytes, seqs = 0, 0
+        t0 = time.perf_counter()
+        j = 0
+        while time.perf_counter() - t0 < budget:
+            i = j % len(d.seqs)
+            K, V = ref.cache.gather(d.tables[i], int(d.ctx[i]))
+            oracle.decode_attention(q[d.seqs[i]], K, V, cfg.scale)
+            done_bytes += kv_bytes(np.array([d.ctx[i]]), cfg.num_kv_heads, cfg.head_dim,
+                                   W_ELEM[cfg.dtype])
+            seqs += 1
+            j += 1
+        return done_bytes, seqs, time.perf_counter() - t0
+
+    done_bytes, seqs, el = run(budget_s)
+    res = {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+           "kind": "oracle",
+           "sample": f"{seqs} sequences of the final decode step ({done_bytes / 1e6:.0f} MB of K/V) "
+                     f"gathered through the table and attended in float64 in {el:.1f} s; "
+                     f"host has {os.cpu_count()} cpus, affinity {len(os.sched_getaffinity(0))}",
+           "tokens_per_s": round(seqs / el, 3)}
+    # the same on one BLAS thread, for a quarter of the budget
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            b1, s1, e1 = run(budget_s / 4)
+        res["one_thread"] = {"value": round(b1 / e1 / 1e9, 4), "unit": "GB/s", "tokens_per_s": round(s1 / e1, 3),
+                             "sample": f"{s1} sequences in {e1:.1f} s"}
+    except Exception as e:  # pragma: no cover
+        res["one_thread"] = f"not measured: {e}"
+    return res
 
 
 W_ELEM = {"f32": 4, "f16": 2, "bf16": 2}
