@@ -426,3 +426,25 @@ def test_step_marks_shared_prefix_blocks(prefix, bs):
         assert list(got) == want, (list(got), want)
         assert (max(want) > 0) == share
     assert torch.equal(res[0], res[1])
+
+
+@pytest.mark.parametrize("n,kern", [(1024, "stream"), (1100, "auto")])
+def test_largest_batches(n, kern):
+    """The stream kernel's largest batch (1024 sequences, every length and
+    prefix sum held in LDS) and one sequence more under automatic selection,
+    which then runs the per-partition kernel: short ragged contexts, every
+    output row against the oracle."""
+    pa, runner = _pa()
+    ctx = list(np.random.default_rng(n).integers(1, 24, size=n))
+    w = W.tiny(num_seqs=n, ctx=ctx, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=8, dtype="bf16",
+               seed=3)
+    say("largest batch", n, kern)
+    ref = oracle.run_scenario(w)
+    k = pa.PA_KERNEL_STREAM if kern == "stream" else pa.PA_KERNEL_AUTO
+    dev = runner.run_script(w, kernel=k)
+    check_run(w, dev, ref, label=f"batch {n} {kern}")
+    if kern == "stream":
+        with pytest.raises(pa.PAError):
+            w2 = W.tiny(num_seqs=n + 1, ctx=ctx + [5], num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=8,
+                        dtype="bf16", seed=3)
+            runner.run_script(w2, kernel=pa.PA_KERNEL_STREAM)
