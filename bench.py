@@ -101,7 +101,7 @@ def kv_bytes(ctx: np.ndarray, hkv: int, d: int, esize: int) -> int:
 def decode_bytes(ctx, cfg, esize, out_esize=4) -> int:
     """Algorithmic bytes of one pa_decode call: K/V rows, the queries, the
     outputs, the table entries and context lengths it reads."""
-    b = cfg.num_seqs
+    b = len(ctx)
     tables = int((-(-ctx.astype(np.int64) // cfg.block_size)).sum()) * 4
     return (kv_bytes(ctx, cfg.num_kv_heads, cfg.head_dim, esize) + b * cfg.num_q_heads * cfg.head_dim * esize
             + b * cfg.num_q_heads * cfg.head_dim * out_esize + tables + 4 * b)
