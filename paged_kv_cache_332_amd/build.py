@@ -62,6 +62,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the host microbenchmark of the block manager's calls, linked to the library
+    tool = os.path.join(PKG, "bm_bench")
+    cmd = [shutil.which("g++") or "g++", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+           os.path.join(PKG, "bm_bench.cpp"), "-o", tool + ".tmp", "-L", PKG, "-lpa", "-Wl,-rpath,$ORIGIN",
+           "-Wl,--allow-shlib-undefined"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        raise RuntimeError(f"host tool build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tool + ".tmp", tool)
     if verbose:
         print(f"built {LIB}")
     return LIB

@@ -392,3 +392,116 @@ def check_bm_prefix_cache(BM, OutOfBlocks, InvalidOp):
     assert tuple(bm.cache_stats())[:2] == (0, 0) and bm.num_free() == 8
     _, hit = bm.add_seq_cached(9, A)
     assert hit == 0
+
+
+# ------------------------------------------------- accounting (waste, admission)
+def check_admit_golden(admit):
+    """Hand-worked admission cases (tests/golden/admit_hand.json): the ceiling
+    exactly reached, one block over, the reserve pushing a request over, the
+    empty request, and a length that is not a multiple of the block size."""
+    g = load_golden("admit_hand.json")
+    for free, tokens, bs, reserve, want, why in g["cases"]:
+        assert admit(free, tokens, bs, reserve) is want, why
+
+
+def check_slab_golden(Slab):
+    """Hand-traced contiguous reservations (tests/golden/
+    slab_fragmentation_hand.json): first fit, merging on release, and a
+    refusal while the free total would cover the request."""
+    g = load_golden("slab_fragmentation_hand.json")
+    s = Slab(g["capacity"])
+    ids, with_room = {}, []
+    for op in g["ops"]:
+        if op[0] == "reserve":
+            name, n = op[1], op[2]
+            ids[name] = len(ids)
+            room = s.free_slots() >= n
+            start = s.reserve(ids[name], n)
+            assert start == g["starts"][name], (name, start)
+            if start is None and room:
+                with_room.append(name)
+        else:
+            s.release(ids[op[1]])
+    assert with_room == g["refused_with_room"]
+    assert [list(h) for h in s.holes] == g["final_holes"]
+
+
+def check_slab_invariants(Slab):
+    """Random reservations and releases: the free runs and the reserved runs
+    tile the pool exactly, free runs are sorted and never touch, a request
+    is refused only when no free run is long enough, and releasing
+    everything leaves one run of the whole pool."""
+    rng = np.random.default_rng(41)
+    cap = 97
+    s = Slab(cap)
+    live = []
+    for k in range(600):
+        if live and rng.random() < 0.45:
+            s.release(live.pop(int(rng.integers(len(live)))))
+        else:
+            n = int(rng.integers(1, 20))
+            longest = max((h[1] for h in s.holes), default=0)
+            first = next((h[0] for h in s.holes if h[1] >= n), None)
+            start = s.reserve(k, n)
+            assert start == first and (start is None) == (longest < n)
+            if start is not None:
+                live.append(k)
+        cover = np.zeros(cap, np.int64)
+        for st, n in s.runs.values():
+            cover[st:st + n] += 1
+        for st, n in s.holes:
+            assert n > 0
+            cover[st:st + n] += 1
+        assert np.all(cover == 1)
+        starts = [h[0] for h in s.holes]
+        assert starts == sorted(starts)
+        assert all(a[0] + a[1] < b[0] for a, b in zip(s.holes, s.holes[1:]))
+        assert s.free_slots() == cap - sum(n for _, n in s.runs.values())
+    for rid in list(live):
+        s.release(rid)
+    assert [list(h) for h in s.holes] == [[0, cap]]
+
+
+def check_replay_golden(replay):
+    """One trace replayed by hand against contiguous runs of the request's
+    length, of the longest context, and blocks from a free list
+    (tests/golden/admission_replay_hand.json)."""
+    from fractions import Fraction
+    g = load_golden("admission_replay_hand.json")
+    ev = [tuple(e) for e in g["events"]]
+    for pol, e in g["expected"].items():
+        r = replay(ev, pol, g["capacity_tokens"], g["block_size"], g["max_len"])
+        for k in ("admitted", "refused", "refused_with_room", "peak_live"):
+            assert r[k] == e[k], (pol, k, r[k], e[k])
+        for k in ("mean_live", "reserved_unused", "used_fraction"):
+            assert abs(r[k] - float(Fraction(*e[k]))) < 1e-12, (pol, k, r[k], e[k])
+
+
+def check_replay_invariants(replay):
+    """What the pages fix about the three pools on a churning trace: blocks
+    from a free list are refused only when too few are free (never with room
+    to spare); a pool that holds every request at once refuses nothing; with
+    every request of one length, contiguous runs of that length do not
+    fragment either; reserving the longest context leaves most of each
+    reservation unused when requests are short."""
+    rng = np.random.default_rng(43)
+    n = 400
+    lens = rng.integers(1, 65, size=n)
+    life = rng.integers(1, 60, size=n)
+    ev, by = [], {}
+    for i in range(n):
+        by.setdefault(i + int(life[i]), []).append(i)
+    for t in range(n):
+        ev += [("depart", i) for i in by.get(t, [])]
+        ev.append(("arrive", t, int(lens[t])))
+    cap = 16 * 32 * 16
+    paged = replay(ev, "paged", 900, 4, 64)
+    assert paged["refused"] > 0 and paged["refused_with_room"] == 0
+    exact = replay(ev, "slab_exact", 900, 4, 64)
+    assert exact["refused_with_room"] > 0
+    for pol in ("paged", "slab_exact"):
+        assert replay(ev, pol, int(lens.sum()) + 64, 4, 64)["refused"] == 0
+    same = [e if e[0] == "depart" else ("arrive", e[1], 8) for e in ev]
+    assert replay(same, "slab_exact", 900, 4, 64)["refused_with_room"] == 0
+    mx = replay(ev, "slab_max", cap, 4, 64)
+    assert mx["reserved_unused"] > 0.4 and paged["reserved_unused"] < 0.1

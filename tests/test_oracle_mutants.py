@@ -17,12 +17,17 @@ import oracle_pins as P
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 
 
-def _mutant(module: str, old: str, new: str, count: int = 1) -> types.ModuleType:
+def _mutant(module: str, old: str, new: str, count: int = 1, pre: str = None, post: str = None,
+            env: dict = None) -> types.ModuleType:
     with open(os.path.join(ORACLE_DIR, module + ".py")) as f:
         src = f.read()
     assert src.count(old) >= count, f"mutation anchor not found: {old!r}"
     src = src.replace(old, new)
+    if pre is not None:
+        assert pre in src
+        src = src.replace(pre, post)
     mod = types.ModuleType(f"oracle_mutant_{module}")
+    mod.__dict__.update(env or {})
     exec(compile(src, f"<mutant {module}>", "exec"), mod.__dict__)
     return mod
 
@@ -145,6 +150,48 @@ def test_cache_mutant_is_caught(name, old, new):
               lambda: P.check_copy_blocks(m.PagedCacheModel)]
     checks += [lambda d=d: P.check_paged_equals_contiguous(m.PagedCacheModel, d) for d in ("bf16", "f32")]
     assert _fails(checks), name
+
+
+ACCOUNTING_MUTANTS = [
+    ("admit with strict inequality", "return need + reserve_blocks <= free_blocks", "return need + reserve_blocks < free_blocks"),
+    ("admit ignores the reserve", "return need + reserve_blocks <= free_blocks", "return need <= free_blocks"),
+    ("admit rounds blocks down", "    need = -(-num_tokens // block_size)\n    return", "    need = num_tokens // block_size\n    return"),
+    ("slab best fit", "for i, (start, length) in enumerate(self.holes):",
+     "for i, (start, length) in sorted(enumerate(self.holes), key=lambda e: e[1][1]):"),
+    ("slab needs a longer run", "            if length >= n:\n", "            if length > n:\n"),
+    ("slab never merges right", "if i + 1 < len(holes) and holes[i][0] + holes[i][1] == holes[i + 1][0]:", "if False:"),
+    ("slab never merges left", "if i > 0 and holes[i - 1][0] + holes[i - 1][1] == holes[i][0]:", "if False:"),
+    ("room judged by the longest run", "room = slab.free_slots() >= ask", "room = slab.largest_hole() >= ask"),
+    ("longest-context pool reserves the length", "ask = max_len if policy == \"slab_max\" else n", "ask = n"),
+    ("paged replay keeps a block back", "ok = admit(bm.num_free(), n, block_size, 0)", "ok = admit(bm.num_free(), n, block_size, 1)"),
+    ("refused request counted live", "            refused += 1\n", "            refused += 1\n            live[rid] = n\n"),
+]
+
+
+def _accounting_checks(m):
+    return [lambda: P.check_admit_golden(m.admit), lambda: P.check_slab_golden(m.SlabAllocator),
+            lambda: P.check_slab_invariants(m.SlabAllocator), lambda: P.check_replay_golden(m.replay_admissions),
+            lambda: P.check_replay_invariants(m.replay_admissions)]
+
+
+def _accounting_mutant(old, new):
+    # the module imports the block-manager model relatively; the mutant gets
+    # the real one
+    import oracle.block_manager as bmm
+    return _mutant("accounting", old, new, pre="from .block_manager import BlockManagerModel",
+                   post="BlockManagerModel = __bm.BlockManagerModel", env={"__bm": bmm})
+
+
+@pytest.mark.parametrize("name,old,new", ACCOUNTING_MUTANTS, ids=[m[0] for m in ACCOUNTING_MUTANTS])
+def test_accounting_mutant_is_caught(name, old, new):
+    m = _accounting_mutant(old, new)
+    assert _fails(_accounting_checks(m)), name
+
+
+def test_unmutated_accounting_passes_every_pin():
+    m = _accounting_mutant("from typing import", "from typing import")
+    for c in _accounting_checks(m):
+        c()
 
 
 @pytest.mark.parametrize("module", ["attention", "block_manager", "cache"])

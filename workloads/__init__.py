@@ -15,7 +15,9 @@ copy-on-write, long-context split-K).  Where the configuration text leaves a
 step open, the reading taken here is stated next to the code.
 
 Seeds: configuration k uses ``numpy.random.default_rng([1000 + k, s])`` with
-stream s = 0 (context lengths), 1 (pool order / churn), 2 (K), 3 (V), 4 (Q).
+stream s = 0 (context lengths), 1 (pool order / churn), 2 (K), 3 (V), 4 (Q);
+the admission trace uses streams 5 (request lengths) and 6 (lifetimes) of
+the 13B-like configuration.
 """
 from __future__ import annotations
 
@@ -27,7 +29,7 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "config", "Workload", "build", "round_to_dtype",
-    "ELEM_BYTES",
+    "ELEM_BYTES", "admission_trace",
 ]
 
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
@@ -338,3 +340,34 @@ def tiny(num_seqs=3, num_q_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
     row_start = np.concatenate([[0], np.cumsum(ctx)[:-1]]).astype(np.int64)
     ops = [("create", nb, order)] + _prefill_then_decode(ctx)
     return Workload(cfg, ctx, k, v, [q], ops, nb, row_start)
+
+
+def admission_trace(num_requests: int = 3000, mean_live: int = 256):
+    """Arrivals and departures shaped like the 13B-like MHA configuration's
+    traffic, for the waste and admission accounting.
+
+    Request i arrives at step i with a length drawn like that configuration's
+    contexts (lognormal, sigma 1, unclipped mean 512, rounded and clipped to
+    [1, 4096]) and leaves d_i steps later, d_i uniform in [1, 2 mean_live - 1]
+    (so about mean_live requests are live at once when all are admitted).  At
+    each step the departures due come first, in request order, then the
+    arrival.  Returns (events, lengths) with events ("arrive", i, length) and
+    ("depart", i); the pool it is replayed against is the configuration's own
+    (the 1.2x rule over its 256 contexts)."""
+    sigma = 1.0
+    mu = math.log(512.0) - sigma * sigma / 2.0
+    lengths = np.clip(np.rint(_rng(3, 5).lognormal(mu, sigma, size=num_requests)), 1, 4096).astype(np.int64)
+    life = _rng(3, 6).integers(1, 2 * mean_live, size=num_requests).astype(np.int64)
+    leave = np.arange(num_requests) + life
+    by_step: dict = {}
+    for i, t in enumerate(leave.tolist()):
+        by_step.setdefault(t, []).append(i)
+    events: List[tuple] = []
+    for step in range(num_requests):
+        for i in by_step.get(step, []):
+            events.append(("depart", i))
+        events.append(("arrive", step, int(lengths[step])))
+    for step in sorted(t for t in by_step if t >= num_requests):
+        for i in by_step[step]:
+            events.append(("depart", i))
+    return events, lengths
