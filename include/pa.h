@@ -393,8 +393,11 @@ pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k
  * table_stride blocks) are checked before any change.
  * Stream kernel only: wg_weights (host, num_weights =
  * pa_decode_stream_grid(...) entries, or NULL for equal shares) sets each
- * workgroup's share of the tiles (clamped to 1..65536; results do not depend
- * on it), and wave_times (pinned host or device memory, 8 * grid int32, or
+ * workgroup's share of the tiles (clamped to 1..65536).  The weights decide
+ * where items are cut between waves, and so the order in which an item's
+ * terms are summed and merged: results with different weights agree to fp32
+ * rounding, not bit for bit; the same weights and lengths give the same bits.
+ * wave_times (pinned host or device memory, 8 * grid int32, or
  * NULL) receives, for the 4 waves of each workgroup in order, the start and
  * end of the wave as the low 32 bits of the GPU's 100 MHz real-time counter
  * (compare stamps by signed difference), from which a caller can give slow

@@ -287,6 +287,10 @@ pa_status pa_step(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* stage_host
   if (wg_weights && num_weights != grid)
     return pa::fail(PA_ERR_INVALID, "%s: %d workgroup weights given, the stream kernel runs %d", fn, num_weights,
                     grid);
+  // the new tokens' rows, checked here too: nothing below may fail once the
+  // manager has changed
+  if (!k_new || !v_new || (reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15u)
+    return pa::fail(PA_ERR_INVALID, "%s: k_new and v_new must be 16-byte aligned device memory", fn);
   int32_t* d_times = nullptr;
   if (wave_times && !(d_times = device_view(wave_times, true)))
     return pa::fail(PA_ERR_INVALID, "%s: wave_times is neither pinned host nor device memory", fn);

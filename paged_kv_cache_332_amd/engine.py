@@ -65,8 +65,11 @@ def rebalance(weights: np.ndarray, stamps: np.ndarray, rate: float = 0.5, groups
     different speeds; single workgroups only add noise).  Each class's weight
     (its share of the tile list) moves towards what would have let it finish
     with the others, w <- w * (mean / class mean) ** rate; the result is
-    scaled to a mean of 1024 and kept within 64..16384.  Results of the
-    decode do not depend on the weights, only the split of the work."""
+    scaled to a mean of 1024 and kept within 64..16384.  The weights move
+    where items are cut between waves, so the decode's results change with
+    them in the last bits (fp32 rounding of a different summation order);
+    an engine with ``balance=False`` keeps equal shares and gives the same
+    bits on every run."""
     return rebalance_classes(weights, class_finish(stamps, weights.shape[0], groups), rate, groups)
 
 

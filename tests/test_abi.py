@@ -522,3 +522,45 @@ def test_shared_blocks_follow_forks_copies_and_frees():
     bm.free_seq(2)
     assert bm.shared_blocks(0) == 0
     assert bm.shared_blocks(2) == -1
+
+
+def _aligned(nbytes, align=256):
+    """A host buffer whose address is a multiple of `align` (stands in for a
+    device pointer: the call below is rejected before anything reads it)."""
+    raw = np.zeros(nbytes + align, np.uint8)
+    off = (-raw.ctypes.data) % align
+    return raw, raw.ctypes.data + off
+
+
+@pytest.mark.parametrize("bad", ["null k_new", "misaligned v_new"])
+def test_rejected_step_leaves_the_manager_unchanged(bad):
+    """pa_step validates every argument before the manager appends: a
+    rejected call (here the new tokens' rows) returns INVALID and leaves
+    lengths, tables, refcounts and counters exactly as they were."""
+    bs, hkv, hq, d, stride = 16, 2, 8, 64, 8
+    bm = pa.BlockManager(40, bs)
+    for s, n in enumerate([16, 5, 33]):
+        bm.add_seq(s, n)
+    bm.fork(0, 3)
+    seqs = np.array([0, 1, 2, 3], np.int64)
+    before = (bm.stats(), bm.export(list(seqs), stride), [bm.refcount(b) for b in range(40)])
+    words = pa.step_record_words(len(seqs), stride, hkv)
+    stage_h = np.zeros(words, np.int32)
+    keep = []
+    ptrs = {}
+    for name, nbytes in (("stage_dev", 4 * words), ("k", 40 * hkv * d * bs * 2), ("v", 40 * hkv * d * bs * 2),
+                         ("q", 4 * hq * d * 2), ("out", 4 * hq * d * 4), ("kn", 4 * hkv * d * 2),
+                         ("vn", 4 * hkv * d * 2), ("ws", 1 << 24)):
+        raw, p = _aligned(nbytes)
+        keep.append(raw)
+        ptrs[name] = p
+    kn, vn = (None, ptrs["vn"]) if bad == "null k_new" else (ptrs["kn"], ptrs["vn"] + 2)
+    st = pa.lib.pa_step(bm._h, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(seqs),
+                        stage_h.ctypes.data, ptrs["stage_dev"], words, stride, ptrs["k"], ptrs["v"], kn, vn,
+                        ptrs["q"], ptrs["out"], 0, 2, hq, hkv, d, bs, 40, 0.125, 0, ptrs["ws"], 1 << 24, 0, None,
+                        None, None, None, None, 0, None)
+    assert st == 1, pa.lib.pa_last_error()
+    assert "k_new" in pa.lib.pa_last_error().decode()
+    after = (bm.stats(), bm.export(list(seqs), stride), [bm.refcount(b) for b in range(40)])
+    assert after[0] == before[0] and after[2] == before[2]
+    assert np.array_equal(after[1][0], before[1][0]) and np.array_equal(after[1][1], before[1][1])

@@ -17,6 +17,15 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+# A second bound, relative to the output's scale: max|err| <= REL * max|ref|.
+# The kernels keep about 16 significant bits of each softmax weight (a 16-bit
+# high part plus its rounded remainder, error <= 2^-17 relative) and sum in
+# fp32, so the error tracks the output's own magnitude (measured ratios
+# 1e-6 .. 6e-6).  Over long contexts the outputs shrink (about 0.01 at 80k
+# tokens with K scaled 0.5) and the absolute bound alone would pass a dropped
+# 16-token tile or 512-token partition (output shifts of 1e-4 .. 1.2e-3); the
+# relative bound fails those by two orders of magnitude.
+REL = 1e-4
 
 
 def _pa():
@@ -36,7 +45,7 @@ def pool_bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int32).cpu().numpy().view(np.uint32)
 
 
-def check_run(w, dev, ref, tol=None, pools=True, label=""):
+def check_run(w, dev, ref, tol=None, pools=True, label="", rel=REL):
     """Compare a device replay with the oracle's replay of the same script."""
     tol = TOL[w.cfg.dtype] if tol is None else tol
     assert len(dev.appends) == len(ref.appends)
@@ -51,8 +60,10 @@ def check_run(w, dev, ref, tol=None, pools=True, label=""):
         rows = r.computed
         assert np.all(np.isfinite(out[rows])), label
         err = float(np.max(np.abs(out[rows] - r.out[rows]))) if rows else 0.0
+        scale = float(np.max(np.abs(r.out[rows]))) if rows else 0.0
         errs.append(err)
         assert err <= tol, f"{label}: max abs error {err:.3e} > {tol}"
+        assert err <= rel * scale + 1e-8, f"{label}: max abs error {err:.3e} > {rel} x max|ref| {scale:.3e}"
     if pools:
         kb, vb = ref.cache.pool_bits()
         assert np.array_equal(pool_bits(dev.engine.k_cache), kb), f"{label}: K pool bytes differ"
@@ -448,3 +459,137 @@ def test_largest_batches(n, kern):
             w2 = W.tiny(num_seqs=n + 1, ctx=ctx + [5], num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=8,
                         dtype="bf16", seed=3)
             runner.run_script(w2, kernel=pa.PA_KERNEL_STREAM)
+
+
+# ------------------------------------------- every tile counted exactly once
+def _position_coded(name=None, ctx=None, hq=64, hkv=8, d=128, bs=32, seed=0):
+    """A workload whose keys are identical within each kv head and whose
+    values encode each token's position: V[t][h][c] = (t + 5h + c) mod 128 -
+    64.  Every score of a (sequence, head) is the same number, so every
+    kernel's softmax weight is exactly 2^0 = 1 and the output is the mean of V
+    over the context (the oracle's identical-keys closed form).  The values
+    are small integers, so every partial sum is an integer below 2^24 and
+    exact in fp32 whatever the order: the kernels' only rounding is the final
+    division (<= 2 ulp of |out| <= 64, under 2e-5).  A tile dropped or counted
+    twice moves some output element by at least 16 x 63.5 / ctx (6.8e-3 at
+    131072 tokens), one token past the context by at least 4.8e-4."""
+    if name is not None:
+        w = W.build(name, values=False)
+        hq, hkv, d = w.cfg.num_q_heads, w.cfg.num_kv_heads, w.cfg.head_dim
+    else:
+        w = W.tiny(num_seqs=len(ctx), num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs, dtype="bf16",
+                   ctx=ctx, seed=seed)
+    rng = np.random.default_rng([901, seed])
+    R = int(np.sum(w.ctx))
+    kvec = W.round_to_dtype(rng.standard_normal((1, hkv, d), dtype=np.float32), "bf16")
+    w.k_rows = np.broadcast_to(kvec, (R, hkv, d))
+    pos = np.concatenate([np.arange(int(n), dtype=np.int64) for n in w.ctx])
+    v = np.empty((R, hkv, d), np.float32)
+    code = 5 * np.arange(hkv)[None, :, None] + np.arange(d)[None, None, :]
+    for i in range(0, R, 1 << 16):
+        v[i:i + (1 << 16)] = (pos[i:i + (1 << 16), None, None] + code) % 128 - 64
+    w.v_rows = v
+    w.q_sets = [W.round_to_dtype(rng.standard_normal((len(w.ctx), hq, d), dtype=np.float32), "bf16")]
+    return w
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("case", ["c5_long_splitk", "mixed_bs16", "mixed_bs8"])
+def test_every_tile_counted_once(case):
+    """Position-coded values with identical keys (see _position_coded) at the
+    long-context configuration's full size (8 sequences of 32k..131k tokens,
+    64 query / 8 kv heads, block size 32, 512-token partitions) and on ragged
+    mixes at block sizes 16 and 8: the fused step (stream kernel with the
+    host plan), pa_decode's stream kernel without a plan, and the 512-token
+    partition kernels (matrix-core and vector) with their log-sum-exp merge
+    each give the oracle's result within 1e-4, so no tile is dropped, doubled
+    or read past the context on any decode path."""
+    pa, runner = _pa()
+    if case == "c5_long_splitk":
+        w = _position_coded("c5_long_splitk")
+    elif case == "mixed_bs16":
+        w = _position_coded(ctx=[70000, 1, 17, 40000, 33, 2049, 512, 511], hq=32, hkv=8, bs=16, seed=1)
+    else:
+        w = _position_coded(ctx=[20000, 9, 3000, 1, 15000, 16], hq=16, hkv=4, d=64, bs=8, seed=2)
+    say("position coded", case, "contexts", [int(x) for x in w.ctx])
+    scale = w.cfg.scale
+    want = []
+    q = w.q_sets[0]
+    for i, n in enumerate(w.ctx):
+        rows = w.row_of(i, np.arange(int(n)))
+        want.append(oracle.decode_attention(q[i], w.k_rows[rows], w.v_rows[rows], scale))
+    want = np.stack(want)
+    dev = runner.run_script(w, partition_size=512, use_step=True)
+    eng = dev.engine
+    seqs = dev.decodes[-1].seqs
+    qd = dev.q_dev[0][torch.tensor(seqs, device="cuda")].contiguous()
+    outs = {"step stream": dev.decodes[-1].out}
+    for label, kern in (("stream", pa.PA_KERNEL_STREAM), ("mfma 512", pa.PA_KERNEL_MFMA),
+                        ("valu 512", pa.PA_KERNEL_VALU)):
+        outs[label] = eng.decode(seqs, qd, partition_size=512, kernel=kern)
+    torch.cuda.synchronize()
+    for label, o in outs.items():
+        err = float(np.max(np.abs(o.double().cpu().numpy() - want)))
+        say("position coded", case, label, "max abs error", err)
+        assert err <= 1e-4, f"{case} {label}: max abs error {err:.3e}"
+    del dev, eng
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("kern", ["mfma", "valu"])
+def test_long_context_partition_kernels(kern):
+    """The long-context configuration at full size through the 512-token
+    partition kernels and the log-sum-exp merge (pa_decode with an explicit
+    kernel, on the pools the fused step built): every output row within the
+    absolute and the relative bound of the oracle."""
+    pa, runner = _pa()
+    w, ref = _config("c5_long_splitk")
+    say("c5 partition kernels", kern)
+    dev = runner.run_script(w, partition_size=512, use_step=True)
+    eng = dev.engine
+    d = dev.decodes[-1]
+    q = dev.q_dev[d.q_index][torch.tensor(d.seqs, device="cuda")].contiguous()
+    out = eng.decode(d.seqs, q, partition_size=512, kernel=KERNELS[kern])
+    torch.cuda.synchronize()
+    r = ref.decodes[-1]
+    got = out.double().cpu().numpy()
+    err = float(np.max(np.abs(got[r.computed] - r.out[r.computed])))
+    scale = float(np.max(np.abs(r.out[r.computed])))
+    say("c5", kern, "max abs error", err, "max|ref|", scale)
+    assert err <= TOL["bf16"] and err <= REL * scale
+    del dev, eng
+    torch.cuda.empty_cache()
+
+
+def test_weights_change_only_rounding():
+    """The stream kernel's workgroup weights move the cuts between waves,
+    hence the summation and merge order: outputs under very different
+    weights agree to rounding (far inside the oracle tolerance), and the same
+    weights give the same bits again."""
+    pa, runner = _pa()
+    ctx = [3000, 17, 900, 4100, 1, 250, 1024, 2000, 33, 700]
+    hq, hkv, d = 32, 8, 128
+    w = W.tiny(num_seqs=len(ctx), dtype="bf16", seed=29, ctx=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+               block_size=16)
+    g = pa.pa_decode_stream_grid(len(ctx), hq, hkv, d)
+    ref = oracle.run_scenario(w)
+
+    def run(kind):
+        def set_weights(eng):
+            wt = eng.weights(len(ctx), hq)
+            if kind == "random":
+                wt[:] = np.random.default_rng(8).integers(1, 65537, size=g)
+            elif kind == "ramp":
+                wt[:] = 1 + 64 * np.arange(g)
+        dev = runner.run_script(w, use_step=True, kernel=pa.PA_KERNEL_STREAM, on_engine=set_weights)
+        check_run(w, dev, ref, label=f"weights {kind}")
+        return dev.decodes[-1].out.cpu()
+
+    outs = {k: run(k) for k in ("equal", "random", "ramp", "equal again")}
+    assert torch.equal(outs["equal"], outs["equal again"])
+    top = float(outs["equal"].abs().max())
+    for k in ("random", "ramp"):
+        diff = float((outs[k] - outs["equal"]).abs().max())
+        say("weights", k, "max |difference| to equal shares", diff, "max|out|", top)
+        assert diff <= 1e-4 * top
