@@ -162,6 +162,31 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_
                     int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * pa_decode_noalloc — pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments without the workspace, the same
+ * kernels (automatic selection) and results.  The workspace is a static
+ * array of PA_DECODE_SCRATCH_BYTES in device memory, one per device, set up
+ * on the first call on that device and held until the process ends; the call
+ * itself allocates nothing.  Its contents need no clearing (every byte a
+ * call reads, the same call wrote first).  Every call on one device shares
+ * that device's array: calls that may overlap on one device (different
+ * streams, or host threads) race and must be ordered by the caller.
+ * Errors: those of pa_decode; PA_ERR_INVALID when the call needs more
+ * workspace than the array holds (every stream-kernel shape fits; partition
+ * kernels need B x Hq x ceil(max_ctx / partition) x (D + 2) x 4 bytes);
+ * PA_ERR_HIP when the array's device address cannot be obtained.
+ * ---------------------------------------------------------------------- */
+#define PA_DECODE_SCRATCH_BYTES (32u << 20)
+
+pa_status pa_decode_noalloc(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                            const void* v_cache, pa_dtype kv_dtype, const int32_t* block_tables,
+                            int32_t table_stride, const int32_t* context_lens, int32_t max_context_len,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
+                            void* stream);
+
 /* pa_decode with an explicit kernel choice (for measurement): PA_KERNEL_VALU
  * supports every shape above; PA_KERNEL_MFMA and PA_KERNEL_STREAM need a
  * 16-bit kv_dtype (STREAM ignores partition_size). */

@@ -23,7 +23,7 @@ __all__ = [
     "PA_PHASE_PASS", "PA_PHASE_MERGE", "PA_PHASE_ALL",
     "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
     "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version", "pa_step",
-    "pa_decode_stream_grid", "step_record_words", "pa_stream_plan", "pa_prefill", "pa_swap_blocks", "pa_step_layer",
+    "pa_decode_stream_grid", "pa_decode_noalloc", "step_record_words", "pa_stream_plan", "pa_prefill", "pa_swap_blocks", "pa_step_layer",
     "STEP_KV", "STEP_PASS", "STEP_MERGE", "STEP_ALL",
 ]
 
@@ -60,6 +60,7 @@ _DECODE_ARGS = [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32
 _sig("pa_decode", _i32, *_DECODE_ARGS)
 _sig("pa_decode_variant", _i32, *_DECODE_ARGS, _i32)
 _sig("pa_decode_phase", _i32, *_DECODE_ARGS, _i32, _i32)
+_sig("pa_decode_noalloc", _i32, *_DECODE_ARGS[:18], _vp)
 _sig("pa_prefill", _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
      _i32, _i32, _f32, _vp)
 _sig("pa_bm_create", _vp, _i32, _i32, _pi32)
@@ -208,6 +209,21 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
               partition_size: int = 0, workspace=None, stream=None) -> None:
     pa_decode_variant(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                       partition_size, workspace, stream, PA_KERNEL_AUTO)
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int, scale: float,
+                      partition_size: int = 0, stream=None) -> None:
+    """pa_decode with the library's static device scratch as its workspace
+    (no allocation; see pa_decode_noalloc in pa.h)."""
+    n, hkv, d, bs = _pool_dims(k_cache, v_cache)
+    b, hq, dq = q.shape
+    assert dq == d and tuple(out.shape) == (b, hq, d) and q.is_contiguous() and out.is_contiguous()
+    assert block_tables.is_contiguous() and block_tables.dim() == 2 and block_tables.shape[0] == b
+    assert context_lens.is_contiguous() and context_lens.numel() == b
+    _check(lib.pa_decode_noalloc(out.data_ptr(), torch_dtype_code(out.dtype), q.data_ptr(), k_cache.data_ptr(),
+                                 v_cache.data_ptr(), torch_dtype_code(k_cache.dtype), block_tables.data_ptr(),
+                                 int(block_tables.shape[1]), context_lens.data_ptr(), int(max_context_len),
+                                 b, hq, hkv, d, bs, n, float(scale), int(partition_size), _stream(stream)))
 
 
 def pa_swap_blocks(k_cache, v_cache, host_k, host_v, blocks, to_host: bool, stream=None) -> None:

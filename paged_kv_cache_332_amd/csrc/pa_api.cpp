@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "pa_internal.h"
@@ -473,3 +474,80 @@ pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------- allocation-free decode
+namespace {
+
+// The decode workspace of pa_decode_noalloc: a fixed array in device memory,
+// one copy per device, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device array: host code passes the
+// device address hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kScratchBytes = PA_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+
+// Device address of the current device's scratch copy (null with *err set
+// when the lookup fails).
+void* scratch_on_current_device(hipError_t* err) {
+  static std::once_flag once[kScratchDevices];
+  static void* ptr[kScratchDevices];
+  static hipError_t status[kScratchDevices];
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kScratchDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev] { status[dev] = hipGetSymbolAddress(&ptr[dev], HIP_SYMBOL(scratch)); });
+  *err = status[dev];
+  return status[dev] == hipSuccess ? ptr[dev] : nullptr;
+}
+
+// Workspace bytes the kernel pa_decode picks for these arguments uses (the
+// stream kernel's per-wave records, or the partition kernels' partials when
+// a sequence spans several partitions).
+size_t selected_workspace_bytes(pa_dtype kv_dtype, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len, int32_t block_size, int32_t partition_size) {
+  if (kv_dtype != PA_F32) {
+    const pa::StreamPlan sp = pa::stream_plan(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, head_dim);
+    if (sp.ok) return sp.ml_bytes + sp.acc_bytes;
+  }
+  const int32_t part = partition_size ? partition_size
+                                      : pa_decode_default_partition(num_seqs, num_kv_heads, max_context_len,
+                                                                    block_size);
+  if (part <= 0) return 0;  // rejected by the validation that follows
+  return pa::partition_ws_bytes(num_seqs, num_q_heads, head_dim, std::max(1, pa::ceil_div(max_context_len, part)));
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode_noalloc(void* out, pa_dtype out_dtype, const void* q, const void* k_cache,
+                                       const void* v_cache, pa_dtype kv_dtype, const int32_t* block_tables,
+                                       int32_t table_stride, const int32_t* context_lens, int32_t max_context_len,
+                                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
+                                       void* stream) {
+  const char* fn = "pa_decode_noalloc";
+  // the sizes the workspace depends on; anything else is left to pa_decode's
+  // own validation below
+  if (num_seqs > 0 && num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 && head_dim > 0 &&
+      max_context_len >= 0 && block_size > 0 && partition_size >= 0) {
+    const size_t need = selected_workspace_bytes(kv_dtype, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                 max_context_len, block_size, partition_size);
+    if (need > kScratchBytes)
+      return pa::fail(PA_ERR_INVALID,
+                      "%s: this call needs %zu bytes of decode workspace, more than the %zu bytes of static "
+                      "scratch (use pa_decode with a workspace)",
+                      fn, need, kScratchBytes);
+  }
+  hipError_t e = hipSuccess;
+  void* ws = scratch_on_current_device(&e);
+  if (!ws) return pa::fail(PA_ERR_HIP, "%s: address of the static scratch: %s", fn, hipGetErrorString(e));
+  return pa::decode_impl(out, out_dtype, q, k_cache, v_cache, kv_dtype, block_tables, table_stride, context_lens,
+                         max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                         scale, partition_size, ws, kScratchBytes, stream, PA_KERNEL_AUTO, 3, nullptr);
+}
