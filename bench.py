@@ -98,6 +98,19 @@ def kv_bytes(ctx: np.ndarray, hkv: int, d: int, esize: int) -> int:
     return int(ctx.astype(np.int64).sum()) * hkv * d * 2 * esize
 
 
+def unique_kv_bytes(tables: np.ndarray, ctx: np.ndarray, block_size: int, hkv: int, d: int, esize: int) -> int:
+    """K+V bytes of the distinct physical blocks a decode reads: a block that
+    several sequences share counts once, with the most tokens any of them
+    uses (the duplication the pages say sharing removes)."""
+    used = {}
+    for row, n in zip(np.asarray(tables), np.asarray(ctx, np.int64)):
+        nb = -(-int(n) // block_size)
+        for j in range(nb):
+            b = int(row[j])
+            used[b] = max(used.get(b, 0), min(block_size, int(n) - j * block_size))
+    return sum(used.values()) * hkv * d * 2 * esize
+
+
 def decode_bytes(ctx, cfg, esize, out_esize=4) -> int:
     """Algorithmic bytes of one pa_decode call: K/V rows, the queries, the
     outputs, the table entries and context lengths it reads."""
@@ -119,20 +132,25 @@ def stream_device_code_sha(hashlib) -> str:
     return hashlib.sha256(text).hexdigest()
 
 
-def measured_traffic(kernel_name: str, config: str):
-    """HBM bytes per launch from the committed counter profile, or None when
-    there is none for this kernel and workload or the kernel source has
-    changed since."""
+def measured_traffic(kernel_name: str, config: str, bytes_per_launch: int):
+    """HBM bytes per launch from the committed counter profile: (traffic,
+    ratio).  ``ratio`` = counted bytes / algorithmic bytes of the counted
+    launches, whenever the record is for this kernel source and workload;
+    ``traffic`` = the counted bytes only when the counted launches moved the
+    same algorithmic bytes as this line's launch (the same steps and warm-up
+    of the same workload), else None."""
     import hashlib
     if kernel_name != "stream" or not os.path.exists(TRAFFIC_FILE):
-        return None
+        return None, None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
-    if rec.get("config") != config:
-        return None
-    if rec.get("source_sha256") != stream_device_code_sha(hashlib):
-        return None
-    return int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+    if rec.get("config") != config or rec.get("source_sha256") != stream_device_code_sha(hashlib):
+        return None, None
+    counted = int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+    algo = int(rec.get("algorithmic_bytes_per_launch", 0))
+    if algo <= 0:
+        return None, None
+    return (counted if algo == int(bytes_per_launch) else None), round(counted / algo, 4)
 
 
 def cpu_baseline(w, budget_s: float):
@@ -615,6 +633,15 @@ def main():
     burst_us = b0.elapsed_time(b1) * 1e3 / args.burst
     burst_bytes = decode_bytes(step_ctx[-1], cfg, esize)
     achieved = float(burst_bytes / (burst_us * 1e-6) / 1e9)
+    # the whole of pa_decode: the pass and the merge of cut items, back to back
+    for rep in range(2):
+        b0.record(stream)
+        for _ in range(args.burst):
+            eng.step_layer(eng.k_cache, eng.v_cache, None, None, q, out, phases=pa.STEP_PASS | pa.STEP_MERGE,
+                           stream=stream)
+        b1.record(stream)
+    torch.cuda.synchronize()
+    decode_us = b0.elapsed_time(b1) * 1e3 / args.burst
 
     # the same pass with a cold Infinity Cache: 1 GiB read before each one, so
     # the cache holds clean lines of another buffer (a write would leave dirty
@@ -632,8 +659,17 @@ def main():
             cold_us.append(c0.elapsed_time(c1) * 1e3)
         del scrub
     value = kv_total / elapsed / 1e9
+    # bytes a shared prefix adds to the logical count (constant over the
+    # timed steps: they append to private blocks only)
+    last_tab, last_ctx = eng.last_tables.copy(), eng.last_ctx.copy()
+    dup = kv_bytes(last_ctx, cfg.num_kv_heads, cfg.head_dim, esize) - unique_kv_bytes(
+        last_tab, last_ctx, cfg.block_size, cfg.num_kv_heads, cfg.head_dim, esize)
     kname = ("stream" if kernel in (pa.PA_KERNEL_AUTO, pa.PA_KERNEL_STREAM) and cfg.dtype != "f32"
              else args.kernel if args.kernel != "auto" else "valu")
+    traffic, traffic_ratio = measured_traffic(kname, args.config, burst_bytes)
+    partition = ("stream: equal tile shares per wave, no fixed partition" if kname == "stream" else
+                 part or pa.pa_decode_default_partition(cfg.num_seqs, cfg.num_kv_heads, int(step_ctx[-1].max()),
+                                                        cfg.block_size))
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -649,20 +685,25 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "batch": cfg.num_seqs, "q_heads": cfg.num_q_heads,
                    "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim, "block_size": cfg.block_size,
-                   "ctx_mean": round(float(np.mean(step_ctx[0])), 1), "partition": part or
-                   pa.pa_decode_default_partition(cfg.num_seqs, cfg.num_kv_heads, int(step_ctx[-1].max()),
-                                                  cfg.block_size),
+                   "ctx_mean": round(float(np.mean(step_ctx[0])), 1), "partition": partition,
                    "kernel": args.kernel, "balance": eng.balance, "pool_order": args.pool_order,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(cfg.num_seqs * args.steps / elapsed, 1),
+        "kv_unique_GBps": round((kv_total - args.steps * dup) / elapsed / 1e9, 2),
+        "kv_unique_note": "K/V bytes of distinct physical blocks per step / step time (equal to value "
+                          "when no block is shared)",
         "host_us_per_step": round(float(np.median(host_s)) * 1e6, 1),
         "host_us_per_step_max": round(float(np.max(host_s)) * 1e6, 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "pa_decode pass (" + kname + ")",
                      "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(kname, args.config), "avg_launch_us": round(burst_us, 2),
+                     "traffic": traffic, "traffic_ratio": traffic_ratio, "avg_launch_us": round(burst_us, 2),
                      "bytes_per_launch": int(burst_bytes), "timed_launches": args.burst,
+                     "decode_frac": round(burst_bytes / (decode_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "decode": {"avg_us": round(decode_us, 2),
+                                "GBps": round(burst_bytes / (decode_us * 1e-6) / 1e9, 2),
+                                "note": "pass + merge of cut items (all of pa_decode), back to back"},
                      "cold": None if not cold_us else {
                          "median_us": round(float(np.median(cold_us)), 2),
                          "GBps": round(burst_bytes / (float(np.median(cold_us)) * 1e-6) / 1e9, 2),

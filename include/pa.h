@@ -453,6 +453,16 @@ pa_status pa_step_layer(const int32_t* stage_host, int32_t* stage_dev, int32_t n
                         void* workspace, size_t workspace_bytes, pa_kernel kernel, void* stream, int32_t phases,
                         void* pass_begin, void* pass_end, int32_t* wave_times);
 
+/* Load-balance feedback for pa_step's wg_weights, from the wave_times of a
+ * completed stream pass: out[c] (host, `classes` entries) receives the mean
+ * finish time of the workgroups b with b % classes == c, a workgroup
+ * finishing at the last end stamp of its four waves, counted from the
+ * earliest start stamp of the pass (signed 32-bit differences of the
+ * 100 MHz counter, in its ticks).  Workgroups are dealt to the GPU's dies in
+ * turn, so with classes = 8 these are the dies' finish times.  INVALID for
+ * null pointers or non-positive sizes. */
+pa_status pa_stream_class_finish(const int32_t* wave_times, int32_t grid, int32_t classes, double* out);
+
 /* Int32 words of a pa_step record for up to max_seqs sequences (0 for bad
  * sizes). */
 size_t pa_step_record_words(int32_t max_seqs, int32_t table_stride, int32_t num_kv_heads);

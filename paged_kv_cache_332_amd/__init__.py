@@ -23,7 +23,8 @@ __all__ = [
     "PA_PHASE_PASS", "PA_PHASE_MERGE", "PA_PHASE_ALL",
     "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
     "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version", "pa_step",
-    "pa_decode_stream_grid", "pa_decode_noalloc", "step_record_words", "pa_stream_plan", "pa_prefill", "pa_swap_blocks", "pa_step_layer",
+    "pa_decode_stream_grid", "pa_decode_noalloc", "step_record_words", "step_args", "step_call",
+    "stream_class_finish", "pa_stream_plan", "pa_prefill", "pa_swap_blocks", "pa_step_layer",
     "STEP_KV", "STEP_PASS", "STEP_MERGE", "STEP_ALL",
 ]
 
@@ -93,6 +94,7 @@ _sig("pa_decode_stream_grid", _i32, _i32, _i32, _i32, _i32)
 _sig("pa_step_layer", _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
      _i32, _f32, _i32, _vp, _sz, _i32, _vp, _i32, _vp, _vp, _vp)
 _sig("pa_step_record_words", _sz, _i32, _i32, _i32)
+_sig("pa_stream_class_finish", _i32, _vp, _i32, _i32, _vp)
 _sig("pa_stream_plan", _i64, _pi32, _i32, _i32, _i32, _pi32, _pi32, _sz, _pi32)
 
 
@@ -285,6 +287,40 @@ def pa_step(bm: "BlockManager", seqs_i64: np.ndarray, stage_host, stage_dev, tab
                        0 if wg_weights is None else int(wg_weights.shape[0]),
                        None if wave_times is None else wave_times.data_ptr()))
     return int(max_ctx.value)
+
+
+def step_args(bm: "BlockManager", seqs_i64: np.ndarray, table_stride: int, k_cache, v_cache, k_new, v_new, q, out,
+              scale: float, partition_size: int, workspace, kernel: int, stream, wg_weights=None) -> list:
+    """pa_step's arguments as a list for ``step_call``, for callers that
+    repeat one step shape: the step record (3, 4 and 5), the pass events (26,
+    27) and the wave stamps (31) are set per call; entry 28 points at a
+    c_int32 that receives the longest context.  ``seqs_i64`` and
+    ``wg_weights`` must stay alive (and in place) while the list is used."""
+    n_, hkv, d, bs = _pool_dims(k_cache, v_cache)
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(),
+                                                          workspace.numel() * workspace.element_size())
+    max_ctx = ctypes.c_int32(0)
+    return [bm._h, seqs_i64.ctypes.data_as(_pi64), int(seqs_i64.shape[0]), None, None, 0, int(table_stride),
+            k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), out.data_ptr(),
+            torch_dtype_code(out.dtype), torch_dtype_code(k_cache.dtype), int(q.shape[1]), hkv, d, bs, n_,
+            float(scale), int(partition_size), ws_ptr, ws_bytes, int(kernel), _stream(stream), None, None,
+            ctypes.pointer(max_ctx), None if wg_weights is None else wg_weights.ctypes.data_as(_pi32),
+            0 if wg_weights is None else int(wg_weights.shape[0]), None]
+
+
+def step_call(args: list) -> int:
+    """pa_step on an argument list from ``step_args``; returns the longest
+    context."""
+    _check(lib.pa_step(*args))
+    return int(args[28].contents.value)
+
+
+def stream_class_finish(wave_times, grid: int, classes: int, out: np.ndarray) -> np.ndarray:
+    """Mean finish time per workgroup class of a completed stream pass (see
+    pa_stream_class_finish in pa.h) into ``out`` (float64, ``classes``)."""
+    ptr = wave_times if isinstance(wave_times, int) else wave_times.data_ptr()
+    _check(lib.pa_stream_class_finish(ptr, int(grid), int(classes), out.ctypes.data))
+    return out
 
 
 STEP_KV, STEP_PASS, STEP_MERGE, STEP_ALL = 1, 2, 4, 7

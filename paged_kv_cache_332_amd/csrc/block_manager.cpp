@@ -49,6 +49,7 @@ struct pa_bm {
     // shared_epoch equals the manager's share_epoch
     mutable int32_t shared_len = 0;
     mutable uint64_t shared_epoch = 0;
+    uint64_t batch_mark = 0;  // the append batch that last listed this sequence
   };
   struct CacheEntry {
     uint64_t cid;
@@ -71,6 +72,13 @@ struct pa_bm {
   // advanced whenever a block starts or stops being shared (its refcount
   // crosses between 1 and 2), which can change any table's shared prefix
   uint64_t share_epoch = 1;
+  // per-append-batch scratch: the count a last block will have once the
+  // batch's earlier copies are done, valid where batch_rc_mark[b] equals
+  // the batch number
+  uint64_t batch = 0;
+  std::vector<uint64_t> batch_rc_mark;
+  std::vector<int32_t> batch_rc;
+  std::vector<Seq*> batch_seqs;
 
   // refcount[b] += d, noting a change of the block's shared state
   void rc_add(int32_t b, int32_t d) {
@@ -209,27 +217,34 @@ pa_status pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t*
   if (!bm || n < 0 || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)) || !num_cow_out)
     return pa::fail(PA_ERR_INVALID, "pa_bm_append_slots: bad arguments");
   // Validate and count the fresh blocks first so the call is all-or-nothing.
-  std::vector<pa_bm::Seq*> ptr(n);
-  std::unordered_map<int32_t, int32_t> rc_after;  // counts of last blocks during the batch
-  std::unordered_map<int64_t, char> seen;
+  const uint64_t mark = ++bm->batch;
+  if (bm->batch_rc_mark.size() != size_t(bm->num_blocks)) {
+    bm->batch_rc_mark.assign(size_t(bm->num_blocks), 0);
+    bm->batch_rc.assign(size_t(bm->num_blocks), 0);
+  }
+  std::vector<pa_bm::Seq*>& ptr = bm->batch_seqs;
+  ptr.resize(size_t(n));
   int64_t need = 0;
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end())
       return pa::fail(PA_ERR_INVALID, "pa_bm_append_slots: unknown sequence %lld", (long long)seqs[i]);
-    if (!seen.emplace(seqs[i], 1).second)
+    if (it->second.batch_mark == mark)
       return pa::fail(PA_ERR_INVALID, "pa_bm_append_slots: sequence %lld repeated", (long long)seqs[i]);
+    it->second.batch_mark = mark;
     ptr[i] = &it->second;
     const pa_bm::Seq& s = it->second;
     if (s.len % bm->block_size == 0) {
       ++need;
     } else {
-      int32_t last = s.table.back();
-      auto f = rc_after.find(last);
-      int32_t c = f == rc_after.end() ? bm->refcount[last] : f->second;
-      if (c > 1) {
+      const int32_t last = s.table.back();
+      if (bm->batch_rc_mark[last] != mark) {
+        bm->batch_rc_mark[last] = mark;
+        bm->batch_rc[last] = bm->refcount[last];
+      }
+      if (bm->batch_rc[last] > 1) {
         ++need;
-        rc_after[last] = c - 1;
+        --bm->batch_rc[last];
       }
     }
   }

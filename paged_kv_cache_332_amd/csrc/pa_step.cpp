@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <vector>
 
@@ -50,6 +51,17 @@ int32_t* device_view(const int32_t* p, bool allow_device) {
 }
 
 constexpr size_t kHeaderWords = 4;
+
+// floor(num / den) for 0 <= num < 2^62, den > 0: the quotient in double
+// precision is within a few units of the exact one (num may exceed 2^53), and
+// exact 64-bit products correct it (a hardware 64-bit division costs tens of
+// cycles, and a plan takes one per workgroup).
+inline int64_t floor_div(int64_t num, int64_t den) {
+  int64_t q = static_cast<int64_t>(static_cast<double>(num) / static_cast<double>(den));
+  while (q > 0 && q * den > num) --q;
+  while ((q + 1) * den <= num) ++q;
+  return q;
+}
 
 // Word where the cut-item entries start in a plan for `grid` workgroups
 // (after the 4 grid + 1 wave starts, rounded up to 4 words).
@@ -181,21 +193,38 @@ size_t build_plan(int32_t* out, const int32_t* pre, int32_t n, int32_t hkv, int3
   const int64_t total = int64_t(hkv) * pre[n];
   const int64_t nw = int64_t(grid) * 4;
   int32_t* S = out;
+  // (per-thread scratch, bound once: each use of a thread_local object in a
+  // shared library can cost a call to look up its address)
+  static thread_local std::vector<int64_t> wts_tls;
+  static thread_local std::vector<int32_t> waves_tls;
+  std::vector<int64_t>& wts = wts_tls;
+  std::vector<int32_t>& waves = waves_tls;
+  wts.resize(size_t(grid));
   int64_t all = 0;
-  for (int32_t b = 0; b < grid; ++b) all += weights ? std::clamp<int64_t>(weights[b], 1, 1 << 16) : 1;
-  int64_t before = 0;
   for (int32_t b = 0; b < grid; ++b) {
-    const int64_t wb = weights ? std::clamp<int64_t>(weights[b], 1, 1 << 16) : 1;
-    const int64_t a0 = total * before / all;
-    const int64_t a1 = total * (before + wb) / all;
-    for (int k = 0; k < 4; ++k) S[4 * b + k] = static_cast<int32_t>(a0 + (a1 - a0) * k / 4);
-    before += wb;
+    wts[b] = weights ? std::clamp<int64_t>(weights[b], 1, 1 << 16) : 1;
+    all += wts[b];
+  }
+  // workgroup b starts at floor(total * (weights before b) / all); each
+  // boundary is computed once and ends one workgroup and starts the next
+  int64_t before = 0, a0 = 0;
+  for (int32_t b = 0; b < grid; ++b) {
+    before += wts[b];
+    const int64_t a1 = floor_div(total * before, all);
+    for (int k = 0; k < 4; ++k) S[4 * b + k] = static_cast<int32_t>(a0 + (((a1 - a0) * k) >> 2));
+    a0 = a1;
   }
   S[nw] = static_cast<int32_t>(total);
-  // items in tile order, with the wave holding their first and last tile
-  static thread_local std::vector<int32_t> entries, waves;
-  entries.clear();
-  waves.clear();
+  // items in tile order, with the wave holding their first and last tile;
+  // entries go straight to their place, the waves they list to scratch
+  // (every cut item lists its waves, adjacent items share one: at most
+  // nw + items in all)
+  const size_t at = plan_entries(grid);
+  std::fill(out + nw + 1, out + at, 0);
+  int32_t* ent = out + at;
+  waves.resize(size_t(nw) + size_t(n) * hkv + 1);
+  int32_t* wl = waves.data();
+  size_t nwl = 0, ncut = 0;
   int64_t w = 0;  // the last wave starting at or before the current tile
   for (int32_t s = 0; s < n; ++s) {
     const int64_t nt = pre[s + 1] - pre[s];
@@ -206,30 +235,29 @@ size_t build_plan(int32_t* out, const int32_t* pre, int32_t n, int32_t hkv, int3
       int64_t wh = w;
       while (wh + 1 < nw && S[wh + 1] <= gs + nt - 1) ++wh;
       if (wh != w) {
-        const size_t off = waves.size();
-        for (int64_t x = w; x <= wh; ++x)
-          if (S[x] < S[x + 1]) waves.push_back(static_cast<int32_t>(x));
-        const int32_t cnt = static_cast<int32_t>(waves.size() - off);
-        const int32_t e[8] = {static_cast<int32_t>(2 * (int64_t(s) * hkv + h) + (S[w] < gs ? 1 : 0)),
-                              cnt,
-                              static_cast<int32_t>(off),
-                              waves[off],
-                              cnt > 1 ? waves[off + 1] : 0,
-                              cnt > 2 ? waves[off + 2] : 0,
-                              cnt > 3 ? waves[off + 3] : 0,
-                              0};
-        entries.insert(entries.end(), e, e + 8);
+        const size_t off = nwl;
+        for (int64_t x = w; x <= wh; ++x) {  // non-empty waves only
+          wl[nwl] = static_cast<int32_t>(x);
+          nwl += S[x] < S[x + 1];
+        }
+        const int32_t cnt = static_cast<int32_t>(nwl - off);
+        int32_t* e = ent + 8 * ncut;
+        e[0] = static_cast<int32_t>(2 * (int64_t(s) * hkv + h) + (S[w] < gs ? 1 : 0));
+        e[1] = cnt;
+        e[2] = static_cast<int32_t>(off);
+        e[3] = wl[off];
+        e[4] = cnt > 1 ? wl[off + 1] : 0;
+        e[5] = cnt > 2 ? wl[off + 2] : 0;
+        e[6] = cnt > 3 ? wl[off + 3] : 0;
+        e[7] = 0;
+        ++ncut;
       }
       w = wh;
     }
   }
-  const size_t ncut = entries.size() / 8;
-  const size_t at = plan_entries(grid);
-  std::fill(out + nw + 1, out + at, 0);
-  std::copy(entries.begin(), entries.end(), out + at);
-  std::copy(waves.begin(), waves.end(), out + at + entries.size());
+  std::copy(wl, wl + nwl, ent + 8 * ncut);
   *ncut_out = static_cast<int32_t>(ncut);
-  return at + entries.size() + waves.size();
+  return at + 8 * ncut + nwl;
 }
 
 }  // namespace
@@ -246,6 +274,29 @@ int64_t pa_stream_plan(const int32_t* tile_prefix, int32_t n, int32_t num_kv_hea
   if (int64_t(num_kv_heads) * tile_prefix[n] >= (int64_t(1) << 31)) return -1;
   if (out_words < plan_entries(grid) + 8 * size_t(n) * num_kv_heads + 8 * size_t(grid)) return -1;
   return static_cast<int64_t>(build_plan(out, tile_prefix, n, num_kv_heads, grid, weights, num_cut));
+}
+
+pa_status pa_stream_class_finish(const int32_t* wave_times, int32_t grid, int32_t classes, double* out) {
+  if (!wave_times || !out || grid <= 0 || classes <= 0)
+    return pa::fail(PA_ERR_INVALID, "pa_stream_class_finish: bad arguments");
+  const int32_t t0 = wave_times[0];
+  int32_t first = 0;  // earliest start, relative to the first wave's
+  for (int32_t i = 0; i < 4 * grid; ++i)
+    first = std::min(first, static_cast<int32_t>(static_cast<uint32_t>(wave_times[2 * i]) - static_cast<uint32_t>(t0)));
+  std::fill(out, out + classes, 0.0);
+  static thread_local std::vector<int32_t> count_tls;
+  std::vector<int32_t>& count = count_tls;
+  count.assign(size_t(classes), 0);
+  for (int32_t b = 0; b < grid; ++b) {
+    int32_t end = INT32_MIN;
+    for (int k = 0; k < 4; ++k)
+      end = std::max(end, static_cast<int32_t>(static_cast<uint32_t>(wave_times[2 * (4 * b + k) + 1]) -
+                                               static_cast<uint32_t>(t0)));
+    out[b % classes] += double(int64_t(end) - first);
+    ++count[b % classes];
+  }
+  for (int32_t c = 0; c < classes; ++c) out[c] = count[c] ? out[c] / count[c] : 0.0;
+  return PA_OK;
 }
 
 size_t pa_step_record_words(int32_t max_seqs, int32_t table_stride, int32_t num_kv_heads) {

@@ -17,8 +17,8 @@ import numpy as np
 import torch
 
 from . import (PA_KERNEL_AUTO, PA_KERNEL_STREAM, STEP_ALL, BlockManager, alloc_cache, pa_copy_blocks, pa_decode_stream_grid,
-               pa_decode_variant, pa_decode_workspace_bytes, pa_step, pa_step_layer, pa_write_kv,
-               step_record_words)
+               pa_decode_variant, pa_decode_workspace_bytes, pa_step_layer, pa_write_kv, step_args, step_call,
+               step_record_words, stream_class_finish)
 
 __all__ = ["PagedKVEngine", "rebalance"]
 
@@ -91,6 +91,8 @@ class _Staging:
         self.times = torch.zeros(8 * _MAX_GRID, dtype=torch.int32, pin_memory=True)
         self.times_key = None     # (balance key, weight version) of the step whose stamps `times` holds
         self.event: Optional[torch.cuda.Event] = None
+        self.h_ptr, self.d_ptr, self.t_ptr = self.h.data_ptr(), self.d.data_ptr(), self.times.data_ptr()
+        self.words = min(self.h.numel(), self.d.numel())
 
     def _views(self, t, b):
         s = self.stride
@@ -136,6 +138,13 @@ class PagedKVEngine:
         self._weights = {}
         self._wver = {}
         self._wacc = {}
+        self._finish = np.zeros(XCDS)
+        # guard events, reused in turn: a guard is recorded again only after
+        # every slot it covered has been reused (and waited on)
+        self._guards = []
+        self._gi = 0
+        self._call_key = None
+        self._last_view = None
 
     # ------------------------------------------------------------- helpers
     def _next(self) -> _Staging:
@@ -163,7 +172,7 @@ class PagedKVEngine:
         acc = self._wacc.get(key)
         if acc is None or acc[0] != version:
             acc = self._wacc[key] = [version, np.zeros(XCDS), 0]
-        acc[1] += class_finish(st.times[: 8 * w.shape[0]].numpy(), w.shape[0])
+        acc[1] += stream_class_finish(st.t_ptr, w.shape[0], XCDS, self._finish)
         acc[2] += 1
         if acc[2] >= self.balance_steps:
             w[:] = rebalance_classes(w, acc[1] / acc[2], self.balance_rate)
@@ -192,7 +201,10 @@ class PagedKVEngine:
         self._pending.append(st)
         if self._uses % self._guard_every:
             return      # the slot keeps its previous guard until the next one is recorded
-        ev = torch.cuda.Event()
+        if len(self._guards) < 4:
+            self._guards.append(torch.cuda.Event())
+        ev = self._guards[self._gi % len(self._guards)]
+        self._gi += 1
         ev.record(stream)
         for p in self._pending:
             p.event = ev
@@ -253,7 +265,7 @@ class PagedKVEngine:
         stream = stream or torch.cuda.current_stream()
         n = len(seqs)
         st, tab, ctx = self.export(seqs)
-        self.last_tables, self.last_ctx = tab, ctx      # views of the pinned staging buffers
+        self._last_view = (tab, ctx)      # views of the pinned staging buffers
         max_ctx = int(ctx.max()) if n else 0
         st.d_tables[:n].copy_(st.h_tables[:n], non_blocking=True)
         st.d_ctx[:n].copy_(st.h_ctx[:n], non_blocking=True)
@@ -286,15 +298,45 @@ class PagedKVEngine:
         # the workspace is sized for the longest context the tables can hold
         ws = self.workspace(n, q.shape[1], self.stride * self.BS, partition_size)
         w = self.weights(n, q.shape[1]) if kernel in (PA_KERNEL_AUTO, PA_KERNEL_STREAM) else None
-        max_ctx = pa_step(self.bm, self._seq_arr, st.h, st.d, self.stride, self.k_cache, self.v_cache, k_new, v_new,
-                          q, out, 1.0 / float(self.D) ** 0.5, partition_size, ws if ws.numel() else None, kernel,
-                          stream, pass_events, wg_weights=w, wave_times=None if w is None else st.times)
+        # one argument list per step shape; per step only the record, the
+        # events and the stamps change
+        call_key = (key, k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), out.data_ptr(), out.dtype, q.shape[1],
+                    partition_size, kernel, stream if isinstance(stream, int) else stream.cuda_stream, ws.data_ptr(),
+                    ws.numel(), id(w))
+        if call_key != self._call_key:
+            self._call_args = step_args(self.bm, self._seq_arr, self.stride, self.k_cache, self.v_cache, k_new, v_new,
+                                        q, out, 1.0 / float(self.D) ** 0.5, partition_size,
+                                        ws if ws.numel() else None, kernel, stream, w)
+            self._call_key, self._call_w = call_key, w
+        args = self._call_args
+        args[3], args[4], args[5] = st.h_ptr, st.d_ptr, st.words
+        args[26], args[27] = (None, None) if pass_events is None else (pass_events[0].cuda_event,
+                                                                       pass_events[1].cuda_event)
+        args[31] = None if w is None else st.t_ptr
+        max_ctx = step_call(args)
         st.times_key = None if w is None else ((n, q.shape[1]), self._wver[(n, q.shape[1])])
-        (hs, hp, hc, ht), _, _ = st.packed(n)
-        self.last_tables, self.last_ctx, self.last_max_ctx = ht.numpy(), hc.numpy(), max_ctx
+        self._last_view = (st, n)
+        self.last_max_ctx = max_ctx
         self._last = (st, n, kernel, partition_size)
         self._record(st, stream)
         return out
+
+    @property
+    def last_tables(self) -> np.ndarray:
+        """Block tables of the last step or decode ([n][stride], views of the
+        pinned record)."""
+        return self._last_tc()[0]
+
+    @property
+    def last_ctx(self) -> np.ndarray:
+        return self._last_tc()[1]
+
+    def _last_tc(self):
+        v = self._last_view
+        if v is not None and isinstance(v[0], _Staging):
+            (hs, hp, hc, ht), _, _ = v[0].packed(v[1])
+            return ht.numpy(), hc.numpy()
+        return v
 
     def step_layer(self, k_cache, v_cache, k_new, v_new, q, out, phases: int = STEP_ALL, stream=None,
                    pass_events=None) -> torch.Tensor:

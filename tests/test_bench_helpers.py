@@ -49,3 +49,15 @@ def test_decode_bytes_closed_form():
     qo = len(ctx) * cfg.num_q_heads * cfg.head_dim * (2 + 4)
     tables = int((-(-ctx // cfg.block_size)).sum()) * 4
     assert b == kv + qo + tables + 4 * len(ctx)
+
+
+def test_unique_kv_bytes_counts_shared_blocks_once():
+    """Two sequences sharing a full first block (id 5) and each holding a
+    private partial block: the shared block counts once; a block two tables
+    hold with different fill counts counts its fullest use."""
+    tables = np.array([[5, 1, -1], [5, 2, -1], [7, -1, -1], [7, -1, -1]], np.int32)
+    ctx = np.array([20, 17, 3, 9])
+    per_token = 2 * 1 * 4 * 2        # hkv 1, d 4, bf16, K and V
+    got = bench.unique_kv_bytes(tables, ctx, 16, 1, 4, 2)
+    assert got == (16 + 4 + 1 + 9) * per_token
+    assert bench.kv_bytes(ctx, 1, 4, 2) == int(ctx.sum()) * per_token

@@ -592,4 +592,4 @@ def test_weights_change_only_rounding():
     for k in ("random", "ramp"):
         diff = float((outs[k] - outs["equal"]).abs().max())
         say("weights", k, "max |difference| to equal shares", diff, "max|out|", top)
-        assert diff <= 1e-4 * top
+        assert diff <= 1e-5 * top        # measured 7e-7 x max|out|
