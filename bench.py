@@ -48,9 +48,9 @@ def parse():
     ap.add_argument("--partition", type=int, default=None, help="tokens per split-K partition (0 = library)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma", "stream"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
-    ap.add_argument("--time-every", type=int, default=8,
-                    help="time the decode pass with HIP events on every k-th timed step (an event packet "
-                         "between kernels costs the stream ~4 us, so sparse timing keeps the step intact)")
+    ap.add_argument("--in-step", type=int, default=4,
+                    help="steps run after the timed ones with HIP events around each pass (an event packet "
+                         "between kernels costs the stream ~5 us, so the timed steps carry none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the short prefill / prefix-cache / swap measurements added to the decode line")
@@ -558,7 +558,7 @@ def main():
 
     # replay the construction (prefill + first decode step) on an engine sized
     # for the extra tokens the timed steps append
-    total_steps = args.warmup + args.steps
+    total_steps = args.warmup + args.steps + args.in_step
     seqs = list(range(cfg.num_seqs))
     # spare blocks for the tokens the warm-up and timed steps append
     extra_blocks = cfg.num_seqs * (-(-total_steps // cfg.block_size) + 1)
@@ -583,18 +583,13 @@ def main():
     stream = torch.cuda.current_stream()
 
     ctx0 = np.array([eng.bm.seq_len(s) for s in seqs], dtype=np.int64)
-    timed_steps = list(range(args.time_every - 1, args.steps, args.time_every)) or [args.steps - 1]
-    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in timed_steps}
-    for a, b in ev.values():          # create the events (torch creates them on first record)
-        a.record(stream)
-        b.record(stream)
 
-    def one_step(i, timed):
+    def one_step(events=None):
         eng.step(seqs, k_new, v_new, q, out=out, partition_size=part, kernel=kernel, stream=stream,
-                 pass_events=ev.get(i) if timed else None)
+                 pass_events=events)
 
     for i in range(args.warmup):
-        one_step(i, False)
+        one_step()
     torch.cuda.synchronize()
     ctx_start = ctx0 + args.warmup
     host_s = []
@@ -605,11 +600,23 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         h0 = time.perf_counter()
-        one_step(i, True)
+        one_step()
         host_s.append(time.perf_counter() - h0)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gc.enable()
+    # the pass alone inside a few more steps (after the timed ones, since the
+    # events' own packets would lengthen the steps they sit in)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.in_step)]
+    for a, b in ev:          # torch creates an event at its first record
+        a.record(stream)
+        b.record(stream)
+    for e in ev:
+        one_step(e)
+    torch.cuda.synchronize()
+    in_step_ctx = [ctx0 + args.warmup + args.steps + 1 + i for i in range(args.in_step)]
+    dec_bytes = [decode_bytes(c, cfg, esize) for c in in_step_ctx]
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev]) if ev else np.zeros(1)
     wts = eng.weights(cfg.num_seqs, cfg.num_q_heads)
     if wts is not None:
         print(f"[bench] workgroup weights by die: {wts[:8].tolist()}", file=sys.stderr, flush=True)
@@ -617,10 +624,8 @@ def main():
     # each timed step appends one token per sequence before attending
     step_ctx = [ctx_start + 1 + i for i in range(args.steps)]
     kv_total = sum(kv_bytes(c, cfg.num_kv_heads, cfg.head_dim, esize) for c in step_ctx)
-    dec_bytes = [decode_bytes(step_ctx[i], cfg, esize) for i in timed_steps]
-    dec_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in timed_steps])
 
-    # the pass alone: the last timed step's pass (same record, plan and data)
+    # the pass alone: the last step's pass (same record, plan and data)
     # launched back to back between two events, so that the event packets'
     # own cost (about 4 us each between kernels) stays out of the duration
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -631,7 +636,8 @@ def main():
         b1.record(stream)
     torch.cuda.synchronize()
     burst_us = b0.elapsed_time(b1) * 1e3 / args.burst
-    burst_bytes = decode_bytes(step_ctx[-1], cfg, esize)
+    last_ctx_all = in_step_ctx[-1] if in_step_ctx else step_ctx[-1]
+    burst_bytes = decode_bytes(last_ctx_all, cfg, esize)
     achieved = float(burst_bytes / (burst_us * 1e-6) / 1e9)
     # the whole of pa_decode: the pass and the merge of cut items, back to back
     for rep in range(2):
@@ -694,6 +700,7 @@ def main():
                           "when no block is shared)",
         "host_us_per_step": round(float(np.median(host_s)) * 1e6, 1),
         "host_us_per_step_max": round(float(np.max(host_s)) * 1e6, 1),
+        "host_us_first_steps": [round(x * 1e6, 1) for x in host_s[:6]],
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "pa_decode pass (" + kname + ")",
                      "achieved": round(achieved, 2),
@@ -714,14 +721,14 @@ def main():
                      "in_step": {"mean_us": round(float(dec_ms.mean()) * 1e3, 2),
                                  "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                                  "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
-                                 "bytes": int(np.mean(dec_bytes)), "launches": len(timed_steps),
-                                 "note": "events around the pass inside timed steps; includes the "
-                                         "event packets' own latency"}},
+                                 "bytes": int(np.mean(dec_bytes)) if dec_bytes else 0, "launches": len(ev),
+                                 "note": "events around the pass in steps run after the timed ones; "
+                                         "includes the event packets' own latency"}},
         "cpu_baseline": None,
     }
     if args.l2_model and kname == "stream":
         res["l2_request_model"] = l2_request_model(
-            step_ctx[-1], cfg.num_kv_heads, cfg.group, cfg.head_dim, esize, cfg.block_size,
+            last_ctx_all, cfg.num_kv_heads, cfg.group, cfg.head_dim, esize, cfg.block_size,
             pa.pa_decode_stream_grid(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim),
             eng.weights(cfg.num_seqs, cfg.num_q_heads), eng.stride, pa)
     if not args.no_cpu_baseline:
