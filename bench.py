@@ -123,12 +123,19 @@ def decode_bytes(ctx, cfg, esize, out_esize=4) -> int:
 def stream_device_code_sha(hashlib) -> str:
     """Hash of the stream kernel's device code: the source text before the
     host-side marker (launch code below it does not change what a pass
-    reads or writes), followed by the device headers it includes."""
+    reads or writes), followed by the device headers it includes and the
+    extra compiler flags the build gives that file."""
     with open(STREAM_SRC, "rb") as f:
         text = f.read().split(STREAM_HOST_MARKER, 1)[0]
     for h in STREAM_HEADERS:
         with open(h, "rb") as f:
             text += f.read()
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("pa_build_flags", os.path.join(ROOT, "paged_kv_cache_332_amd",
+                                                                                 "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    text += " ".join(b.FILE_FLAGS.get(os.path.basename(STREAM_SRC), [])).encode()
     return hashlib.sha256(text).hexdigest()
 
 
@@ -588,15 +595,18 @@ def main():
         eng.step(seqs, k_new, v_new, q, out=out, partition_size=part, kernel=kernel, stream=stream,
                  pass_events=events)
 
+    # no garbage-collection pause inside the timed region (the loop allocates
+    # little; a collection there would stall the stream for milliseconds).
+    # The collection runs before the warm-up: right before the timed steps it
+    # evicts the host caches the step's bookkeeping lives in, and the first
+    # timed step then took 130-225 us on the host instead of about 35.
+    gc.collect()
+    gc.disable()
     for i in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
     ctx_start = ctx0 + args.warmup
     host_s = []
-    # no garbage-collection pause inside the timed region (the loop allocates
-    # little; a collection there would stall the stream for milliseconds)
-    gc.collect()
-    gc.disable()
     t0 = time.perf_counter()
     for i in range(args.steps):
         h0 = time.perf_counter()

@@ -36,13 +36,21 @@ FLAGS = [
 ]
 
 
+# Per-file additions.  The decode kernels keep their matrix-core
+# accumulators in VGPRs: with the default heuristic they live in AGPRs and
+# the compiler copies all 32 of them between the two register files in every
+# tile's softmax and at the loop head (about 100 v_accvgpr moves per 16-token
+# tile, more than the tile's own vector work), read off the gfx950 assembly.
+FILE_FLAGS = {f: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for f in ("decode_stream.hip", "decode_mfma.hip")}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
