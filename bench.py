@@ -65,6 +65,10 @@ def parse():
                     help="measure prefill with prefix caching instead: the config's batch of prompts sharing a "
                          "P-token prefix plus U[128,512] own tokens, prefilled with cached prefix blocks reused "
                          "and again with none (prints its own JSON line)")
+    ap.add_argument("--waste", action="store_true",
+                    help="measure the block manager instead: admission and occupancy on the 13B-like "
+                         "configuration's arrival/departure trace, and the host cost of each pa_bm_* call "
+                         "(prints its own JSON line; no GPU work)")
     ap.add_argument("--burst", type=int, default=16,
                     help="back-to-back pass launches timed for the roofline's launch duration")
     ap.add_argument("--pool-order", default="config", choices=["config", "identity"],
@@ -496,6 +500,72 @@ def prefix_cache_bench(args, cfg, pa, torch):
     }
 
 
+def waste_bench(pa):
+    """The block manager on the 13B-like configuration's traffic
+    (workloads.admission_trace: lognormal lengths, about 256 live requests)
+    over that configuration's pool: pa_bm_admit with no headroom for each
+    arrival (refused requests are dropped), pa_bm_free_seq for each
+    departure; after every arrival pa_bm_occupancy is sampled.  Reports
+    admissions, refusals, peak and mean live requests, the unused room of
+    the blocks held and the slots in use; then the native host cost of each
+    pa_bm_* call (the bm_bench tool built beside the library)."""
+    import subprocess
+    import workloads as W
+    wl = W.build("c3_mha_f16_churn", values=False)
+    bs = wl.cfg.block_size
+    events, lengths = W.admission_trace()
+    bm = pa.BlockManager(wl.num_blocks, bs)
+    live = set()
+    admitted = refused = peak = 0
+    live_sum = unused_sum = used_sum = 0.0
+    t_admit = t_free = 0.0
+    n_free = 0
+    for ev in events:
+        if ev[0] == "depart":
+            if ev[1] in live:
+                live.discard(ev[1])
+                t0 = time.perf_counter()
+                bm.free_seq(ev[1])
+                t_free += time.perf_counter() - t0
+                n_free += 1
+            continue
+        t0 = time.perf_counter()
+        try:
+            bm.admit(ev[1], ev[2], 0)
+            ok = True
+        except pa.OutOfBlocks:
+            ok = False
+        t_admit += time.perf_counter() - t0
+        if ok:
+            admitted += 1
+            live.add(ev[1])
+        else:
+            refused += 1
+        held, tokens, slack, free_slots = bm.occupancy()
+        peak = max(peak, len(live))
+        live_sum += len(live)
+        unused_sum += slack / held if held else 0.0
+        used_sum += tokens / (wl.num_blocks * bs)
+    arrivals = admitted + refused
+    tool = os.path.join(ROOT, "paged_kv_cache_332_amd", "bm_bench")
+    try:
+        ops = json.loads(subprocess.run([tool, "0.3"], capture_output=True, text=True, check=True).stdout)
+    except Exception as e:  # reported, not fatal
+        ops = {"error": f"{type(e).__name__}: {e}"}
+    return {
+        "metric": "paged admission on the 13B-like traffic", "value": admitted, "unit": "requests admitted",
+        "higher_is_better": True, "n_gpus": 0, "data": "synthetic",
+        "config": {"workload": "c3_mha_f16_churn admission trace", "requests": arrivals,
+                   "mean_length": round(float(lengths.mean()), 1), "pool_blocks": wl.num_blocks, "block_size": bs,
+                   "admission_headroom_blocks": 0},
+        "admitted": admitted, "refused": refused, "peak_live": peak, "mean_live": round(live_sum / arrivals, 2),
+        "unused_of_held": round(unused_sum / arrivals, 4), "used_fraction": round(used_sum / arrivals, 4),
+        "host_ns_per_call_via_python": {"admit": round(t_admit / arrivals * 1e9, 1),
+                                        "free_seq": round(t_free / max(n_free, 1) * 1e9, 1)},
+        "host_ns_per_call_native": ops,
+    }
+
+
 def next_rows(args, w, cfg, pa, runner, torch):
     """Short measurements of the rows beyond decode on the same workload's
     shapes (each in full by its own flag): paged prefill of 512-token chunks
@@ -543,6 +613,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.waste:
+        import paged_kv_cache_332_amd as pa
+        print(json.dumps(waste_bench(pa)), flush=True)
         return
     import torch
     import workloads as W
