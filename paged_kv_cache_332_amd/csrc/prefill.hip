@@ -15,21 +15,31 @@
 // 64 CB / group query tokens); its four waves each own CB blocks of 16
 // matrix-core columns, the (query token, query head) pairs of 16 / group
 // tokens of the kv head's group per block.  The workgroup streams the
-// 16-token K/V tiles of the positions its tokens can see through a 6-slot LDS
-// ring filled by direct global->LDS loads, each wave loading a quarter of
-// every tile, so every K/V byte read serves 64 CB columns (CB = 2 for long
-// chunks: twice the flops per byte streamed; CB = 1 keeps short chunks
+// 16-token K/V tiles of the positions its tokens can see through an 8-slot
+// LDS ring filled by direct global->LDS loads, each wave loading a quarter of
+// every tile, so every K/V byte read serves 64 CB columns (CB = 2 or 3 for
+// long chunks: more flops per byte streamed; CB = 1 keeps short chunks
 // spread over many workgroups).  Per tile, wave and column block:
 // S^T = K Q^T with v_mfma_f32_16x16x32 (the K operand read once for all
 // blocks), a causal limit per column (skipped where every key of the tiles
 // is visible to every column of the block), an online softmax over a lazy
 // reference maximum (the exponent folds the scale in as one fma; the
-// reference is raised to the column's exact maximum only when a lane's terms
-// of a step sum past 2^16, which leaves no maximum on the common path), P
-// split into a 16-bit high part and the rounded remainder for two P V
-// products into O^T; a block none of whose columns sees the tiles skips
-// them.  No split of the context: a workgroup covers its tokens' whole
-// prefix, and many workgroups run at once.
+// reference is raised to the column's exact maximum only when a lane's
+// weights of a step sum past 2^15, which leaves no maximum on the common
+// path), P rounded to fp16 for one P V product into O^T; a block none of
+// whose columns sees the tiles skips them.  No split of the context: a
+// workgroup covers its tokens' whole prefix, and many workgroups run at
+// once.
+//
+// P V in fp16.  The weights are at most 2^15 and keep 11 significant bits
+// (bf16 would keep 8, too few for the 2e-3 bound); the values are converted
+// to fp16 once per workgroup, in LDS, by the wave that loaded them, while the
+// pair before them computes.  bf16 values fp16 cannot hold as they are (a
+// group of 32 dims whose largest magnitude so far is 2^16 or more, or below
+// 2^-10) are held as v 2^frame with a power-of-two frame per group; the
+// group's accumulators follow its frame, which never grows once a nonzero
+// value was seen, so they only ever shrink (exactly, but for what falls below
+// fp32's range).
 //
 // Tiles go in pairs: one softmax step covers 32 keys (one cross-lane
 // reduction and one rescale check per 32 keys), and P V is one
@@ -53,6 +63,45 @@ template <class V>
 __device__ __forceinline__ V ring_read(const uint8_t* p) {
   return *(const volatile __attribute__((address_space(3))) V*)(p);
 }
+template <class V>
+__device__ __forceinline__ void ring_write(uint8_t* p, const V& v) {
+  *(volatile __attribute__((address_space(3))) V*)(p) = v;
+}
+
+// Sum of the eight fp16 values of h in fp32 (products by one are exact).
+// The pairs are taken with shuffles: reading them as the 32-bit words of a
+// bit cast of h made this compiler (ROCm 7.2) use the first word four times.
+__device__ __forceinline__ float sum8_f16(const f16x8& h) {
+  const f16x2 one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  float a = __builtin_amdgcn_fdot2(__builtin_shufflevector(h, h, 0, 1), one, 0.f, false);
+  float b = __builtin_amdgcn_fdot2(__builtin_shufflevector(h, h, 2, 3), one, 0.f, false);
+  a = __builtin_amdgcn_fdot2(__builtin_shufflevector(h, h, 4, 5), one, a, false);
+  b = __builtin_amdgcn_fdot2(__builtin_shufflevector(h, h, 6, 7), one, b, false);
+  return a + b;
+}
+
+// Power-of-two frame of a half of the values, from the largest exponent e
+// (the unbiased exponent field) of its values so far: values are held in
+// fp16 as v 2^frame.  0 while e is in [-10, 15] (every bf16 value converts
+// exactly or, below 2^-14, within 2^-25 of an absolute error) or no nonzero
+// value was seen (e = kNoExp), else the frame that puts 2^e at 2^14.  The
+// frame never grows once a nonzero value was seen, so the accumulators only
+// ever shrink when it changes.
+constexpr int kNoExp = -(1 << 20);
+__device__ __forceinline__ int fp16_frame(int e) {
+  return (e == kNoExp || (e >= -10 && e <= 15)) ? 0 : 14 - e;
+}
+
+// The bf16 magnitude (bits, sign cleared) from which a value can change the
+// frame of a group whose largest exponent so far is e: any nonzero value
+// while none was seen, 2^16 while e is in [-10, 15], else 2^(e + 1) (the
+// infinity bits at most, so that infinities and NaN always take the exact
+// path).
+__device__ __forceinline__ uint32_t fp16_frame_threshold(int e) {
+  if (e == kNoExp) return 1u;
+  if (e >= -10 && e <= 15) return 0x4780u;
+  return uint32_t(min(e + 128, 255)) << 7;
+}
 
 // Wait until this wave's loads of the oldest tiles in flight have landed,
 // when k newer tiles (LPW loads each) may stay in flight (k uniform, at most
@@ -74,8 +123,8 @@ template <class T, int D, int BS, int G, int CB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
   using bits = typename T::bits;
   using MF = MfmaOps<T>;
-  using v8 = typename MF::v8;
-  using el = typename MF::e;
+  using PV = MfmaOps<F16>;             // P V in fp16 whatever the cache type
+  constexpr bool kBf16 = std::is_same_v<T, BF16>;
   constexpr int TB = 16 / G;           // query tokens per column block
   constexpr int TQ = CB * TB;          // per wave
   constexpr int TQW = 4 * TQ;          // per workgroup
@@ -83,7 +132,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int NT = D / 16;           // PV row tiles of 16 dims
   constexpr int KI = D / 32;           // 1 KiB loads per K (and per V) tile
   constexpr int LPW = 2 * KI / 4;      // loads per wave per tile
-  constexpr int NSL = 6;               // ring slots: three pairs of tiles
+  constexpr int NSL = 8;               // ring slots: four pairs of tiles
   constexpr int IDCAP = 512;           // tiles whose block ids are staged at once
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   static_assert(LPW >= 1 && LPW * (NSL - 1) < 64, "loads per wave");
@@ -93,6 +142,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   constexpr int SLOT = 2 * KI * 1024;
   __shared__ int2 s_ids[IDCAP];
+  __shared__ int s_frame[2][4];        // per pair parity and group of 32 dims: the values' power-of-two frame
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -178,14 +228,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
     id_base = from;
   };
-  // this wave's quarter of the loads of tile t into its slot
+  // this wave's share of the loads of tile t into its slot: with D = 128
+  // K load w and V load w (its own group of 32 value dims), with D = 64 load
+  // w (waves 2 and 3 the values)
   auto issue = [&](int t) {
     uint8_t* sl = ring + (t % NSL) * SLOT;
     const int b0 = uniform(ring_read<int32_t>(reinterpret_cast<const uint8_t*>(&s_ids[t - id_base].x)));
     const int b1 = uniform(ring_read<int32_t>(reinterpret_cast<const uint8_t*>(&s_ids[t - id_base].y)));
 #pragma unroll
     for (int ii = 0; ii < LPW; ++ii) {
-      const int i = wave * LPW + ii;             // load i of the tile's 2 KI
+      const int i = LPW == 1 ? wave : ii * KI + wave;   // load i of the tile's 2 KI
       if (i < KI) {
         const int u = i * 64 + lane;
         const int jj = u >> 4, tt = u & 15;
@@ -224,6 +276,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   f32x4 acc[CB][NT];
   float m_ref[CB], l_lane[CB];                   // (reference maximum: scaled, log2 units)
+  int frame[KI];                                 // accumulators of each group of 32 dims hold O 2^frame
+#pragma unroll
+  for (int g = 0; g < KI; ++g) frame[g] = 0;
+  int vexp = kNoExp;                             // (value loaders) largest exponent of their group so far
+  uint32_t vthr = 1u;                            // and the magnitude bits from which it can change
+  const int vgrp = LPW == 1 ? wave - 2 : wave;   // the group of 32 value dims this wave loads (if in [0, KI))
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
@@ -231,6 +289,124 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     m_ref[cb] = kNegInf;
     l_lane[cb] = 0.f;
   }
+
+  // The values of pair t in fp16, 16-dim tile n (1 KiB, laid out as the P V
+  // operand: [key quad q][dim c of the tile] x 16 bytes, keys 4 q .. 4 q + 3
+  // of tile t, then of tile t + 1), where the raw values of its group of 32
+  // dims were: tile 2 g of group g in the value part of tile t's slot, tile
+  // 2 g + 1 in that of tile t + 1.
+  auto cv_tile = [&](int t, int n) __attribute__((always_inline)) {
+    return ring + ((t + (n & 1)) % NSL) * SLOT + KI * 1024 + (n >> 1) * 1024;
+  };
+
+  // Every wave that loads values converts its group of 32 dims of pair t to
+  // fp16 in place once its loads of the pair have landed (it reads all of
+  // its bytes before it writes), zeros past the workgroup's last position
+  // (which may hold anything, NaN poison included); bf16 values are held as
+  // v 2^frame, the group's frame (see fp16_frame) published with the pair.
+  auto convert = [&](int t) __attribute__((always_inline)) {
+    const uint8_t* sa = ring + (t % NSL) * SLOT + KI * 1024 + vgrp * 1024;
+    const uint8_t* sb = ring + ((t + 1) % NSL) * SLOT + KI * 1024 + vgrp * 1024;
+    constexpr int NH = 2;                        // 16-dim tiles per group
+    u32x4 w[NH];
+#pragma unroll
+    for (int n2 = 0; n2 < NH; ++n2) {
+      const int d = 16 * n2 + c;                 // dim in the group
+      const u32x2 va = ring_read<u32x2>(sa + d * 32 + 8 * q);
+      const u32x2 vb = ring_read<u32x2>(sb + d * 32 + 8 * q);
+      w[n2] = u32x4{va[0], va[1], vb[0], vb[1]};
+    }
+    if (16 * t + 32 > kmax) {
+      const int kp0 = 16 * t + 4 * q;
+#pragma unroll
+      for (int n2 = 0; n2 < NH; ++n2) {
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const int k0 = kp0 + (w2 >> 1) * 16 + 2 * (w2 & 1);   // the two keys of 32-bit word w2
+          uint32_t x = w[n2][w2];
+          if (k0 >= kmax) x &= 0xFFFF0000u;
+          if (k0 + 1 >= kmax) x &= 0x0000FFFFu;
+          w[n2][w2] = x;
+        }
+      }
+    }
+    if constexpr (kBf16) {
+      // the frame can change only if a magnitude reaches the group's
+      // threshold (16-bit integer maxima of the bits); then the exact
+      // largest magnitude of the pair updates the group's exponent
+      u16x2 m16 = {0, 0};
+#pragma unroll
+      for (int n2 = 0; n2 < NH; ++n2)
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2)
+          m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(u16x2, w[n2][w2] & 0x7FFF7FFFu));
+      const uint32_t mlane = max(uint32_t(m16[0]), uint32_t(m16[1]));
+      if (__builtin_amdgcn_ballot_w64(mlane >= vthr)) {
+        float mx = 0.f;
+#pragma unroll
+        for (int n2 = 0; n2 < NH; ++n2)
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2)
+            mx = fmaxf(mx, fmaxf(fabsf(BF16::lo(w[n2][w2])), fabsf(BF16::hi(w[n2][w2]))));
+        mx = reduce_low_bits<OpMax, 6>(mx);
+        const uint32_t mb = uniform(__float_as_uint(mx));
+        if (mb != 0u) vexp = uniform(max(vexp, int(mb >> 23) - 127));
+        vthr = uniform(fp16_frame_threshold(vexp));
+      }
+      const int fr = fp16_frame(vexp);
+      if (fr == 0) {
+#pragma unroll
+        for (int n2 = 0; n2 < NH; ++n2)
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2)
+            w[n2][w2] = __builtin_bit_cast(
+                uint32_t, f16x2{static_cast<_Float16>(BF16::lo(w[n2][w2])), static_cast<_Float16>(BF16::hi(w[n2][w2]))});
+      } else {
+#pragma unroll
+        for (int n2 = 0; n2 < NH; ++n2)
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2)
+            w[n2][w2] = __builtin_bit_cast(
+                uint32_t, f16x2{static_cast<_Float16>(__builtin_amdgcn_ldexpf(BF16::lo(w[n2][w2]), fr)),
+                                static_cast<_Float16>(__builtin_amdgcn_ldexpf(BF16::hi(w[n2][w2]), fr))});
+      }
+      if (lane == 0) ring_write<int>(reinterpret_cast<uint8_t*>(&s_frame[(t >> 1) & 1][vgrp]), fr);
+    }
+#pragma unroll
+    for (int n2 = 0; n2 < NH; ++n2) ring_write<u32x4>(cv_tile(t, 2 * vgrp + n2) + (q * 16 + c) * 16, w[n2]);
+  };
+
+  // P V of one column block over the pair: P rounded to fp16 (h) against
+  // the converted values
+  auto pv_pair = [&](int cb, const f16x8& h, const u32x4 (&vr)[NT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[cb][n] = PV::pv32(vr[n], h, acc[cb][n]);
+  };
+
+  // raise column block cb's reference maximum to the exact maximum of its
+  // column over the pair (sv: its raw scores, masked ones -inf), rescaling
+  // what was summed against the old one
+  auto raise_reference = [&](int cb, const float (&sv)[8]) __attribute__((always_inline)) {
+    float cm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    cm = xor16<OpMax>(cm);
+    cm = xor32<OpMax>(cm);
+    const float mn = cm * sf;
+    const bool up = mn > m_ref[cb];
+    const float alpha = up ? (m_ref[cb] == kNegInf ? 0.f : fast_exp2(m_ref[cb] - mn)) : 1.f;
+    m_ref[cb] = up ? mn : m_ref[cb];
+    l_lane[cb] *= alpha;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[cb][n] *= alpha;
+  };
+
+  // exponents of the raw scores sv against block cb's reference, rounded to
+  // fp16 (h) with their sum (ps)
+  auto weights = [&](int cb, const float (&sv)[8], f16x8& h, float& ps) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb])));
+    ps = sum8_f16(h);
+  };
 
   // one softmax step over tiles t, t + 1 (OPEN: every key of the pair is
   // visible to every column of the wave, and the reference maxima are finite)
@@ -256,79 +432,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int m = 0; m < NS; ++m) sc[cb][h2] = MF::qk(kr[m], qop[cb][m], sc[cb][h2]);
       }
     }
-    // V rows of both tiles, 8 keys per lane (k = 8 q + i: key kp0 + i of
-    // tile t for i < 4, of tile t + 1 for i >= 4), zeros past the
-    // workgroup's last position (which may hold anything, NaN poison
-    // included)
+    if constexpr (kBf16) {
+      // the accumulators follow the frames of the values (a change, rare,
+      // only ever shrinks them, exactly but for what falls below fp32's
+      // range)
+      int fr[KI];
+      bool moved = false;
+#pragma unroll
+      for (int g = 0; g < KI; ++g) {
+        fr[g] = uniform(ring_read<int>(reinterpret_cast<const uint8_t*>(&s_frame[(t >> 1) & 1][g])));
+        moved = moved || fr[g] != frame[g];
+      }
+      if (moved) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[cb][n][i] = __builtin_amdgcn_ldexpf(acc[cb][n][i], fr[n >> 1] - frame[n >> 1]);
+#pragma unroll
+        for (int g = 0; g < KI; ++g) frame[g] = fr[g];
+      }
+    }
+    // the next pair: once this wave's loads of it have landed (those of the
+    // two pairs after it may stay in flight), its values are converted, the
+    // vector work overlapping this pair's matrix products
+    if (t + 2 < nt) {
+      wait_oldest_tile<LPW, 4>(min(nt, t + 8) - min(nt, t + 4));
+      if (vgrp >= 0 && vgrp < KI) convert(t + 2);
+    }
+    // the pair's values in fp16, 8 keys per lane (k = 8 q + i: key kp0 + i
+    // of tile t for i < 4, of tile t + 1 for i >= 4)
     u32x4 vr[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const u32x2 va = ring_read<u32x2>(sa + KI * 1024 + (16 * n + c) * 32 + 8 * q);
-      const u32x2 vb = ring_read<u32x2>(sb + KI * 1024 + (16 * n + c) * 32 + 8 * q);
-      vr[n] = u32x4{va[0], va[1], vb[0], vb[1]};
-    }
+    for (int n = 0; n < NT; ++n) vr[n] = ring_read<u32x4>(cv_tile(t, n) + (q * 16 + c) * 16);
     if constexpr (OPEN) {
-      // exponents against the reference maxima as they stand; a column's
-      // reference is raised to its exact maximum only when one of its terms
-      // would pass 2^13 (or is not a number)
-      float x[CB][8], xm[CB];
+      // weights against the reference maxima as they stand; a column's
+      // reference is raised to its exact maximum only when a lane's eight
+      // weights sum past 2^15 (or are not a number), so that every weight
+      // fits fp16; one check for all blocks
+      f16x8 h[CB];
+      float ps[CB];
       bool over = false;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[cb][i] = __builtin_fmaf(sc[cb][0][i], sf, -m_ref[cb]);
-          x[cb][4 + i] = __builtin_fmaf(sc[cb][1][i], sf, -m_ref[cb]);
-        }
-        xm[cb] = fmaxf(fmaxf(fmaxf(x[cb][0], x[cb][1]), fmaxf(x[cb][2], x[cb][3])),
-                       fmaxf(fmaxf(x[cb][4], x[cb][5]), fmaxf(x[cb][6], x[cb][7])));
-        over = over || !(xm[cb] <= 13.f);
+        const float sv[8] = {sc[cb][0][0], sc[cb][0][1], sc[cb][0][2], sc[cb][0][3],
+                             sc[cb][1][0], sc[cb][1][1], sc[cb][1][2], sc[cb][1][3]};
+        weights(cb, sv, h[cb], ps[cb]);
+        over = over || !(ps[cb] <= 32768.f);
       }
       if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          float cm = xor16<OpMax>(xm[cb]);
-          cm = xor32<OpMax>(cm);
-          const bool up = cm > 0.f;
-          const float mn = up ? m_ref[cb] + cm : m_ref[cb];
-          const float d = mn - m_ref[cb];
-          const float alpha = fast_exp2(-d);
-          m_ref[cb] = mn;
-          l_lane[cb] *= alpha;
-#pragma unroll
-          for (int n = 0; n < NT; ++n) acc[cb][n] *= alpha;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) x[cb][i] -= d;
+          const float sv[8] = {sc[cb][0][0], sc[cb][0][1], sc[cb][0][2], sc[cb][0][3],
+                               sc[cb][1][0], sc[cb][1][1], sc[cb][1][2], sc[cb][1][3]};
+          raise_reference(cb, sv);
+          weights(cb, sv, h[cb], ps[cb]);
         }
       }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        float pv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(x[cb][i]);
-        l_lane[cb] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-        v8 phi, plo;
-        MF::split(pv, phi, plo);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          acc[cb][n] = MF::pv32(vr[n], phi, acc[cb][n]);
-          acc[cb][n] = MF::pv32(vr[n], plo, acc[cb][n]);
-        }
+        l_lane[cb] += ps[cb];
+        pv_pair(cb, h[cb], vr);
       }
     } else {
-      if (16 * t + 32 > kmax) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-#pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2) {
-            const int k0 = kp0 + (w2 >> 1) * 16 + 2 * (w2 & 1);   // the two keys of 32-bit word w2
-            uint32_t x = vr[n][w2];
-            if (k0 >= kmax) x &= 0xFFFF0000u;
-            if (k0 + 1 >= kmax) x &= 0x0000FFFFu;
-            vr[n][w2] = x;
-          }
-        }
-      }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         // (tile 0 holds position 0, which every column sees, so no block
@@ -350,38 +518,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             sv[4 + i] = kp0 + 16 + i < lim[cb] ? sc[cb][1][i] : kNegInf;
           }
         }
-        // exponents against the column's reference maximum as it stands; it
-        // is raised (to the column's exact maximum, over its four lanes) only
-        // when a lane's eight terms sum past 2^16 or are not finite (the first
-        // step, whose reference is -inf): no maximum at all on the common path
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb]));
-        float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        if (__builtin_amdgcn_ballot_w64(!(ps <= 65536.f))) {
-          float cm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                           fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-          cm = xor16<OpMax>(cm);
-          cm = xor32<OpMax>(cm);
-          const float mn = cm * sf;
-          const bool up = mn > m_ref[cb];
-          const float alpha = up ? (m_ref[cb] == kNegInf ? 0.f : fast_exp2(m_ref[cb] - mn)) : 1.f;
-          m_ref[cb] = up ? mn : m_ref[cb];
-          l_lane[cb] *= alpha;
-#pragma unroll
-          for (int n = 0; n < NT; ++n) acc[cb][n] *= alpha;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb]));
-          ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        // weights against the column's reference maximum as it stands; it is
+        // raised (to the column's exact maximum, over its four lanes) only
+        // when a lane's eight weights sum past 2^15 or are not finite (the
+        // first step, whose reference is -inf): no maximum at all on the
+        // common path
+        f16x8 h;
+        float ps;
+        weights(cb, sv, h, ps);
+        if (__builtin_amdgcn_ballot_w64(!(ps <= 32768.f))) {
+          raise_reference(cb, sv);
+          weights(cb, sv, h, ps);
         }
         l_lane[cb] += ps;
-        v8 phi, plo;
-        MF::split(p, phi, plo);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          acc[cb][n] = MF::pv32(vr[n], phi, acc[cb][n]);
-          acc[cb][n] = MF::pv32(vr[n], plo, acc[cb][n]);
-        }
+        pv_pair(cb, h, vr);
       }
     }
   };
@@ -389,22 +539,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   stage_ids(0);
   __syncthreads();
   // tiles go in pairs (32 keys per softmax step): pair p computes from slots
-  // 2p, 2p + 1 (mod NSL) while pair p + 1 is in flight and pair p + 2 fills
-  // the slots of pair p - 1
+  // 2p, 2p + 1 (mod NSL), its values converted while pair p - 1 computed;
+  // pair p + 1 lands and is converted during pair p, pair p + 2 is in flight
+  // and pair p + 3 fills the slots of pair p - 1
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 6; ++i)
     if (i < nt) issue(i);
-  // one pair: wait for its tiles, refill the slots of the pair before it,
-  // compute
+  // the first pair's values, before any math
+  wait_oldest_tile<LPW, 4>(min(nt, 6) - min(nt, 2));
+  if (vgrp >= 0 && vgrp < KI) convert(0);
+  lgkm_wait0();
+  wg_barrier();
+  // one pair: refill the slots of the pair before it, compute (converting
+  // the next pair), then finish this wave's LDS writes and meet the others:
+  // past the barrier every wave is done with this pair and the next one is
+  // landed and converted
   auto advance = [&](int t, auto open_tag) __attribute__((always_inline)) {
-    // this wave's loads of tiles t and t + 1 have landed once at most its
-    // loads of the newer tiles are outstanding; the barrier then covers every
-    // wave's share (and every wave is done with the previous pair, whose
-    // slots are refilled next)
-    wait_oldest_tile<LPW, 2>(min(nt - 1, t + 3) - min(nt - 1, t + 1));
-    wg_barrier();
 #pragma unroll
-    for (int i = 4; i < 6; ++i) {
+    for (int i = 6; i < 8; ++i) {
       const int tn = t + i;
       if (tn < nt) {
         if (tn >= id_base + IDCAP) {
@@ -418,6 +570,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
     }
     pair_step(t, open_tag);
+    lgkm_wait0();
+    wg_barrier();
   };
   // Pairs past the first whose keys every column of the wave sees (those
   // before the wave's first causal limit) take the open path: no causal
@@ -443,7 +597,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const int64_t o = qrow[cb] * D + 4 * q;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const f32x4 v = acc[cb][n] * inv;
+        f32x4 v = acc[cb][n] * inv;
+        if constexpr (kBf16) {
+          const int fr = frame[n >> 1];
+          if (fr != 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_ldexpf(acc[cb][n][i], -fr) * inv;
+          }
+        }
         if (a.out_f32) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o + 16 * n) = v;
         } else {
@@ -460,7 +621,7 @@ template <class T, int D, int BS, int G>
 hipError_t launch_g(const PrefillArgs& a, int32_t max_query_len, hipStream_t stream) {
   const int cb = prefill_column_blocks(G, max_query_len, a.num_seqs, a.num_kv_heads);
   const int tpw = 4 * cb * (16 / G);
-  const size_t lds = 6 * 2 * (D / 32) * 1024;   // the tile ring: 6 slots of K and V
+  const size_t lds = 8 * 2 * (D / 32) * 1024;   // the tile ring: 8 slots of K and V
   dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads), block(256);
   if (cb == 3) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 3>), grid, block, lds, stream, a);
   else if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2>), grid, block, lds, stream, a);

@@ -254,3 +254,54 @@ def test_prefill_scale_sign_zero_and_large(dtype, which):
         err = max(err, float(np.max(np.abs(got[qs[i]: qs[i + 1]] - ref))))
     say(which, dtype, "max abs error", err)
     assert err <= 2e-3
+
+
+def test_prefill_values_far_from_one():
+    """bf16 values far from the unit range (all of them: the prefill keeps
+    P V in 16-bit products, whose range must not limit them).  Sequences
+    with huge values (2^40), tiny ones (2^-30), a switch from tiny to huge
+    along the context, leading zero values, and one outlier of 2^30 in one
+    half of the dims of one kv head: every output row is within 2e-3 of the
+    oracle relative to the largest value its row sees in the same kv head
+    and half of the dims."""
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    ctx, chunk = [700, 500, 900, 300, 200], [300, 200, 400, 300, 50]
+    hq, hkv, d, bs = 16, 4, 128, 16
+    say("prefill values far from one")
+    w = W.tiny(num_seqs=len(ctx), dtype="bf16", seed=95, ctx=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+               block_size=bs)
+    # powers of two keep every bf16 value exact
+    w.v_rows[w.row_of(0, np.arange(700))] *= 2.0 ** 40
+    w.v_rows[w.row_of(1, np.arange(500))] *= 2.0 ** -30
+    w.v_rows[w.row_of(2, np.arange(450))] *= 2.0 ** -30
+    w.v_rows[w.row_of(2, np.arange(450, 900))] *= 2.0 ** 20
+    w.v_rows[w.row_of(3, np.arange(100))] = 0.0
+    w.v_rows[w.row_of(4, np.array([150])), 0, :4] = 2.0 ** 30
+    dev = runner.run_script(w, decode=False)
+    eng = dev.engine
+    tab, _ = eng.bm.export(list(range(len(ctx))), eng.stride)
+    rng = np.random.default_rng(96)
+    T = sum(chunk)
+    q = W.round_to_dtype(rng.standard_normal((T, hq, d), dtype=np.float32), "bf16")
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    out = torch.full((T, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    pa.pa_prefill(out, torch.from_numpy(q).to("cuda").to(torch.bfloat16), eng.k_cache, eng.v_cache,
+                  torch.from_numpy(np.ascontiguousarray(tab)).to("cuda"), torch.from_numpy(qs).to("cuda"),
+                  torch.from_numpy(np.asarray(ctx, np.int32)).to("cuda"), max(chunk), max(ctx), 1.0 / d ** 0.5)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    G = hq // hkv
+    worst = 0.0
+    for i, (n, L) in enumerate(zip(ctx, chunk)):
+        V = w.v_rows[w.row_of(i, np.arange(n))].astype(np.float64)
+        ref = oracle.prefill_attention(q[qs[i]: qs[i + 1]], w.k_rows[w.row_of(i, np.arange(n))], V, 1.0 / d ** 0.5)
+        # largest magnitude seen by row t, per kv head and half of the dims
+        half_max = np.abs(V).reshape(n, hkv, 2, d // 2).max(axis=3)          # [n, hkv, 2]
+        seen = np.maximum.accumulate(half_max, axis=0)[n - L:]               # [L, hkv, 2]
+        bound = np.repeat(np.repeat(seen, G, axis=1), d // 2, axis=2)        # [L, hq, d]
+        rel = np.abs(got[qs[i]: qs[i + 1]] - ref) / np.maximum(bound, 1e-300)
+        say("sequence", i, "max error relative to the values seen", float(rel.max()))
+        worst = max(worst, float(rel.max()))
+    assert worst <= 2e-3
