@@ -125,6 +125,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   using MF = MfmaOps<T>;
   using PV = MfmaOps<F16>;             // P V in fp16 whatever the cache type
   constexpr bool kBf16 = std::is_same_v<T, BF16>;
+  // bf16 values with three column blocks are converted to fp16 in LDS for
+  // one P V product (the conversion pays off over that many columns); other
+  // bf16 shapes split P into a bf16 high part and the rounded remainder for
+  // two products; fp16 values take one fp16 product as they are
+  constexpr bool CONV = kBf16 && CB == 3;
+  constexpr bool SPLIT = kBf16 && !CONV;
   constexpr int TB = 16 / G;           // query tokens per column block
   constexpr int TQ = CB * TB;          // per wave
   constexpr int TQW = 4 * TQ;          // per workgroup
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int NT = D / 16;           // PV row tiles of 16 dims
   constexpr int KI = D / 32;           // 1 KiB loads per K (and per V) tile
   constexpr int LPW = 2 * KI / 4;      // loads per wave per tile
-  constexpr int NSL = 8;               // ring slots: four pairs of tiles
+  constexpr int NSL = CONV ? 8 : 6;    // ring slots: four (three) pairs of tiles
   constexpr int IDCAP = 512;           // tiles whose block ids are staged at once
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   static_assert(LPW >= 1 && LPW * (NSL - 1) < 64, "loads per wave");
@@ -276,6 +282,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   f32x4 acc[CB][NT];
   float m_ref[CB], l_lane[CB];                   // (reference maximum: scaled, log2 units)
+  // one column block's weights of a pair for P V
+  struct Weights {
+    f16x8 h;                                     // rounded to fp16
+    float p[SPLIT ? 8 : 1];                      // (SPLIT) in fp32
+  };
   int frame[KI];                                 // accumulators of each group of 32 dims hold O 2^frame
 #pragma unroll
   for (int g = 0; g < KI; ++g) frame[g] = 0;
@@ -376,11 +387,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int n2 = 0; n2 < NH; ++n2) ring_write<u32x4>(cv_tile(t, 2 * vgrp + n2) + (q * 16 + c) * 16, w[n2]);
   };
 
-  // P V of one column block over the pair: P rounded to fp16 (h) against
-  // the converted values
-  auto pv_pair = [&](int cb, const f16x8& h, const u32x4 (&vr)[NT]) __attribute__((always_inline)) {
+  // P V of one column block over the pair: P rounded to fp16 against fp16
+  // values in one product, or (SPLIT) its bf16 high part and remainder in two
+  auto pv_pair = [&](int cb, const Weights& wt, const u32x4 (&vr)[NT]) __attribute__((always_inline)) {
+    if constexpr (SPLIT) {
+      typename MF::v8 phi, plo;
+      MF::split(wt.p, phi, plo);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[cb][n] = PV::pv32(vr[n], h, acc[cb][n]);
+      for (int n = 0; n < NT; ++n) {
+        acc[cb][n] = MF::pv32(vr[n], phi, acc[cb][n]);
+        acc[cb][n] = MF::pv32(vr[n], plo, acc[cb][n]);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[cb][n] = PV::pv32(vr[n], wt.h, acc[cb][n]);
+    }
   };
 
   // raise column block cb's reference maximum to the exact maximum of its
@@ -401,11 +422,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   };
 
   // exponents of the raw scores sv against block cb's reference, rounded to
-  // fp16 (h) with their sum (ps)
-  auto weights = [&](int cb, const float (&sv)[8], f16x8& h, float& ps) __attribute__((always_inline)) {
+  // fp16 (SPLIT: kept in fp32) with their sum (ps)
+  auto weights = [&](int cb, const float (&sv)[8], Weights& wt, float& ps) __attribute__((always_inline)) {
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb])));
-    ps = sum8_f16(h);
+      for (int i = 0; i < 8; ++i) wt.p[i] = fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb]));
+      ps = ((wt.p[0] + wt.p[1]) + (wt.p[2] + wt.p[3])) + ((wt.p[4] + wt.p[5]) + (wt.p[6] + wt.p[7]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wt.h[i] = static_cast<_Float16>(fast_exp2(__builtin_fmaf(sv[i], sf, -m_ref[cb])));
+      ps = sum8_f16(wt.h);
+    }
   };
 
   // one softmax step over tiles t, t + 1 (OPEN: every key of the pair is
@@ -432,7 +459,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int m = 0; m < NS; ++m) sc[cb][h2] = MF::qk(kr[m], qop[cb][m], sc[cb][h2]);
       }
     }
-    if constexpr (kBf16) {
+    if constexpr (CONV) {
       // the accumulators follow the frames of the values (a change, rare,
       // only ever shrinks them, exactly but for what falls below fp32's
       // range)
@@ -458,28 +485,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // the next pair: once this wave's loads of it have landed (those of the
     // two pairs after it may stay in flight), its values are converted, the
     // vector work overlapping this pair's matrix products
-    if (t + 2 < nt) {
-      wait_oldest_tile<LPW, 4>(min(nt, t + 8) - min(nt, t + 4));
-      if (vgrp >= 0 && vgrp < KI) convert(t + 2);
+    if constexpr (CONV) {
+      if (t + 2 < nt) {
+        wait_oldest_tile<LPW, 4>(min(nt, t + 8) - min(nt, t + 4));
+        if (vgrp >= 0 && vgrp < KI) convert(t + 2);
+      }
     }
-    // the pair's values in fp16, 8 keys per lane (k = 8 q + i: key kp0 + i
-    // of tile t for i < 4, of tile t + 1 for i >= 4)
+    // the pair's values, 8 keys per lane (k = 8 q + i: key kp0 + i of tile t
+    // for i < 4, of tile t + 1 for i >= 4): converted, or as the slots hold
+    // them with zeros past the workgroup's last position (which may hold
+    // anything, NaN poison included)
     u32x4 vr[NT];
+    if constexpr (CONV) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) vr[n] = ring_read<u32x4>(cv_tile(t, n) + (q * 16 + c) * 16);
+      for (int n = 0; n < NT; ++n) vr[n] = ring_read<u32x4>(cv_tile(t, n) + (q * 16 + c) * 16);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const u32x2 va = ring_read<u32x2>(sa + KI * 1024 + (16 * n + c) * 32 + 8 * q);
+        const u32x2 vb = ring_read<u32x2>(sb + KI * 1024 + (16 * n + c) * 32 + 8 * q);
+        vr[n] = u32x4{va[0], va[1], vb[0], vb[1]};
+      }
+      if (!OPEN && 16 * t + 32 > kmax) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) {
+            const int k0 = kp0 + (w2 >> 1) * 16 + 2 * (w2 & 1);   // the two keys of 32-bit word w2
+            uint32_t x = vr[n][w2];
+            if (k0 >= kmax) x &= 0xFFFF0000u;
+            if (k0 + 1 >= kmax) x &= 0x0000FFFFu;
+            vr[n][w2] = x;
+          }
+        }
+      }
+    }
     if constexpr (OPEN) {
       // weights against the reference maxima as they stand; a column's
       // reference is raised to its exact maximum only when a lane's eight
       // weights sum past 2^15 (or are not a number), so that every weight
       // fits fp16; one check for all blocks
-      f16x8 h[CB];
+      Weights wt[CB];
       float ps[CB];
       bool over = false;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const float sv[8] = {sc[cb][0][0], sc[cb][0][1], sc[cb][0][2], sc[cb][0][3],
                              sc[cb][1][0], sc[cb][1][1], sc[cb][1][2], sc[cb][1][3]};
-        weights(cb, sv, h[cb], ps[cb]);
+        weights(cb, sv, wt[cb], ps[cb]);
         over = over || !(ps[cb] <= 32768.f);
       }
       if (__builtin_amdgcn_ballot_w64(over)) {
@@ -488,13 +541,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           const float sv[8] = {sc[cb][0][0], sc[cb][0][1], sc[cb][0][2], sc[cb][0][3],
                                sc[cb][1][0], sc[cb][1][1], sc[cb][1][2], sc[cb][1][3]};
           raise_reference(cb, sv);
-          weights(cb, sv, h[cb], ps[cb]);
+          weights(cb, sv, wt[cb], ps[cb]);
         }
       }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         l_lane[cb] += ps[cb];
-        pv_pair(cb, h[cb], vr);
+        pv_pair(cb, wt[cb], vr);
       }
     } else {
 #pragma unroll
@@ -523,40 +576,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         // when a lane's eight weights sum past 2^15 or are not finite (the
         // first step, whose reference is -inf): no maximum at all on the
         // common path
-        f16x8 h;
+        Weights wt;
         float ps;
-        weights(cb, sv, h, ps);
+        weights(cb, sv, wt, ps);
         if (__builtin_amdgcn_ballot_w64(!(ps <= 32768.f))) {
           raise_reference(cb, sv);
-          weights(cb, sv, h, ps);
+          weights(cb, sv, wt, ps);
         }
         l_lane[cb] += ps;
-        pv_pair(cb, h, vr);
+        pv_pair(cb, wt, vr);
       }
     }
   };
 
   stage_ids(0);
   __syncthreads();
-  // tiles go in pairs (32 keys per softmax step): pair p computes from slots
-  // 2p, 2p + 1 (mod NSL), its values converted while pair p - 1 computed;
-  // pair p + 1 lands and is converted during pair p, pair p + 2 is in flight
-  // and pair p + 3 fills the slots of pair p - 1
+  // refill the slots of tiles t + i, i in [I0, I0 + 2) (the pair before
+  // the one computing)
+  auto refill = [&](int t, auto i0_tag) __attribute__((always_inline)) {
+    constexpr int I0 = decltype(i0_tag)::value;
 #pragma unroll
-  for (int i = 0; i < 6; ++i)
-    if (i < nt) issue(i);
-  // the first pair's values, before any math
-  wait_oldest_tile<LPW, 4>(min(nt, 6) - min(nt, 2));
-  if (vgrp >= 0 && vgrp < KI) convert(0);
-  lgkm_wait0();
-  wg_barrier();
-  // one pair: refill the slots of the pair before it, compute (converting
-  // the next pair), then finish this wave's LDS writes and meet the others:
-  // past the barrier every wave is done with this pair and the next one is
-  // landed and converted
-  auto advance = [&](int t, auto open_tag) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 6; i < 8; ++i) {
+    for (int i = I0; i < I0 + 2; ++i) {
       const int tn = t + i;
       if (tn < nt) {
         if (tn >= id_base + IDCAP) {
@@ -569,9 +609,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         issue(tn);
       }
     }
-    pair_step(t, open_tag);
+  };
+  // Tiles go in pairs (32 keys per softmax step).  CONV: pair p computes from
+  // slots 2p, 2p + 1 (mod 8), its values converted while pair p - 1
+  // computed; pair p + 1 lands and is converted during pair p, pair p + 2 is
+  // in flight and pair p + 3 fills the slots of pair p - 1.  Otherwise pair p
+  // computes from slots 2p, 2p + 1 (mod 6) while pair p + 1 is in flight and
+  // pair p + 2 fills the slots of pair p - 1.
+#pragma unroll
+  for (int i = 0; i < NSL - 2; ++i)
+    if (i < nt) issue(i);
+  if constexpr (CONV) {
+    // the first pair's values, before any math
+    wait_oldest_tile<LPW, 4>(min(nt, 6) - min(nt, 2));
+    if (vgrp >= 0 && vgrp < KI) convert(0);
     lgkm_wait0();
     wg_barrier();
+  }
+  auto advance = [&](int t, auto open_tag) __attribute__((always_inline)) {
+    if constexpr (CONV) {
+      // refill, compute (converting the next pair), then finish this wave's
+      // LDS writes and meet the others: past the barrier every wave is done
+      // with this pair and the next one is landed and converted
+      refill(t, std::integral_constant<int, 6>{});
+      pair_step(t, open_tag);
+      lgkm_wait0();
+      wg_barrier();
+    } else {
+      // this wave's loads of tiles t and t + 1 have landed once at most its
+      // loads of the newer tiles are outstanding; the barrier then covers
+      // every wave's share (and every wave is done with the previous pair,
+      // whose slots are refilled next)
+      wait_oldest_tile<LPW, 2>(min(nt - 1, t + 3) - min(nt - 1, t + 1));
+      wg_barrier();
+      refill(t, std::integral_constant<int, 4>{});
+      pair_step(t, open_tag);
+    }
   };
   // Pairs past the first whose keys every column of the wave sees (those
   // before the wave's first causal limit) take the open path: no causal
@@ -621,7 +694,8 @@ template <class T, int D, int BS, int G>
 hipError_t launch_g(const PrefillArgs& a, int32_t max_query_len, hipStream_t stream) {
   const int cb = prefill_column_blocks(G, max_query_len, a.num_seqs, a.num_kv_heads);
   const int tpw = 4 * cb * (16 / G);
-  const size_t lds = 8 * 2 * (D / 32) * 1024;   // the tile ring: 8 slots of K and V
+  // the tile ring: 8 slots of K and V for bf16 with three column blocks, else 6
+  const size_t lds = size_t(std::is_same_v<T, BF16> && cb == 3 ? 8 : 6) * 2 * (D / 32) * 1024;
   dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads), block(256);
   if (cb == 3) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 3>), grid, block, lds, stream, a);
   else if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2>), grid, block, lds, stream, a);
