@@ -56,6 +56,8 @@ namespace pa {
 
 namespace {
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
 // LDS reads of the ring and the block ids.  As volatile LDS accesses the
 // compiler keeps them where they are (after the explicit waits and the
 // barrier) and does not add a wait for every direct load still in flight.
