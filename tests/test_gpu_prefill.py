@@ -120,6 +120,15 @@ WIDE = {
     "mha_f16_bs8_d64": ("f16", 64, 8, 16, 16, 8, 1024, (1030, 1500)),
     "gqa8_bf16_bs32": ("bf16", 128, 32, 64, 8, 8, 256, (300, 2000)),
     "gqa16_bf16_d64": ("bf16", 64, 16, 16, 1, 8, 1024, (1024, 1300)),
+    # bf16 with three column blocks converts the values to fp16: every block
+    # size, both head dims and groups 1, 4, 8 and 16 (batches of >= 4096
+    # workgroups)
+    "gqa4_bf16_bs8_three_blocks": ("bf16", 128, 8, 32, 8, 32, 768, (770, 1000)),
+    "gqa4_bf16_bs32_three_blocks": ("bf16", 128, 32, 32, 8, 32, 768, (770, 1000)),
+    "gqa4_bf16_d64_three_blocks": ("bf16", 64, 16, 16, 4, 32, 1536, (1536, 1700)),
+    "gqa8_bf16_three_blocks": ("bf16", 128, 16, 64, 8, 16, 768, (768, 900)),
+    "gqa16_bf16_d64_three_blocks": ("bf16", 64, 16, 16, 1, 16, 3072, (3072, 3200)),
+    "mha_bf16_d64_three_blocks": ("bf16", 64, 16, 16, 16, 16, 3072, (3072, 3200)),
 }
 
 
