@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   constexpr int SLOT = 2 * KI * 1024;
   __shared__ int2 s_ids[IDCAP];
-  __shared__ int s_frame[2][4];        // per pair parity and group of 32 dims: the values' power-of-two frame
+  __shared__ __attribute__((aligned(16))) int s_frame[2][4];   // per pair parity and group of 32 dims: the values' frame
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -294,6 +294,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   for (int g = 0; g < KI; ++g) frame[g] = 0;
   int vexp = kNoExp;                             // (value loaders) largest exponent of their group so far
   uint32_t vthr = 1u;                            // and the magnitude bits from which it can change
+  int vfr = 0;                                   // and its frame
   const int vgrp = LPW == 1 ? wave - 2 : wave;   // the group of 32 value dims this wave loads (if in [0, KI))
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
@@ -317,11 +318,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // its bytes before it writes), zeros past the workgroup's last position
   // (which may hold anything, NaN poison included); bf16 values are held as
   // v 2^frame, the group's frame (see fp16_frame) published with the pair.
-  auto convert = [&](int t) __attribute__((always_inline)) {
+  constexpr int NH = 2;                          // 16-dim tiles per group
+  auto convert_read = [&](int t, u32x4 (&w)[NH]) __attribute__((always_inline)) {
     const uint8_t* sa = ring + (t % NSL) * SLOT + KI * 1024 + vgrp * 1024;
     const uint8_t* sb = ring + ((t + 1) % NSL) * SLOT + KI * 1024 + vgrp * 1024;
-    constexpr int NH = 2;                        // 16-dim tiles per group
-    u32x4 w[NH];
 #pragma unroll
     for (int n2 = 0; n2 < NH; ++n2) {
       const int d = 16 * n2 + c;                 // dim in the group
@@ -329,6 +329,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const u32x2 vb = ring_read<u32x2>(sb + d * 32 + 8 * q);
       w[n2] = u32x4{va[0], va[1], vb[0], vb[1]};
     }
+  };
+  auto convert_finish = [&](int t, u32x4 (&w)[NH]) __attribute__((always_inline)) {
     if (16 * t + 32 > kmax) {
       const int kp0 = 16 * t + 4 * q;
 #pragma unroll
@@ -365,8 +367,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         const uint32_t mb = uniform(__float_as_uint(mx));
         if (mb != 0u) vexp = uniform(max(vexp, int(mb >> 23) - 127));
         vthr = uniform(fp16_frame_threshold(vexp));
+        vfr = uniform(fp16_frame(vexp));
       }
-      const int fr = fp16_frame(vexp);
+      const int fr = vfr;
       if (fr == 0) {
 #pragma unroll
         for (int n2 = 0; n2 < NH; ++n2)
@@ -387,6 +390,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
 #pragma unroll
     for (int n2 = 0; n2 < NH; ++n2) ring_write<u32x4>(cv_tile(t, 2 * vgrp + n2) + (q * 16 + c) * 16, w[n2]);
+  };
+  auto convert = [&](int t) __attribute__((always_inline)) {
+    u32x4 w[NH];
+    convert_read(t, w);
+    convert_finish(t, w);
   };
 
   // P V of one column block over the pair: P rounded to fp16 against fp16
@@ -465,11 +473,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       // the accumulators follow the frames of the values (a change, rare,
       // only ever shrinks them, exactly but for what falls below fp32's
       // range)
+      const u32x4 f4 = ring_read<u32x4>(reinterpret_cast<const uint8_t*>(&s_frame[(t >> 1) & 1][0]));
       int fr[KI];
       bool moved = false;
 #pragma unroll
       for (int g = 0; g < KI; ++g) {
-        fr[g] = uniform(ring_read<int>(reinterpret_cast<const uint8_t*>(&s_frame[(t >> 1) & 1][g])));
+        fr[g] = uniform(int(f4[g]));
         moved = moved || fr[g] != frame[g];
       }
       if (moved) {
