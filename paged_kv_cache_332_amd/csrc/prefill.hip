@@ -682,7 +682,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         f32x4 v = acc[cb][n] * inv;
-        if constexpr (kBf16) {
+        if constexpr (CONV) {
           const int fr = frame[n >> 1];
           if (fr != 0) {
 #pragma unroll
