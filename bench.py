@@ -575,7 +575,10 @@ def next_rows(args, w, cfg, pa, runner, torch):
     out = {}
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup = 10, 8
-    for key, run in (("prefill_512", lambda: prefill_bench(_with(sub, prefill=512), w, cfg, pa, runner, torch)),
+    # (the prefill gets a longer warm-up: it follows the CPU-oracle leg, during
+    # which the GPU idled and its clock dropped; 48 launches are about 65 ms)
+    for key, run in (("prefill_512", lambda: prefill_bench(_with(sub, prefill=512, warmup=48, steps=20), w, cfg, pa,
+                                                           runner, torch)),
                      ("prefix_cache_2048", lambda: prefix_cache_bench(_with(sub, prefix_cache=2048), cfg, pa, torch)),
                      ("swap_half_batch", lambda: swap_bench(_with(sub, swap=0.5), w, cfg, pa, runner, torch))):
         print(f"[bench] next row: {key}", file=sys.stderr, flush=True)
