@@ -129,6 +129,9 @@ WIDE = {
     "gqa8_bf16_three_blocks": ("bf16", 128, 16, 64, 8, 16, 768, (768, 900)),
     "gqa16_bf16_d64_three_blocks": ("bf16", 64, 16, 16, 1, 16, 3072, (3072, 3200)),
     "mha_bf16_d64_three_blocks": ("bf16", 64, 16, 16, 16, 16, 3072, (3072, 3200)),
+    # contexts past 512 tiles: the block ids are staged again inside the
+    # conversion pipeline
+    "gqa4_bf16_long_three_blocks": ("bf16", 128, 16, 32, 8, 8, 3072, (8400, 9200)),
 }
 
 
