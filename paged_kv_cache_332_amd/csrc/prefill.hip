@@ -535,30 +535,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       // weights against the reference maxima as they stand; a column's
       // reference is raised to its exact maximum only when a lane's eight
       // weights sum past 2^15 (or are not a number), so that every weight
-      // fits fp16; one check for all blocks
-      Weights wt[CB];
-      float ps[CB];
-      bool over = false;
+      // fits fp16; one check per block, so that the P V products of a block
+      // overlap the vector work of the next
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const float sv[8] = {sc[cb][0][0], sc[cb][0][1], sc[cb][0][2], sc[cb][0][3],
                              sc[cb][1][0], sc[cb][1][1], sc[cb][1][2], sc[cb][1][3]};
-        weights(cb, sv, wt[cb], ps[cb]);
-        over = over || !(ps[cb] <= 32768.f);
-      }
-      if (__builtin_amdgcn_ballot_w64(over)) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const float sv[8] = {sc[cb][0][0], sc[cb][0][1], sc[cb][0][2], sc[cb][0][3],
-                               sc[cb][1][0], sc[cb][1][1], sc[cb][1][2], sc[cb][1][3]};
+        Weights wt;
+        float ps;
+        weights(cb, sv, wt, ps);
+        if (__builtin_amdgcn_ballot_w64(!(ps <= 32768.f))) {
           raise_reference(cb, sv);
-          weights(cb, sv, wt[cb], ps[cb]);
+          weights(cb, sv, wt, ps);
         }
-      }
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        l_lane[cb] += ps[cb];
-        pv_pair(cb, wt[cb], vr);
+        l_lane[cb] += ps;
+        pv_pair(cb, wt, vr);
       }
     } else {
 #pragma unroll
