@@ -306,8 +306,13 @@ def prefill_bench(args, w, cfg, pa, runner, torch):
     qs_d = torch.from_numpy(qs).to("cuda")
     ctx_d = torch.from_numpy(ctx.astype(np.int32)).to("cuda")
     scale = 1.0 / cfg.head_dim ** 0.5
+    # the workspace lets launches of few workgroups (short chunks) split each
+    # context into pieces merged by log-sum-exp
+    ws_bytes = pa.pa_prefill_workspace_bytes(int(chunk.max()), int(ctx.max()), cfg.num_seqs, cfg.num_q_heads,
+                                             cfg.num_kv_heads, cfg.head_dim)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
     run = lambda: pa.pa_prefill(out, q, eng.k_cache, eng.v_cache, tab_d, qs_d, ctx_d, int(chunk.max()),
-                                int(ctx.max()), scale)
+                                int(ctx.max()), scale, workspace=ws)
     for _ in range(args.warmup):
         run()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -343,7 +348,7 @@ def prefill_bench(args, w, cfg, pa, runner, torch):
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": args.config, "batch": cfg.num_seqs, "chunk": int(args.prefill),
                    "query_tokens": T, "ctx_mean": round(float(ctx.mean()), 1)},
-        "column_blocks_per_wave": cb,
+        "column_blocks_per_wave": cb, "context_split_workspace_bytes": int(ws_bytes),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4), "kv_bytes_streamed": int(kv_bytes),
                      "kv_GBps": round(kv_bytes / (us * 1e-6) / 1e9, 1)},
@@ -466,8 +471,10 @@ def prefix_cache_bench(args, cfg, pa, torch):
         out = torch.empty((T, hq, d), dtype=torch.float32, device="cuda")
         tab_d = torch.from_numpy(np.ascontiguousarray(tab)).to("cuda")
         qs_d, ctx_d = torch.from_numpy(qs).to("cuda"), torch.from_numpy(np.asarray(ctx, np.int32)).to("cuda")
+        nb = pa.pa_prefill_workspace_bytes(int(max(chunks)), int(max(ctx)), len(seqs), hq, eng.H, d)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
         fn = lambda: pa.pa_prefill(out, q, eng.k_cache, eng.v_cache, tab_d, qs_d, ctx_d, int(max(chunks)),
-                                   int(max(ctx)), 1.0 / d ** 0.5)
+                                   int(max(ctx)), 1.0 / d ** 0.5, workspace=ws)
         for _ in range(3):
             fn()
         steps = max(1, min(args.steps, 20))

@@ -370,14 +370,28 @@ pa_status pa_swap_blocks(void* k_cache, void* v_cache, void* host_k, void* host_
  * max_context_len (>= every context length, <= table_stride * block_size)
  * are host bounds that size the grid; device lengths are clamped to them.
  * 16-bit caches only (PA_ERR_UNSUPPORTED for F32); group in {1,2,4,8,16};
- * at most 65535 (sequence, kv head) pairs.  No workspace.  Asynchronous on
- * `stream`.
+ * at most 65535 (sequence, kv head) pairs.
+ * workspace (device, 16-byte aligned, caller-owned, any contents; may be
+ * NULL): with it, a launch of few workgroups (short chunks, where one
+ * workgroup would stream a whole context) splits each sequence's prefix
+ * into pieces and merges their partial states by log-sum-exp (the same
+ * softmax, summed in another order); it must then hold
+ * pa_prefill_workspace_bytes(...) bytes (PA_ERR_INVALID if smaller).  NULL,
+ * or a shape the library does not split, streams each context in one piece.
+ * Asynchronous on `stream`.
  * ---------------------------------------------------------------------- */
 pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,
                      pa_dtype kv_dtype, const int32_t* block_tables, int32_t table_stride,
                      const int32_t* query_start, const int32_t* context_lens, int32_t max_query_len,
                      int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, void* stream);
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_prefill's context split needs for a launch of this
+ * shape (same bounds as the call); 0 when the library streams each context
+ * in one piece (or the shape is invalid). */
+size_t pa_prefill_workspace_bytes(int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
 
 /* ------------------------------------------------------------------------
  * pa_step — one decode step of a batch, host and device parts in one call:

@@ -24,7 +24,8 @@ __all__ = [
     "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
     "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version", "pa_step",
     "pa_decode_stream_grid", "pa_decode_noalloc", "step_record_words", "step_args", "step_call",
-    "stream_class_finish", "pa_stream_plan", "pa_prefill", "pa_swap_blocks", "pa_step_layer",
+    "stream_class_finish", "pa_stream_plan", "pa_prefill", "pa_prefill_workspace_bytes", "pa_swap_blocks",
+    "pa_step_layer",
     "STEP_KV", "STEP_PASS", "STEP_MERGE", "STEP_ALL",
 ]
 
@@ -63,7 +64,8 @@ _sig("pa_decode_variant", _i32, *_DECODE_ARGS, _i32)
 _sig("pa_decode_phase", _i32, *_DECODE_ARGS, _i32, _i32)
 _sig("pa_decode_noalloc", _i32, *_DECODE_ARGS[:18], _vp)
 _sig("pa_prefill", _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
-     _i32, _i32, _f32, _vp)
+     _i32, _i32, _f32, _vp, _sz, _vp)
+_sig("pa_prefill_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32)
 _sig("pa_bm_create", _vp, _i32, _i32, _pi32)
 _sig("pa_bm_destroy", None, _vp)
 _sig("pa_bm_add_seq", _i32, _vp, _i64, _i32, _pi32)
@@ -246,16 +248,26 @@ def pa_swap_blocks(k_cache, v_cache, host_k, host_v, blocks, to_host: bool, stre
 
 
 def pa_prefill(out, q, k_cache, v_cache, block_tables, query_start, context_lens, max_query_len: int,
-               max_context_len: int, scale: float, stream=None) -> None:
+               max_context_len: int, scale: float, stream=None, workspace=None) -> None:
     """Causal attention of the chunks q[query_start[i]:query_start[i+1]] over
     their sequences' paged context (see pa_prefill in pa.h).  Tensors on the
-    device; query_start / context_lens int32."""
+    device; query_start / context_lens int32; workspace (uint8, device, at
+    least pa_prefill_workspace_bytes(...) bytes) lets short chunks split
+    their contexts."""
     n_, hkv, d, bs = _pool_dims(k_cache, v_cache)
     _check(lib.pa_prefill(out.data_ptr(), torch_dtype_code(out.dtype), q.data_ptr(), k_cache.data_ptr(),
                           v_cache.data_ptr(), torch_dtype_code(k_cache.dtype), block_tables.data_ptr(),
                           int(block_tables.shape[1]), query_start.data_ptr(), context_lens.data_ptr(),
                           int(max_query_len), int(max_context_len), int(context_lens.shape[0]), int(q.shape[1]), hkv,
-                          d, bs, n_, float(scale), _stream(stream)))
+                          d, bs, n_, float(scale), None if workspace is None else workspace.data_ptr(),
+                          0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def pa_prefill_workspace_bytes(max_query_len: int, max_context_len: int, num_seqs: int, num_q_heads: int,
+                               num_kv_heads: int, head_dim: int) -> int:
+    """Bytes of workspace pa_prefill's context split needs (0: no split)."""
+    return int(lib.pa_prefill_workspace_bytes(int(max_query_len), int(max_context_len), int(num_seqs),
+                                              int(num_q_heads), int(num_kv_heads), int(head_dim)))
 
 
 def pa_step(bm: "BlockManager", seqs_i64: np.ndarray, stage_host, stage_dev, table_stride: int, k_cache, v_cache,

@@ -415,7 +415,8 @@ pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k
                      pa_dtype kv_dtype, const int32_t* block_tables, int32_t table_stride,
                      const int32_t* query_start, const int32_t* context_lens, int32_t max_query_len,
                      int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, void* stream) {
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   const char* fn = "pa_prefill";
   if (pa_status st = pa::check_cache_shape(fn, num_kv_heads, head_dim, block_size, num_blocks, kv_dtype)) return st;
   if (kv_dtype == PA_F32) return pa::fail(PA_ERR_UNSUPPORTED, "%s: the prefill kernel needs a 16-bit cache", fn);
@@ -457,8 +458,34 @@ pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k
   a.num_kv_heads = num_kv_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out_f32 = out_dtype == PA_F32;
+  if (workspace) {
+    const pa::PrefillSplit sp = pa::prefill_split(group, max_query_len, max_context_len, num_seqs, num_q_heads,
+                                                  num_kv_heads, head_dim);
+    if (sp.split_tiles) {
+      if (workspace_bytes < sp.bytes)
+        return pa::fail(PA_ERR_INVALID, "%s: workspace of %zu bytes, the context split needs %zu", fn,
+                        workspace_bytes, sp.bytes);
+      if (!pa::aligned16(workspace)) return pa::fail(PA_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+      a.split_tiles = sp.split_tiles;
+      a.split_max = sp.split_max;
+      a.rows_per_seq = sp.rows_per_seq;
+      a.ws_ml = static_cast<float*>(workspace);
+      a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + sp.ml_bytes);
+    }
+  }
   return pa::hip_status(fn, pa::launch_prefill(a, kv_dtype, head_dim, block_size, group, max_query_len,
                                                static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_prefill_workspace_bytes(int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  if (max_query_len <= 0 || max_context_len <= 0 || num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || num_q_heads % num_kv_heads)
+    return 0;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return 0;
+  return pa::prefill_split(group, max_query_len, max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim)
+      .bytes;
 }
 
 pa_status pa_decode(void* out, pa_dtype out_dtype, const void* q, const void* k_cache, const void* v_cache,

@@ -168,6 +168,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int p0 = P - L;                          // position of the chunk's first token
   const int kmax = p0 + min(L, tq0 + TQW);       // positions the workgroup's tokens see
   const int nt = (kmax + 15) / 16;
+  // Context split (asked for by the launch, for launches with few
+  // workgroups): piece z of S streams tiles [z SPL, (z + 1) SPL) and the last
+  // one every tile from (S - 1) SPL on.  The pieces but the last end before
+  // the chunk's first position, so every column sees every key of those and
+  // the first key of the last one.  A split sequence leaves each piece's
+  // partial state in the workspace for the merge.
+  const int S = a.split_tiles ? p0 / (16 * a.split_tiles) + 1 : 1;
+  if (int(blockIdx.z) >= S) return;                 // (whole workgroup)
+  const int zp = S - 1 - int(blockIdx.z);           // the longest piece first
+  const int tb = zp * a.split_tiles;                // tiles [tb, te) (tb even)
+  const int te = zp == S - 1 ? nt : tb + a.split_tiles;
 
   // this lane's column in block cb: token cb TB + j of the wave, head gc of
   // the group
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // block ids of tiles [from, from + IDCAP) (the whole workgroup)
   int id_base = 0;
   auto stage_ids = [&](int from) {
-    const int n = min(IDCAP, nt - from);
+    const int n = min(IDCAP, te - from);
     for (int i = threadIdx.x; i < n; i += 256) {
       const int t = from + i;
       int2 ids;
@@ -497,8 +508,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // two pairs after it may stay in flight), its values are converted, the
     // vector work overlapping this pair's matrix products
     if constexpr (CONV) {
-      if (t + 2 < nt) {
-        wait_oldest_tile<LPW, 4>(min(nt, t + 8) - min(nt, t + 4));
+      if (t + 2 < te) {
+        wait_oldest_tile<LPW, 4>(min(te, t + 8) - min(te, t + 4));
         if (vgrp >= 0 && vgrp < KI) convert(t + 2);
       }
     }
@@ -591,7 +602,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   };
 
-  stage_ids(0);
+  stage_ids(tb);
   __syncthreads();
   // refill the slots of tiles t + i, i in [I0, I0 + 2) (the pair before
   // the one computing)
@@ -600,7 +611,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int i = I0; i < I0 + 2; ++i) {
       const int tn = t + i;
-      if (tn < nt) {
+      if (tn < te) {
         if (tn >= id_base + IDCAP) {
           // next window of block ids (every slot's loads have landed: the
           // compiler waits for the table reads before the LDS writes)
@@ -620,11 +631,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // pair p + 2 fills the slots of pair p - 1.
 #pragma unroll
   for (int i = 0; i < NSL - 2; ++i)
-    if (i < nt) issue(i);
+    if (tb + i < te) issue(tb + i);
   if constexpr (CONV) {
     // the first pair's values, before any math
-    wait_oldest_tile<LPW, 4>(min(nt, 6) - min(nt, 2));
-    if (vgrp >= 0 && vgrp < KI) convert(0);
+    wait_oldest_tile<LPW, 4>(min(te, tb + 6) - min(te, tb + 2));
+    if (vgrp >= 0 && vgrp < KI) convert(tb);
     lgkm_wait0();
     wg_barrier();
   }
@@ -642,7 +653,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       // loads of the newer tiles are outstanding; the barrier then covers
       // every wave's share (and every wave is done with the previous pair,
       // whose slots are refilled next)
-      wait_oldest_tile<LPW, 2>(min(nt - 1, t + 3) - min(nt - 1, t + 1));
+      wait_oldest_tile<LPW, 2>(min(te - 1, t + 3) - min(te - 1, t + 1));
       wg_barrier();
       refill(t, std::integral_constant<int, 4>{});
       pair_step(t, open_tag);
@@ -657,17 +668,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // diagonal on take the general path: a causal limit per column, blocks
   // past their last position skipped, and a missing tile t + 1 read from a
   // stale slot with every score masked and every value selected to zero.
-  const int open_end = max(2, (blk_open[0] - 32) / 16 + 1);   // first t (even or odd) not open
-  int t = 0;
+  const int open_end = min(te, max(tb + 2, (blk_open[0] - 32) / 16 + 1));   // first t (even or odd) not open
+  int t = tb;
   advance(t, std::false_type{});
-  for (t = 2; t < open_end; t += 2) advance(t, std::true_type{});
-  for (; t < nt; t += 2) advance(t, std::false_type{});
+  for (t = tb + 2; t < open_end; t += 2) advance(t, std::true_type{});
+  for (; t < te; t += 2) advance(t, std::false_type{});
 
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     float l = xor16<OpSum>(l_lane[cb]);
     l = xor32<OpSum>(l);
-    if (col_valid[cb]) {
+    if (col_valid[cb] && S > 1) {
+      // this piece's partial state: reference maximum and sum of the column,
+      // and its unnormalised output (the frames taken out)
+      const int64_t prow =
+          ((int64_t(zp) * a.num_seqs + s) * a.rows_per_seq + tw0 + cb * TB + j) * Hq + int64_t(h) * G + gc;
+      if (q == 0) *reinterpret_cast<float2*>(a.ws_ml + 2 * prow) = float2{m_ref[cb], l};
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        f32x4 v = acc[cb][n];
+        if constexpr (CONV) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_ldexpf(v[i], -frame[n >> 1]);
+        }
+        *reinterpret_cast<f32x4*>(a.ws_acc + prow * D + 16 * n + 4 * q) = v;
+      }
+    } else if (col_valid[cb]) {
       const float inv = 1.f / l;
       const int64_t o = qrow[cb] * D + 4 * q;
 #pragma unroll
@@ -692,16 +718,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
 }
 
+// Log-sum-exp merge of the pieces of each split sequence: for every query
+// token and head
+//     M = max_z m_z,  out = sum_z 2^(m_z - M) acc_z / sum_z 2^(m_z - M) l_z
+// over its pieces in order (the same pieces as the prefill kernel's, from the
+// same lengths).  One thread per 4 output columns; grid y = sequences.
+template <class T, int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
+  using bits = typename T::bits;
+  const int s = blockIdx.y;
+  const int Hq = a.num_q_heads;
+  const int qs = a.query_start[s];
+  const int P = min(max(a.ctx[s], 0), a.max_ctx);
+  const int L = min(max(a.query_start[s + 1] - qs, 0), P);
+  const int S = (P - L) / (16 * a.split_tiles) + 1;
+  if (S == 1) return;                            // written by the prefill kernel
+  constexpr int U = D / 4;
+  const int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int tok = int(u / (int64_t(Hq) * U));
+  if (tok >= L || tok >= a.rows_per_seq) return;
+  const int r = int(u % (int64_t(Hq) * U));
+  const int hd = r / U, d4 = r % U;
+  float M = kNegInf, l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int z = 0; z < S; ++z) {
+    const int64_t prow = ((int64_t(z) * a.num_seqs + s) * a.rows_per_seq + tok) * Hq + hd;
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + 2 * prow);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(a.ws_acc + prow * D + 4 * d4);
+    if (ml.x == kNegInf) continue;               // (no key: cannot happen, every piece has one)
+    const float mn = fmaxf(M, ml.x);
+    const float c0 = M == kNegInf ? 0.f : fast_exp2(M - mn);
+    const float c1 = fast_exp2(ml.x - mn);
+    l = l * c0 + ml.y * c1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = o[i] * c0 + v[i] * c1;
+    M = mn;
+  }
+  const float inv = 1.f / l;
+  const int64_t off = (int64_t(qs + tok) * Hq + hd) * D + 4 * d4;
+  if (a.out_f32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + off) = o * inv;
+  } else {
+    const uint32_t lo = T::from_f32(o[0] * inv) | (T::from_f32(o[1] * inv) << 16);
+    const uint32_t hi = T::from_f32(o[2] * inv) | (T::from_f32(o[3] * inv) << 16);
+    *reinterpret_cast<u32x2*>(static_cast<bits*>(a.out) + off) = u32x2{lo, hi};
+  }
+}
+
 template <class T, int D, int BS, int G>
 hipError_t launch_g(const PrefillArgs& a, int32_t max_query_len, hipStream_t stream) {
   const int cb = prefill_column_blocks(G, max_query_len, a.num_seqs, a.num_kv_heads);
   const int tpw = 4 * cb * (16 / G);
   // the tile ring: 8 slots of K and V for bf16 with three column blocks, else 6
   const size_t lds = size_t(std::is_same_v<T, BF16> && cb == 3 ? 8 : 6) * 2 * (D / 32) * 1024;
-  dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads), block(256);
+  // (pieces of a split context along z, the longest first)
+  dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads, a.split_tiles ? a.split_max : 1),
+      block(256);
   if (cb == 3) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 3>), grid, block, lds, stream, a);
   else if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2>), grid, block, lds, stream, a);
   else hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1>), grid, block, lds, stream, a);
+  if (hipError_t e = hipGetLastError()) return e;
+  if (!a.split_tiles) return hipSuccess;
+  const int64_t units = int64_t(a.rows_per_seq) * a.num_q_heads * (D / 4);
+  hipLaunchKernelGGL((prefill_merge_kernel<T, D>), dim3(static_cast<uint32_t>((units + 255) / 256), a.num_seqs),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

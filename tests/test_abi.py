@@ -459,21 +459,41 @@ def test_stream_plan_rejects_bad_input():
 def _prefill_args(**over):
     a = dict(out=16, out_dtype=pa.PA_F32, q=16, k=16, v=16, kv_dtype=pa.PA_BF16, tables=16, stride=256,
              qs=16, ctx=16, max_q=512, max_ctx=4096, B=64, Hq=32, Hkv=8, D=128, BS=16, N=1000, scale=0.1,
-             stream=0)
+             ws=None, ws_bytes=0, stream=0)
     a.update(over)
     return [a[k] for k in ["out", "out_dtype", "q", "k", "v", "kv_dtype", "tables", "stride", "qs", "ctx",
-                           "max_q", "max_ctx", "B", "Hq", "Hkv", "D", "BS", "N", "scale", "stream"]]
+                           "max_q", "max_ctx", "B", "Hq", "Hkv", "D", "BS", "N", "scale", "ws", "ws_bytes", "stream"]]
 
 
 @pytest.mark.parametrize("over,status", [
     (dict(kv_dtype=pa.PA_F32), 4), (dict(D=96), 4), (dict(Hq=24, Hkv=8), 4), (dict(Hq=12, Hkv=8), 1),
     (dict(out_dtype=pa.PA_F16), 1), (dict(max_q=5000), 1), (dict(stride=10), 1), (dict(q=8), 1),
     (dict(qs=0), 1), (dict(B=10000), 4),
+    (dict(max_q=16, B=8, ws=16, ws_bytes=100), 1),      # short chunks of 8 sequences split: workspace too small
+    (dict(max_q=16, B=8, ws=8, ws_bytes=1 << 30), 1),   # workspace not 16-byte aligned
 ])
 def test_prefill_rejects_bad_arguments(over, status):
     """Host validation of pa_prefill, before any launch."""
     assert pa.lib.pa_prefill(*_prefill_args(**over)) == status
     assert pa.lib.pa_last_error()
+
+
+def test_prefill_workspace_bytes():
+    """The context split is asked for only where few workgroups would run
+    (fewer than two per compute unit; one per sequence, kv head and query
+    block), and holds at least two pieces' partial states for every query row
+    it covers."""
+    Hq, Hkv, D = 32, 8, 128
+    assert pa.pa_prefill_workspace_bytes(512, 4160, 64, Hq, Hkv, D) == 0      # 5632 workgroups
+    assert pa.pa_prefill_workspace_bytes(16, 4160, 64, Hq, Hkv, D) == 0       # 512 workgroups
+    short = pa.pa_prefill_workspace_bytes(16, 131072, 8, Hq, Hkv, D)         # 64 workgroups
+    assert short >= 2 * 8 * 16 * Hq * (D + 2) * 4
+    # a longer bound never needs less; a context of one piece has nothing to split
+    assert pa.pa_prefill_workspace_bytes(16, 262144, 8, Hq, Hkv, D) >= short
+    assert pa.pa_prefill_workspace_bytes(16, 512, 8, Hq, Hkv, D) == 0
+    # shapes pa_prefill rejects need none
+    assert pa.pa_prefill_workspace_bytes(16, 131072, 8, 24, Hkv, D) == 0
+    assert pa.pa_prefill_workspace_bytes(0, 131072, 8, Hq, Hkv, D) == 0
 
 
 def _swap_args(**over):

@@ -322,3 +322,126 @@ def test_prefill_values_far_from_one():
         say("sequence", i, "max error relative to the values seen", float(rel.max()))
         worst = max(worst, float(rel.max()))
     assert worst <= 2e-3
+
+
+# ------------------------------------------------------------ context split
+def _prefill_run(pa, eng, q_dev, tab, qs, ctx, chunk, scale, split, out_dtype=torch.float32):
+    """pa_prefill of the chunks, with the workspace its context split asks for
+    (split=True; the shape must ask for one) or without (one piece each)."""
+    T, hq, d = q_dev.shape
+    ws = None
+    if split:
+        nbytes = pa.pa_prefill_workspace_bytes(max(chunk), max(ctx), len(ctx), hq, eng.H, d)
+        assert nbytes > 0, "this shape does not split"
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.full((T, hq, d), float("nan"), dtype=out_dtype, device="cuda")
+    pa.pa_prefill(out, q_dev, eng.k_cache, eng.v_cache, torch.from_numpy(np.ascontiguousarray(tab)).to("cuda"),
+                  torch.from_numpy(np.asarray(qs, np.int32)).to("cuda"),
+                  torch.from_numpy(np.asarray(ctx, np.int32)).to("cuda"), max(chunk), max(ctx), scale, workspace=ws)
+    return out
+
+
+# launches of fewer than 512 workgroups (two per compute unit), which split:
+# dtype, head_dim, block size, q heads, kv heads, context lengths, chunk lengths
+SPLIT_RANDOM = {
+    "gqa4_bf16_bs16": ("bf16", 128, 16, 8, 2, [300, 17, 1, 2049, 64], [300, 5, 1, 100, 64]),
+    "gqa8_bf16_bs32": ("bf16", 128, 32, 32, 4, [1000, 260], [250, 1]),
+    "long_context_bf16": ("bf16", 128, 16, 32, 8, [9000, 300], [64, 300]),
+    "mha_f16_d64_bs8": ("f16", 64, 8, 8, 8, [3000, 129, 7, 1500], [40, 33, 7, 1]),
+    "gqa16_bf16_d64": ("bf16", 64, 16, 16, 1, [2000, 33], [77, 20]),
+}
+
+
+@pytest.mark.parametrize("case", list(SPLIT_RANDOM))
+def test_prefill_context_split_matches_oracle(case):
+    """With a workspace, launches of few workgroups split each sequence's
+    prefix into pieces of at least 32 tiles and merge them by log-sum-exp
+    (these cases cut their longer contexts into 2 to 7 pieces): within 2e-3 of
+    the oracle, and the 16-bit output is the fp32 one rounded."""
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    dtype, d, bs, hq, hkv, ctx, chunk = SPLIT_RANDOM[case]
+    say("prefill split", case)
+    w = W.tiny(num_seqs=len(ctx), dtype=dtype, seed=41, ctx=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+               block_size=bs)
+    dev = runner.run_script(w, decode=False)
+    eng = dev.engine
+    tab, _ = eng.bm.export(list(range(len(ctx))), eng.stride)
+    rng = np.random.default_rng([41, len(ctx)])
+    T = int(sum(chunk))
+    q = W.round_to_dtype(rng.standard_normal((T, hq, d), dtype=np.float32), dtype)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    tdt = runner.TORCH_DTYPE[dtype]
+    q_dev = torch.from_numpy(q).to("cuda").to(tdt)
+    scale = 1.0 / d ** 0.5
+    out = _prefill_run(pa, eng, q_dev, tab, qs, ctx, chunk, scale, True)
+    out_h = _prefill_run(pa, eng, q_dev, tab, qs, ctx, chunk, scale, True, out_dtype=tdt)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = 0.0
+    for i, n in enumerate(ctx):
+        rows = w.row_of(i, np.arange(n))
+        ref = oracle.prefill_attention(q[qs[i]: qs[i + 1]], w.k_rows[rows], w.v_rows[rows], scale)
+        err = max(err, float(np.max(np.abs(got[qs[i]: qs[i + 1]] - ref))))
+    say(case, "split: max abs error", err)
+    assert err <= 2e-3
+    assert torch.equal(out_h, out.to(tdt))
+
+
+# contexts, chunks, q heads, kv heads, head dim, block size, dtype
+SPLIT_CODED = {
+    # chunks of at most 16 tokens: one query block per (sequence, kv head),
+    # pieces of 32 tiles, up to 18 of them
+    "short_bf16_bs16": ([9000, 17, 2049, 300, 4097, 1, 4112, 4111], [16, 5, 16, 16, 1, 1, 16, 16], 32, 8, 128, 16,
+                        "bf16"),
+    # longer chunks beside short ones: pieces of 114 tiles, the chunk's
+    # query blocks in the last piece
+    "mixed_bf16_bs16": ([9000, 17, 2049, 300, 4097, 1], [16, 5, 100, 300, 16, 1], 16, 4, 128, 16, "bf16"),
+    "short_f16_d64_bs8": ([6000, 257, 1, 3001], [8, 8, 1, 3], 16, 4, 64, 8, "f16"),
+    "short_bf16_g16_bs32": ([5000, 640, 33], [1, 16, 16], 16, 1, 128, 32, "bf16"),
+}
+
+
+@pytest.mark.parametrize("case", list(SPLIT_CODED))
+def test_prefill_context_split_counts_every_tile_once(case):
+    """Keys identical within each kv head and position-coded values
+    V[t][h][c] = (t + 5h + c) mod 128 - 64: every weight is exactly 2^0, so
+    each query token's output is the mean of V over its prefix, and every
+    partial sum is an integer exact in fp32 in any order (pieces and merge
+    included: every piece has the same reference, so the merge scales by 1).
+    Split and unsplit launches both give the oracle's result within 1e-4; a
+    tile dropped or counted twice moves an output by at least 16 x 63.5 /
+    9000 = 0.11, one token past a prefix by at least 63.5 / 9000 = 7e-3."""
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    ctx, chunk, hq, hkv, d, bs, dtype = SPLIT_CODED[case]
+    say("prefill split position coded", case)
+    w = W.tiny(num_seqs=len(ctx), dtype=dtype, seed=43, ctx=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+               block_size=bs)
+    rng = np.random.default_rng([902, len(ctx)])
+    R = int(np.sum(w.ctx))
+    kvec = W.round_to_dtype(rng.standard_normal((1, hkv, d), dtype=np.float32), dtype)
+    w.k_rows = np.broadcast_to(kvec, (R, hkv, d))
+    pos = np.concatenate([np.arange(int(n), dtype=np.int64) for n in w.ctx])
+    code = 5 * np.arange(hkv)[None, :, None] + np.arange(d)[None, None, :]
+    w.v_rows = ((pos[:, None, None] + code) % 128 - 64).astype(np.float32)
+    dev = runner.run_script(w, decode=False)
+    eng = dev.engine
+    tab, _ = eng.bm.export(list(range(len(ctx))), eng.stride)
+    T = int(sum(chunk))
+    q = W.round_to_dtype(rng.standard_normal((T, hq, d), dtype=np.float32), dtype)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    q_dev = torch.from_numpy(q).to("cuda").to(runner.TORCH_DTYPE[dtype])
+    scale = 1.0 / d ** 0.5
+    outs = {"split": _prefill_run(pa, eng, q_dev, tab, qs, ctx, chunk, scale, True),
+            "one piece": _prefill_run(pa, eng, q_dev, tab, qs, ctx, chunk, scale, False)}
+    torch.cuda.synchronize()
+    want = np.concatenate([
+        oracle.prefill_attention(q[qs[i]: qs[i + 1]], w.k_rows[w.row_of(i, np.arange(n))],
+                                 w.v_rows[w.row_of(i, np.arange(n))], scale)
+        for i, n in enumerate(ctx)])
+    for label, o in outs.items():
+        err = float(np.max(np.abs(o.double().cpu().numpy() - want)))
+        say(case, label, "max abs error", err)
+        assert err <= 1e-4, f"{case} {label}: max abs error {err:.3e}"
