@@ -11,6 +11,7 @@
 
 #include "pa_internal.h"
 #include "pa_kernels.h"
+#include "prefill_split.h"
 
 namespace pa {
 
@@ -458,6 +459,7 @@ pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k
   a.num_kv_heads = num_kv_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out_f32 = out_dtype == PA_F32;
+  pa::PrefillSplitArgs sa;
   if (workspace) {
     const pa::PrefillSplit sp = pa::prefill_split(group, max_query_len, max_context_len, num_seqs, num_q_heads,
                                                   num_kv_heads, head_dim);
@@ -466,15 +468,15 @@ pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k
         return pa::fail(PA_ERR_INVALID, "%s: workspace of %zu bytes, the context split needs %zu", fn,
                         workspace_bytes, sp.bytes);
       if (!pa::aligned16(workspace)) return pa::fail(PA_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
-      a.split_tiles = sp.split_tiles;
-      a.split_max = sp.split_max;
-      a.rows_per_seq = sp.rows_per_seq;
-      a.ws_ml = static_cast<float*>(workspace);
-      a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + sp.ml_bytes);
+      sa.split_tiles = sp.split_tiles;
+      sa.split_max = sp.split_max;
+      sa.rows_per_seq = sp.rows_per_seq;
+      sa.ws_ml = static_cast<float*>(workspace);
+      sa.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + sp.ml_bytes);
     }
   }
-  return pa::hip_status(fn, pa::launch_prefill(a, kv_dtype, head_dim, block_size, group, max_query_len,
-                                               static_cast<hipStream_t>(stream)));
+  return pa::hip_status(fn, pa::launch_prefill_split(a, sa, kv_dtype, head_dim, block_size, group, max_query_len,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 size_t pa_prefill_workspace_bytes(int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,

@@ -51,6 +51,7 @@
 
 #include "pa_device.h"
 #include "pa_kernels.h"
+#include "prefill_split.h"
 
 namespace pa {
 
@@ -122,7 +123,7 @@ __device__ __forceinline__ void wait_oldest_tile(int k) {
 }
 
 template <class T, int D, int BS, int G, int CB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a, PrefillSplitArgs sp) {
   using bits = typename T::bits;
   using MF = MfmaOps<T>;
   using PV = MfmaOps<F16>;             // P V in fp16 whatever the cache type
@@ -174,11 +175,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // the chunk's first position, so every column sees every key of those and
   // the first key of the last one.  A split sequence leaves each piece's
   // partial state in the workspace for the merge.
-  const int S = a.split_tiles ? p0 / (16 * a.split_tiles) + 1 : 1;
+  const int S = sp.split_tiles ? p0 / (16 * sp.split_tiles) + 1 : 1;
   if (int(blockIdx.z) >= S) return;                 // (whole workgroup)
   const int zp = S - 1 - int(blockIdx.z);           // the longest piece first
-  const int tb = zp * a.split_tiles;                // tiles [tb, te) (tb even)
-  const int te = zp == S - 1 ? nt : tb + a.split_tiles;
+  const int tb = zp * sp.split_tiles;                // tiles [tb, te) (tb even)
+  const int te = zp == S - 1 ? nt : tb + sp.split_tiles;
 
   // this lane's column in block cb: token cb TB + j of the wave, head gc of
   // the group
@@ -682,8 +683,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       // this piece's partial state: reference maximum and sum of the column,
       // and its unnormalised output (the frames taken out)
       const int64_t prow =
-          ((int64_t(zp) * a.num_seqs + s) * a.rows_per_seq + tw0 + cb * TB + j) * Hq + int64_t(h) * G + gc;
-      if (q == 0) *reinterpret_cast<float2*>(a.ws_ml + 2 * prow) = float2{m_ref[cb], l};
+          ((int64_t(zp) * a.num_seqs + s) * sp.rows_per_seq + tw0 + cb * TB + j) * Hq + int64_t(h) * G + gc;
+      if (q == 0) *reinterpret_cast<float2*>(sp.ws_ml + 2 * prow) = float2{m_ref[cb], l};
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         f32x4 v = acc[cb][n];
@@ -691,7 +692,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_ldexpf(v[i], -frame[n >> 1]);
         }
-        *reinterpret_cast<f32x4*>(a.ws_acc + prow * D + 16 * n + 4 * q) = v;
+        *reinterpret_cast<f32x4*>(sp.ws_acc + prow * D + 16 * n + 4 * q) = v;
       }
     } else if (col_valid[cb]) {
       const float inv = 1.f / l;
@@ -724,27 +725,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // over its pieces in order (the same pieces as the prefill kernel's, from the
 // same lengths).  One thread per 4 output columns; grid y = sequences.
 template <class T, int D>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, PrefillSplitArgs sp) {
   using bits = typename T::bits;
   const int s = blockIdx.y;
   const int Hq = a.num_q_heads;
   const int qs = a.query_start[s];
   const int P = min(max(a.ctx[s], 0), a.max_ctx);
   const int L = min(max(a.query_start[s + 1] - qs, 0), P);
-  const int S = (P - L) / (16 * a.split_tiles) + 1;
+  const int S = (P - L) / (16 * sp.split_tiles) + 1;
   if (S == 1) return;                            // written by the prefill kernel
   constexpr int U = D / 4;
   const int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int tok = int(u / (int64_t(Hq) * U));
-  if (tok >= L || tok >= a.rows_per_seq) return;
+  if (tok >= L || tok >= sp.rows_per_seq) return;
   const int r = int(u % (int64_t(Hq) * U));
   const int hd = r / U, d4 = r % U;
   float M = kNegInf, l = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   for (int z = 0; z < S; ++z) {
-    const int64_t prow = ((int64_t(z) * a.num_seqs + s) * a.rows_per_seq + tok) * Hq + hd;
-    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + 2 * prow);
-    const f32x4 v = *reinterpret_cast<const f32x4*>(a.ws_acc + prow * D + 4 * d4);
+    const int64_t prow = ((int64_t(z) * a.num_seqs + s) * sp.rows_per_seq + tok) * Hq + hd;
+    const float2 ml = *reinterpret_cast<const float2*>(sp.ws_ml + 2 * prow);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(sp.ws_acc + prow * D + 4 * d4);
     if (ml.x == kNegInf) continue;               // (no key: cannot happen, every piece has one)
     const float mn = fmaxf(M, ml.x);
     const float c0 = M == kNegInf ? 0.f : fast_exp2(M - mn);
@@ -766,67 +767,74 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
 }
 
 template <class T, int D, int BS, int G>
-hipError_t launch_g(const PrefillArgs& a, int32_t max_query_len, hipStream_t stream) {
+hipError_t launch_g(const PrefillArgs& a, const PrefillSplitArgs& sp, int32_t max_query_len, hipStream_t stream) {
   const int cb = prefill_column_blocks(G, max_query_len, a.num_seqs, a.num_kv_heads);
   const int tpw = 4 * cb * (16 / G);
   // the tile ring: 8 slots of K and V for bf16 with three column blocks, else 6
   const size_t lds = size_t(std::is_same_v<T, BF16> && cb == 3 ? 8 : 6) * 2 * (D / 32) * 1024;
   // (pieces of a split context along z, the longest first)
-  dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads, a.split_tiles ? a.split_max : 1),
+  dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads, sp.split_tiles ? sp.split_max : 1),
       block(256);
-  if (cb == 3) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 3>), grid, block, lds, stream, a);
-  else if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2>), grid, block, lds, stream, a);
-  else hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1>), grid, block, lds, stream, a);
+  if (cb == 3) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 3>), grid, block, lds, stream, a, sp);
+  else if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2>), grid, block, lds, stream, a, sp);
+  else hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1>), grid, block, lds, stream, a, sp);
   if (hipError_t e = hipGetLastError()) return e;
-  if (!a.split_tiles) return hipSuccess;
-  const int64_t units = int64_t(a.rows_per_seq) * a.num_q_heads * (D / 4);
+  if (!sp.split_tiles) return hipSuccess;
+  const int64_t units = int64_t(sp.rows_per_seq) * a.num_q_heads * (D / 4);
   hipLaunchKernelGGL((prefill_merge_kernel<T, D>), dim3(static_cast<uint32_t>((units + 255) / 256), a.num_seqs),
-                     dim3(256), 0, stream, a);
+                     dim3(256), 0, stream, a, sp);
   return hipGetLastError();
 }
 
 template <class T, int D, int BS>
-hipError_t launch_b(const PrefillArgs& a, int32_t group, int32_t max_query_len, hipStream_t stream) {
+hipError_t launch_b(const PrefillArgs& a, const PrefillSplitArgs& sp, int32_t group, int32_t max_query_len,
+                    hipStream_t stream) {
   switch (group) {
-    case 1: return launch_g<T, D, BS, 1>(a, max_query_len, stream);
-    case 2: return launch_g<T, D, BS, 2>(a, max_query_len, stream);
-    case 4: return launch_g<T, D, BS, 4>(a, max_query_len, stream);
-    case 8: return launch_g<T, D, BS, 8>(a, max_query_len, stream);
-    case 16: return launch_g<T, D, BS, 16>(a, max_query_len, stream);
+    case 1: return launch_g<T, D, BS, 1>(a, sp, max_query_len, stream);
+    case 2: return launch_g<T, D, BS, 2>(a, sp, max_query_len, stream);
+    case 4: return launch_g<T, D, BS, 4>(a, sp, max_query_len, stream);
+    case 8: return launch_g<T, D, BS, 8>(a, sp, max_query_len, stream);
+    case 16: return launch_g<T, D, BS, 16>(a, sp, max_query_len, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <class T, int D>
-hipError_t launch_d(const PrefillArgs& a, int32_t bs, int32_t group, int32_t max_query_len, hipStream_t stream) {
+hipError_t launch_d(const PrefillArgs& a, const PrefillSplitArgs& sp, int32_t bs, int32_t group, int32_t max_query_len,
+                    hipStream_t stream) {
   switch (bs) {
-    case 8: return launch_b<T, D, 8>(a, group, max_query_len, stream);
-    case 16: return launch_b<T, D, 16>(a, group, max_query_len, stream);
-    case 32: return launch_b<T, D, 32>(a, group, max_query_len, stream);
+    case 8: return launch_b<T, D, 8>(a, sp, group, max_query_len, stream);
+    case 16: return launch_b<T, D, 16>(a, sp, group, max_query_len, stream);
+    case 32: return launch_b<T, D, 32>(a, sp, group, max_query_len, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <class T>
-hipError_t launch_t(const PrefillArgs& a, int32_t d, int32_t bs, int32_t group, int32_t max_query_len,
-                    hipStream_t stream) {
+hipError_t launch_t(const PrefillArgs& a, const PrefillSplitArgs& sp, int32_t d, int32_t bs, int32_t group,
+                    int32_t max_query_len, hipStream_t stream) {
   switch (d) {
-    case 64: return launch_d<T, 64>(a, bs, group, max_query_len, stream);
-    case 128: return launch_d<T, 128>(a, bs, group, max_query_len, stream);
+    case 64: return launch_d<T, 64>(a, sp, bs, group, max_query_len, stream);
+    case 128: return launch_d<T, 128>(a, sp, bs, group, max_query_len, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int32_t dtype, int32_t d, int32_t bs, int32_t group,
-                          int32_t max_query_len, hipStream_t stream) {
+hipError_t launch_prefill_split(const PrefillArgs& a, const PrefillSplitArgs& sp, int32_t dtype, int32_t d,
+                                int32_t bs, int32_t group, int32_t max_query_len, hipStream_t stream) {
   if (max_query_len <= 0 || a.num_seqs <= 0) return hipSuccess;
   switch (dtype) {
-    case 1: return launch_t<F16>(a, d, bs, group, max_query_len, stream);
-    case 2: return launch_t<BF16>(a, d, bs, group, max_query_len, stream);
+    case 1: return launch_t<F16>(a, sp, d, bs, group, max_query_len, stream);
+    case 2: return launch_t<BF16>(a, sp, d, bs, group, max_query_len, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int32_t dtype, int32_t d, int32_t bs, int32_t group,
+                          int32_t max_query_len, hipStream_t stream) {
+  return launch_prefill_split(a, PrefillSplitArgs{}, dtype, d, bs, group, max_query_len, stream);
 }
 
 }  // namespace pa
