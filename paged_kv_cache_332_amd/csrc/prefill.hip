@@ -122,7 +122,7 @@ __device__ __forceinline__ void wait_oldest_tile(int k) {
   }
 }
 
-template <class T, int D, int BS, int G, int CB>
+template <class T, int D, int BS, int G, int CB, bool SPLITK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a, PrefillSplitArgs sp) {
   using bits = typename T::bits;
   using MF = MfmaOps<T>;
@@ -169,17 +169,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int p0 = P - L;                          // position of the chunk's first token
   const int kmax = p0 + min(L, tq0 + TQW);       // positions the workgroup's tokens see
   const int nt = (kmax + 15) / 16;
-  // Context split (asked for by the launch, for launches with few
-  // workgroups): piece z of S streams tiles [z SPL, (z + 1) SPL) and the last
-  // one every tile from (S - 1) SPL on.  The pieces but the last end before
-  // the chunk's first position, so every column sees every key of those and
-  // the first key of the last one.  A split sequence leaves each piece's
-  // partial state in the workspace for the merge.
-  const int S = sp.split_tiles ? p0 / (16 * sp.split_tiles) + 1 : 1;
-  if (int(blockIdx.z) >= S) return;                 // (whole workgroup)
-  const int zp = S - 1 - int(blockIdx.z);           // the longest piece first
-  const int tb = zp * sp.split_tiles;                // tiles [tb, te) (tb even)
-  const int te = zp == S - 1 ? nt : tb + sp.split_tiles;
+  // Context split (SPLITK, launches with few workgroups, which take one
+  // column block): piece z of S streams tiles [z SPL, (z + 1) SPL) and the
+  // last one every tile from (S - 1) SPL on.  The pieces but the last end
+  // before the chunk's first position, so every column sees every key of
+  // those and the first key of the last one.  A split sequence leaves each
+  // piece's partial state in the workspace for the merge.  (Without SPLITK
+  // the bounds are the constants 0 and nt: runtime bounds cost the
+  // three-block kernel 2%.)
+  const int S = SPLITK ? p0 / (16 * sp.split_tiles) + 1 : 1;
+  if (SPLITK && int(blockIdx.z) >= S) return;       // (whole workgroup)
+  const int zp = SPLITK ? S - 1 - int(blockIdx.z) : 0;   // the longest piece first
+  const int tb = SPLITK ? zp * sp.split_tiles : 0;       // tiles [tb, te) (tb even)
+  const int te = SPLITK && zp < S - 1 ? tb + sp.split_tiles : nt;
 
   // this lane's column in block cb: token cb TB + j of the wave, head gc of
   // the group
@@ -669,7 +671,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // diagonal on take the general path: a causal limit per column, blocks
   // past their last position skipped, and a missing tile t + 1 read from a
   // stale slot with every score masked and every value selected to zero.
-  const int open_end = min(te, max(tb + 2, (blk_open[0] - 32) / 16 + 1));   // first t (even or odd) not open
+  // first t (even or odd) not open (no later than the end: (blk_open - 32) / 16 + 1 < nt)
+  const int open_end = SPLITK ? min(te, max(tb + 2, (blk_open[0] - 32) / 16 + 1)) : max(2, (blk_open[0] - 32) / 16 + 1);
   int t = tb;
   advance(t, std::false_type{});
   for (t = tb + 2; t < open_end; t += 2) advance(t, std::true_type{});
@@ -775,9 +778,13 @@ hipError_t launch_g(const PrefillArgs& a, const PrefillSplitArgs& sp, int32_t ma
   // (pieces of a split context along z, the longest first)
   dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads, sp.split_tiles ? sp.split_max : 1),
       block(256);
-  if (cb == 3) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 3>), grid, block, lds, stream, a, sp);
-  else if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2>), grid, block, lds, stream, a, sp);
-  else hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1>), grid, block, lds, stream, a, sp);
+  // (a split launch has fewer workgroups than two or three column blocks
+  // are chosen for: it always takes one)
+  if (sp.split_tiles && cb != 1) return hipErrorInvalidValue;
+  if (sp.split_tiles) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1, true>), grid, block, lds, stream, a, sp);
+  else if (cb == 3) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 3, false>), grid, block, lds, stream, a, sp);
+  else if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2, false>), grid, block, lds, stream, a, sp);
+  else hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1, false>), grid, block, lds, stream, a, sp);
   if (hipError_t e = hipGetLastError()) return e;
   if (!sp.split_tiles) return hipSuccess;
   const int64_t units = int64_t(sp.rows_per_seq) * a.num_q_heads * (D / 4);
