@@ -141,7 +141,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int NT = D / 16;           // PV row tiles of 16 dims
   constexpr int KI = D / 32;           // 1 KiB loads per K (and per V) tile
   constexpr int LPW = 2 * KI / 4;      // loads per wave per tile
-  constexpr int NSL = CONV ? 8 : 6;    // ring slots: four (three) pairs of tiles
+  // ring slots: four pairs of tiles (the split variant, whose launches hold
+  // about 2048 workgroups, three: 6 slots keep three workgroups per compute
+  // unit where 8 allow two)
+  constexpr int NSL = SPLITK ? 6 : 8;
   constexpr int IDCAP = 512;           // tiles whose block ids are staged at once
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   static_assert(LPW >= 1 && LPW * (NSL - 1) < 64, "loads per wave");
@@ -630,8 +633,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // slots 2p, 2p + 1 (mod 8), its values converted while pair p - 1
   // computed; pair p + 1 lands and is converted during pair p, pair p + 2 is
   // in flight and pair p + 3 fills the slots of pair p - 1.  Otherwise pair p
-  // computes from slots 2p, 2p + 1 (mod 6) while pair p + 1 is in flight and
-  // pair p + 2 fills the slots of pair p - 1.
+  // computes from slots 2p, 2p + 1 (mod NSL) while the next NSL / 2 - 2 pairs
+  // are in flight and the one after them fills the slots of pair p - 1.
 #pragma unroll
   for (int i = 0; i < NSL - 2; ++i)
     if (tb + i < te) issue(tb + i);
@@ -656,9 +659,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       // loads of the newer tiles are outstanding; the barrier then covers
       // every wave's share (and every wave is done with the previous pair,
       // whose slots are refilled next)
-      wait_oldest_tile<LPW, 2>(min(te - 1, t + 3) - min(te - 1, t + 1));
+      wait_oldest_tile<LPW, NSL - 4>(min(te - 1, t + NSL - 3) - min(te - 1, t + 1));
       wg_barrier();
-      refill(t, std::integral_constant<int, 4>{});
+      refill(t, std::integral_constant<int, NSL - 2>{});
       pair_step(t, open_tag);
     }
   };
@@ -773,8 +776,8 @@ template <class T, int D, int BS, int G>
 hipError_t launch_g(const PrefillArgs& a, const PrefillSplitArgs& sp, int32_t max_query_len, hipStream_t stream) {
   const int cb = prefill_column_blocks(G, max_query_len, a.num_seqs, a.num_kv_heads);
   const int tpw = 4 * cb * (16 / G);
-  // the tile ring: 8 slots of K and V for bf16 with three column blocks, else 6
-  const size_t lds = size_t(std::is_same_v<T, BF16> && cb == 3 ? 8 : 6) * 2 * (D / 32) * 1024;
+  // the tile ring: 8 slots of K and V (6 for a split launch)
+  const size_t lds = size_t(sp.split_tiles ? 6 : 8) * 2 * (D / 32) * 1024;
   // (pieces of a split context along z, the longest first)
   dim3 grid((max_query_len + tpw - 1) / tpw, a.num_seqs * a.num_kv_heads, sp.split_tiles ? sp.split_max : 1),
       block(256);
