@@ -41,6 +41,14 @@
 // value was seen, so they only ever shrink (exactly, but for what falls below
 // fp32's range).
 //
+// Context split.  A launch of few workgroups (short chunks of few sequences)
+// may cut each sequence's prefix into pieces streamed by workgroups of their
+// own (grid z, the last piece first); each piece leaves its columns' partial
+// states (reference maximum, weight sum, unnormalised output) in a
+// workspace, and prefill_merge_kernel combines them by log-sum-exp.  The
+// pieces end before the chunk's first position, so every column sees at
+// least the first key of every piece.
+//
 // Tiles go in pairs: one softmax step covers 32 keys (one cross-lane
 // reduction and one rescale check per 32 keys), and P V is one
 // v_mfma_f32_16x16x32 per 16 value dims over both tiles (on gfx950 twice the
