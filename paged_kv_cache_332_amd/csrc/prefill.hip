@@ -27,9 +27,9 @@
 // reference is raised to the column's exact maximum only when a lane's
 // weights of a step sum past 2^15, which leaves no maximum on the common
 // path), P rounded to fp16 for one P V product into O^T; a block none of
-// whose columns sees the tiles skips them.  No split of the context: a
-// workgroup covers its tokens' whole prefix, and many workgroups run at
-// once.
+// whose columns sees the tiles skips them.  A workgroup covers its tokens'
+// whole prefix, and many workgroups run at once (but for the context split
+// below).
 //
 // P V in fp16.  The weights are at most 2^15 and keep 11 significant bits
 // (bf16 would keep 8, too few for the 2e-3 bound); the values are converted
