@@ -154,6 +154,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // unit where 8 allow two)
   constexpr int NSL = SPLITK ? 6 : 8;
   constexpr int IDCAP = 512;           // tiles whose block ids are staged at once
+  static_assert(kPrefillRankMax % 4 == 0 && kPrefillRankMax <= 256 && 2 * IDCAP - 1 >= kPrefillRankMax, "rank scratch");
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   static_assert(LPW >= 1 && LPW * (NSL - 1) < 64, "loads per wave");
   // the ring is the dynamic LDS array, a separate object from the block ids,
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // of a landed slot are ordered by the explicit waits below
   extern __shared__ __attribute__((aligned(16))) uint8_t ring[];
   constexpr int SLOT = 2 * KI * 1024;
-  __shared__ int2 s_ids[IDCAP];
+  __shared__ __attribute__((aligned(16))) int2 s_ids[IDCAP];   // (16-byte reads of the ranked lengths)
   __shared__ __attribute__((aligned(16))) int s_frame[2][4];   // per pair parity and group of 32 dims: the values' frame
 
   const int lane = threadIdx.x & 63;
@@ -170,8 +171,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int c = lane & 15;
   const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
-  const int s = blockIdx.y / Hkv;
+  // Sequences go in order of decreasing context (ties by index): grid y
+  // counts (rank, kv head), so the workgroups of the longest contexts are
+  // dispatched first and the launch's tail holds short ones (with the index
+  // order a long sequence dispatched last left most compute units idle).
+  // Each workgroup ranks the lengths itself, in the block-id array before
+  // it is staged: one comparison per sequence and thread, up to
+  // kPrefillRankMax sequences (more keep the index order).
   const int h = blockIdx.y % Hkv;
+  int s = blockIdx.y / Hkv;
+  if (a.num_seqs <= kPrefillRankMax) {
+    // [0, B): lengths (-1 past B, up to a multiple of 4), [2 IDCAP - 1]: the
+    // sequence of rank s
+    int* rk = reinterpret_cast<int*>(s_ids);
+    const int B = a.num_seqs;
+    const int t = threadIdx.x;
+    if (t < ((B + 3) & ~3)) rk[t] = t < B ? min(max(a.ctx[t], 0), a.max_ctx) : -1;
+    __syncthreads();
+    if (t < B) {
+      const int pt = rk[t];
+      int rank = 0;
+      for (int u = 0; u < B; u += 4) {
+        const int4 pu = *reinterpret_cast<const int4*>(rk + u);
+        rank += (pu.x > pt || (pu.x == pt && u + 0 < t)) ? 1 : 0;
+        rank += (pu.y > pt || (pu.y == pt && u + 1 < t)) ? 1 : 0;
+        rank += (pu.z > pt || (pu.z == pt && u + 2 < t)) ? 1 : 0;
+        rank += (pu.w > pt || (pu.w == pt && u + 3 < t)) ? 1 : 0;
+      }
+      if (rank == s) rk[2 * IDCAP - 1] = t;
+    }
+    __syncthreads();
+    s = uniform(rk[2 * IDCAP - 1]);
+    __syncthreads();                             // (the array is the block ids' next)
+  }
   const int qs = a.query_start[s];
   const int P = min(max(a.ctx[s], 0), a.max_ctx);
   const int L = min(max(a.query_start[s + 1] - qs, 0), P);

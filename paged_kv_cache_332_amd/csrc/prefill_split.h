@@ -29,6 +29,11 @@ struct PrefillSplitArgs {
 // merges the pieces' partial states by log-sum-exp.  bytes: the workspace it
 // needs (0: no split).
 constexpr int64_t kPrefillSplitBelow = 512;
+// Prefill workgroups rank the sequences by context length (longest first) up
+// to this many sequences (one per thread of a workgroup; every workgroup
+// pays a comparison per sequence, and the workgroups grow with the batch:
+// at 256 sequences the ranking cost the fp16 MHA launch 15%).
+constexpr int32_t kPrefillRankMax = 128;
 constexpr int64_t kPrefillSplitTarget = 2048;
 constexpr int32_t kPrefillMinSplitTiles = 32;
 struct PrefillSplit {
