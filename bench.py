@@ -328,12 +328,14 @@ def prefill_bench(args, w, cfg, pa, runner, torch):
     flops = 4.0 * cfg.num_q_heads * cfg.head_dim * keys
     # K/V tiles each workgroup streams (16-token tiles up to its last token)
     # (the workgroup size the library picks: 3 column blocks per wave when
-    # that leaves at least 4096 workgroups, 2 for at least 1024, else 1)
+    # that leaves at least 1024 workgroups and the last query block is at
+    # most a fifth empty, 2 for at least 1024 workgroups, else 1)
     G = cfg.num_q_heads // cfg.num_kv_heads
     maxq = int(chunk.max())
     wgs = lambda cbk: (0 if maxq < 4 * cbk * (16 // G) else
                        cfg.num_seqs * cfg.num_kv_heads * (-(-maxq // (4 * cbk * (16 // G)))))
-    cb = 3 if wgs(3) >= 4096 else (2 if wgs(2) >= 1024 else 1)
+    rows3 = -(-maxq // (12 * (16 // G))) * (12 * (16 // G))
+    cb = 3 if wgs(3) >= 1024 and 5 * (rows3 - maxq) <= rows3 else (2 if wgs(2) >= 1024 else 1)
     tpw = 4 * cb * (16 // G)
     tiles = 0
     for c, L in zip(ctx, chunk):

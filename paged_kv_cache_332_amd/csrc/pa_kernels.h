@@ -98,14 +98,17 @@ struct PrefillArgs {
 };
 // Column blocks per prefill wave (16 / group tokens each): more blocks
 // share each streamed tile and K operand among more columns, fewer keep
-// short chunks spread over enough workgroups.  3 when that still leaves at
-// least 4096 workgroups, 2 for at least 1024, else 1.
+// short chunks spread over enough workgroups.  3 when that leaves at least
+// 1024 workgroups and the chunk's last query block of 12 (16 / group) tokens
+// is at most a fifth empty, 2 for at least 1024 workgroups, else 1.
 inline int32_t prefill_column_blocks(int32_t group, int32_t max_query_len, int32_t num_seqs, int32_t num_kv_heads) {
   auto wgs = [&](int64_t cb) {
     const int64_t tpw = 4 * cb * (16 / group);
     return max_query_len < tpw ? int64_t(0) : int64_t(num_seqs) * num_kv_heads * ((max_query_len + tpw - 1) / tpw);
   };
-  if (wgs(3) >= 4096) return 3;
+  const int64_t tpw3 = 12 * (16 / group);
+  const int64_t rows3 = (int64_t(max_query_len) + tpw3 - 1) / tpw3 * tpw3;
+  if (wgs(3) >= 1024 && 5 * (rows3 - max_query_len) <= rows3) return 3;
   return wgs(2) >= 1024 ? 2 : 1;
 }
 hipError_t launch_prefill(const PrefillArgs& a, int32_t dtype, int32_t d, int32_t bs, int32_t group,

@@ -114,7 +114,8 @@ def test_prefill_rejects_bad_arguments():
 # enough for two column blocks per wave, three for the *_three_blocks cases (the same sequence
 # alone takes one)
 WIDE = {
-    "gqa4_bf16_bs16": ("bf16", 128, 16, 32, 8, 16, 512, (520, 1400)),
+    # (8 sequences: 1024 workgroups with two column blocks, 704 with three)
+    "gqa4_bf16_bs16": ("bf16", 128, 16, 32, 8, 8, 512, (520, 1400)),
     "gqa4_bf16_bs16_three_blocks": ("bf16", 128, 16, 32, 8, 32, 768, (770, 1200)),
     "mha_f16_bs8_d64_three_blocks": ("f16", 64, 8, 16, 16, 16, 3072, (3072, 3400)),
     "mha_f16_bs8_d64": ("f16", 64, 8, 16, 16, 8, 1024, (1030, 1500)),
