@@ -326,16 +326,10 @@ def prefill_bench(args, w, cfg, pa, runner, torch):
     # visible keys per query token: its position + 1
     keys = sum(int(((c - L + 1) + c) * L // 2) for c, L in zip(ctx, chunk))
     flops = 4.0 * cfg.num_q_heads * cfg.head_dim * keys
-    # K/V tiles each workgroup streams (16-token tiles up to its last token)
-    # (the workgroup size the library picks: 3 column blocks per wave when
-    # that leaves at least 1024 workgroups and the last query block is at
-    # most a fifth empty, 2 for at least 1024 workgroups, else 1)
+    # K/V tiles each workgroup streams (16-token tiles up to its last token),
+    # with the workgroup size the library picks for this launch
     G = cfg.num_q_heads // cfg.num_kv_heads
-    maxq = int(chunk.max())
-    wgs = lambda cbk: (0 if maxq < 4 * cbk * (16 // G) else
-                       cfg.num_seqs * cfg.num_kv_heads * (-(-maxq // (4 * cbk * (16 // G)))))
-    rows3 = -(-maxq // (12 * (16 // G))) * (12 * (16 // G))
-    cb = 3 if wgs(3) >= 1024 and 5 * (rows3 - maxq) <= rows3 else (2 if wgs(2) >= 1024 else 1)
+    cb = pa.pa_prefill_column_blocks(cfg.num_q_heads, cfg.num_kv_heads, int(chunk.max()), cfg.num_seqs)
     tpw = 4 * cb * (16 // G)
     tiles = 0
     for c, L in zip(ctx, chunk):

@@ -393,6 +393,14 @@ pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k
 size_t pa_prefill_workspace_bytes(int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,
                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
 
+/* Column blocks per wave pa_prefill takes for a launch of this shape (each
+ * wave holds CB blocks of 16 query columns, (16 / group) tokens each, so a
+ * workgroup covers 64 CB / group query tokens): 3 when that leaves at least
+ * 1024 workgroups and the last query block is at most a fifth empty, 2 for
+ * at least 1024 workgroups, else 1; 0 for a group size pa_prefill rejects.
+ * For callers that count what a launch streams. */
+int32_t pa_prefill_column_blocks(int32_t num_q_heads, int32_t num_kv_heads, int32_t max_query_len, int32_t num_seqs);
+
 /* ------------------------------------------------------------------------
  * pa_step — one decode step of a batch, host and device parts in one call:
  *   1. pa_bm_append_slots: the new token of each of seqs[0..n) gets a slot

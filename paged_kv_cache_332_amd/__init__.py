@@ -24,7 +24,8 @@ __all__ = [
     "pa_decode_workspace_bytes", "pa_decode_default_partition", "pa_check_tables",
     "BlockManager", "alloc_cache", "cache_shapes", "torch_dtype_code", "pa_version", "pa_step",
     "pa_decode_stream_grid", "pa_decode_noalloc", "step_record_words", "step_args", "step_call",
-    "stream_class_finish", "pa_stream_plan", "pa_prefill", "pa_prefill_workspace_bytes", "pa_swap_blocks",
+    "stream_class_finish", "pa_stream_plan", "pa_prefill", "pa_prefill_workspace_bytes", "pa_prefill_column_blocks",
+    "pa_swap_blocks",
     "pa_step_layer",
     "STEP_KV", "STEP_PASS", "STEP_MERGE", "STEP_ALL",
 ]
@@ -66,6 +67,7 @@ _sig("pa_decode_noalloc", _i32, *_DECODE_ARGS[:18], _vp)
 _sig("pa_prefill", _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
      _i32, _i32, _f32, _vp, _sz, _vp)
 _sig("pa_prefill_workspace_bytes", _sz, _i32, _i32, _i32, _i32, _i32, _i32)
+_sig("pa_prefill_column_blocks", _i32, _i32, _i32, _i32, _i32)
 _sig("pa_bm_create", _vp, _i32, _i32, _pi32)
 _sig("pa_bm_destroy", None, _vp)
 _sig("pa_bm_add_seq", _i32, _vp, _i64, _i32, _pi32)
@@ -261,6 +263,11 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, query_start, context_lens
                           int(max_query_len), int(max_context_len), int(context_lens.shape[0]), int(q.shape[1]), hkv,
                           d, bs, n_, float(scale), None if workspace is None else workspace.data_ptr(),
                           0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def pa_prefill_column_blocks(num_q_heads: int, num_kv_heads: int, max_query_len: int, num_seqs: int) -> int:
+    """Column blocks per wave pa_prefill takes for this launch shape (see pa.h)."""
+    return int(lib.pa_prefill_column_blocks(int(num_q_heads), int(num_kv_heads), int(max_query_len), int(num_seqs)))
 
 
 def pa_prefill_workspace_bytes(max_query_len: int, max_context_len: int, num_seqs: int, num_q_heads: int,

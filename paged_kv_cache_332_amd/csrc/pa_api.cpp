@@ -479,6 +479,14 @@ pa_status pa_prefill(void* out, pa_dtype out_dtype, const void* q, const void* k
                                                      static_cast<hipStream_t>(stream)));
 }
 
+int32_t pa_prefill_column_blocks(int32_t num_q_heads, int32_t num_kv_heads, int32_t max_query_len, int32_t num_seqs) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || max_query_len < 0 || num_seqs < 0)
+    return 0;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return 0;
+  return pa::prefill_column_blocks(group, max_query_len, num_seqs, num_kv_heads);
+}
+
 size_t pa_prefill_workspace_bytes(int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,
                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
   if (max_query_len <= 0 || max_context_len <= 0 || num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||

@@ -496,6 +496,22 @@ def test_prefill_workspace_bytes():
     assert pa.pa_prefill_workspace_bytes(0, 131072, 8, Hq, Hkv, D) == 0
 
 
+@pytest.mark.parametrize("hq,hkv,maxq,b,want", [
+    (32, 8, 512, 64, 3),      # 5632 workgroups; the last of 11 blocks of 48 tokens holds 32: 16 of 528 rows empty
+    (32, 8, 128, 64, 3),      # 1536 workgroups, 16 of 144 rows empty
+    (32, 8, 64, 64, 2),       # a third of the last three-block rows empty
+    (32, 8, 16, 64, 1),       # 512 workgroups at two blocks
+    (64, 8, 512, 8, 3),       # group 8: 24-token blocks, 1408 workgroups
+    (64, 8, 128, 8, 1),       # 384 / 512 workgroups
+    (32, 8, 512, 8, 2),       # 704 at three blocks, 1024 at two
+    (24, 8, 512, 64, 0),      # group 3: rejected
+])
+def test_prefill_column_blocks(hq, hkv, maxq, b, want):
+    """The prefill's workgroup size per launch shape (the benchmark counts
+    streamed bytes with it)."""
+    assert pa.pa_prefill_column_blocks(hq, hkv, maxq, b) == want
+
+
 def _swap_args(**over):
     a = dict(k=16, v=16, hk=16, hv=16, blocks=16, n=4, to_host=1, Hkv=8, D=128, BS=16, N=1000, dtype=pa.PA_BF16,
              stream=0)
