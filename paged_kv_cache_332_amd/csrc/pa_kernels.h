@@ -100,7 +100,8 @@ struct PrefillArgs {
 // share each streamed tile and K operand among more columns, fewer keep
 // short chunks spread over enough workgroups.  3 when that leaves at least
 // 1024 workgroups and the chunk's last query block of 12 (16 / group) tokens
-// is at most a fifth empty, 2 for at least 1024 workgroups, else 1.
+// is at most a fifth empty, 2 when that leaves at least 512 and its last
+// block of 8 (16 / group) tokens is at most a fifth empty, else 1.
 inline int32_t prefill_column_blocks(int32_t group, int32_t max_query_len, int32_t num_seqs, int32_t num_kv_heads) {
   auto wgs = [&](int64_t cb) {
     const int64_t tpw = 4 * cb * (16 / group);
@@ -109,7 +110,9 @@ inline int32_t prefill_column_blocks(int32_t group, int32_t max_query_len, int32
   const int64_t tpw3 = 12 * (16 / group);
   const int64_t rows3 = (int64_t(max_query_len) + tpw3 - 1) / tpw3 * tpw3;
   if (wgs(3) >= 1024 && 5 * (rows3 - max_query_len) <= rows3) return 3;
-  return wgs(2) >= 1024 ? 2 : 1;
+  const int64_t tpw2 = 8 * (16 / group);
+  const int64_t rows2 = (int64_t(max_query_len) + tpw2 - 1) / tpw2 * tpw2;
+  return wgs(2) >= 512 && 5 * (rows2 - max_query_len) <= rows2 ? 2 : 1;
 }
 hipError_t launch_prefill(const PrefillArgs& a, int32_t dtype, int32_t d, int32_t bs, int32_t group,
                           int32_t max_query_len, hipStream_t stream);

@@ -502,7 +502,9 @@ def test_prefill_workspace_bytes():
     (32, 8, 64, 64, 2),       # a third of the last three-block rows empty
     (32, 8, 16, 64, 1),       # 512 workgroups at two blocks
     (64, 8, 512, 8, 3),       # group 8: 24-token blocks, 1408 workgroups
-    (64, 8, 128, 8, 1),       # 384 / 512 workgroups
+    (64, 8, 128, 8, 2),       # 384 workgroups at three blocks, 512 at two
+    (32, 8, 32, 64, 2),       # 512 workgroups at two blocks, none empty
+    (32, 8, 48, 64, 1),       # a quarter of the last two-block rows empty
     (32, 8, 512, 8, 2),       # 704 at three blocks, 1024 at two
     (24, 8, 512, 64, 0),      # group 3: rejected
 ])
