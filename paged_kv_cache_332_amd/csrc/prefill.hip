@@ -130,7 +130,7 @@ __device__ __forceinline__ void wait_oldest_tile(int k) {
   }
 }
 
-template <class T, int D, int BS, int G, int CB, bool SPLITK>
+template <class T, int D, int BS, int G, int CB, bool SPLITK, bool ONCE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a, PrefillSplitArgs sp) {
   using bits = typename T::bits;
   using MF = MfmaOps<T>;
@@ -318,7 +318,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           tk = tt & 7;
         }
         const int64_t e = ((int64_t(blk) * Hkv + h) * (D / 8) + jj) * (BS * 8) + tk * 8;
-        dma16(kpool + e, sl + i * 1024);
+        if constexpr (ONCE) dma16_once(kpool + e, sl + i * 1024);
+        else dma16(kpool + e, sl + i * 1024);
       } else {
         const int u = (i - KI) * 64 + lane;
         const int d = u >> 1, hh = u & 1;
@@ -334,7 +335,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           tk0 = 0;
         }
         const int64_t e = ((int64_t(blk) * Hkv + h) * D + d) * BS + tk0;
-        dma16(vpool + e, sl + i * 1024);
+        if constexpr (ONCE) dma16_once(vpool + e, sl + i * 1024);
+        else dma16(vpool + e, sl + i * 1024);
       }
     }
   };
@@ -824,9 +826,14 @@ hipError_t launch_g(const PrefillArgs& a, const PrefillSplitArgs& sp, int32_t ma
   // (a split launch has fewer workgroups than two or three column blocks
   // are chosen for: it always takes one)
   if (sp.split_tiles && cb != 1) return hipErrorInvalidValue;
-  if (sp.split_tiles) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1, true>), grid, block, lds, stream, a, sp);
+  // (with one query block per sequence, every tile is read by one
+  // workgroup: the loads take the streaming policy of the decode pass)
+  const bool once = max_query_len <= tpw;
+  if (sp.split_tiles && once) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1, true, true>), grid, block, lds, stream, a, sp);
+  else if (sp.split_tiles) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1, true>), grid, block, lds, stream, a, sp);
   else if (cb == 3) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 3, false>), grid, block, lds, stream, a, sp);
   else if (cb == 2) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 2, false>), grid, block, lds, stream, a, sp);
+  else if (once) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1, false, true>), grid, block, lds, stream, a, sp);
   else hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1, false>), grid, block, lds, stream, a, sp);
   if (hipError_t e = hipGetLastError()) return e;
   if (!sp.split_tiles) return hipSuccess;
