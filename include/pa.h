@@ -396,9 +396,10 @@ size_t pa_prefill_workspace_bytes(int32_t max_query_len, int32_t max_context_len
 /* Column blocks per wave pa_prefill takes for a launch of this shape (each
  * wave holds CB blocks of 16 query columns, (16 / group) tokens each, so a
  * workgroup covers 64 CB / group query tokens): 3 when that leaves at least
- * 1024 workgroups and the last query block is at most a fifth empty, 2 when
- * that leaves at least 512 and the last block is at most a fifth empty, else
- * 1; 0 for a group size pa_prefill rejects.
+ * 1024 workgroups and rounding max_query_len up to whole query blocks pads at
+ * most a fifth of the rounded rows, 2 when that leaves at least 512 and the
+ * padding is at most a fifth, else 1 (a chunk shorter than one block of a
+ * count takes neither); 0 for a group size pa_prefill rejects.
  * For callers that count what a launch streams. */
 int32_t pa_prefill_column_blocks(int32_t num_q_heads, int32_t num_kv_heads, int32_t max_query_len, int32_t num_seqs);
 

@@ -99,9 +99,10 @@ struct PrefillArgs {
 // Column blocks per prefill wave (16 / group tokens each): more blocks
 // share each streamed tile and K operand among more columns, fewer keep
 // short chunks spread over enough workgroups.  3 when that leaves at least
-// 1024 workgroups and the chunk's last query block of 12 (16 / group) tokens
-// is at most a fifth empty, 2 when that leaves at least 512 and its last
-// block of 8 (16 / group) tokens is at most a fifth empty, else 1.
+// 1024 workgroups and rounding the longest chunk up to whole query blocks of
+// 12 (16 / group) tokens pads at most a fifth of the rounded rows, 2 when
+// that leaves at least 512 and blocks of 8 (16 / group) tokens pad at most a
+// fifth, else 1 (a chunk shorter than one block takes neither).
 inline int32_t prefill_column_blocks(int32_t group, int32_t max_query_len, int32_t num_seqs, int32_t num_kv_heads) {
   auto wgs = [&](int64_t cb) {
     const int64_t tpw = 4 * cb * (16 / group);
