@@ -826,8 +826,9 @@ hipError_t launch_g(const PrefillArgs& a, const PrefillSplitArgs& sp, int32_t ma
   // (a split launch has fewer workgroups than two or three column blocks
   // are chosen for: it always takes one)
   if (sp.split_tiles && cb != 1) return hipErrorInvalidValue;
-  // (with one query block per sequence, every tile is read by one
-  // workgroup: the loads take the streaming policy of the decode pass)
+  // (with one query block per sequence, no two workgroups of a sequence
+  // read the same tile: the loads take the streaming policy of the decode
+  // pass; a block that sequences share is still read once per sharer)
   const bool once = max_query_len <= tpw;
   if (sp.split_tiles && once) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1, true, true>), grid, block, lds, stream, a, sp);
   else if (sp.split_tiles) hipLaunchKernelGGL((prefill_kernel<T, D, BS, G, 1, true>), grid, block, lds, stream, a, sp);
