@@ -606,8 +606,9 @@ __device__ __forceinline__ void merge_item(const StreamArgs& sa, int seq, int kv
     if (a.out_f32) {
       *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = O[u] * inv;
     } else {
-      const uint32_t lo = T::from_f32(O[u][0] * inv) | (T::from_f32(O[u][1] * inv) << 16);
-      const uint32_t hi = T::from_f32(O[u][2] * inv) | (T::from_f32(O[u][3] * inv) << 16);
+      // (the fp32 output rounded: see opaque_f32)
+      const uint32_t lo = T::from_f32(opaque_f32(O[u][0] * inv)) | (T::from_f32(opaque_f32(O[u][1] * inv)) << 16);
+      const uint32_t hi = T::from_f32(opaque_f32(O[u][2] * inv)) | (T::from_f32(opaque_f32(O[u][3] * inv)) << 16);
       *reinterpret_cast<u32x2*>(static_cast<bits*>(a.out) + o) = u32x2{lo, hi};
     }
   }

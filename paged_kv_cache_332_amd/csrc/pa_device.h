@@ -236,6 +236,16 @@ __device__ __forceinline__ void dma16_once(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)dst, 16, 0, kCpolStreamOnce);
 }
 
+// x as an opaque fp32 value: converting the result to 16 bits rounds this
+// fp32 value, as converting a stored fp32 output would (left visible, the
+// multiply that produced x can be fused with the conversion into one
+// mixed-precision fma that rounds the exact product once, which lands on the
+// other side of a tie).  The empty asm emits no instruction.
+__device__ __forceinline__ float opaque_f32(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 // The memory clobber keeps LDS reads of the landed tile below the wait.
 template <int N>

@@ -808,8 +808,9 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, Prefi
   if (a.out_f32) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + off) = o * inv;
   } else {
-    const uint32_t lo = T::from_f32(o[0] * inv) | (T::from_f32(o[1] * inv) << 16);
-    const uint32_t hi = T::from_f32(o[2] * inv) | (T::from_f32(o[3] * inv) << 16);
+    // (the fp32 output rounded: see opaque_f32)
+    const uint32_t lo = T::from_f32(opaque_f32(o[0] * inv)) | (T::from_f32(opaque_f32(o[1] * inv)) << 16);
+    const uint32_t hi = T::from_f32(opaque_f32(o[2] * inv)) | (T::from_f32(opaque_f32(o[3] * inv)) << 16);
     *reinterpret_cast<u32x2*>(static_cast<bits*>(a.out) + off) = u32x2{lo, hi};
   }
 }

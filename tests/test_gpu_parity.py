@@ -162,6 +162,37 @@ def test_config_parity(name):
     torch.cuda.empty_cache()
 
 
+
+@pytest.mark.timeout(600)
+def test_fp16_output_is_rounded_fp32():
+    """The fp16 output is the fp32 output rounded to nearest even, bit for
+    bit, on the fp16 MHA configuration's last decode (256 sequences, 40
+    heads: about a thousand items cut between waves and merged, where a
+    multiply fused into the fp16 conversion would round the exact product
+    once and land on the other side of some ties)."""
+    pa, runner = _pa()
+    w = W.build("c3_mha_f16_churn")
+    say("fp16 output")
+    dev = runner.run_script(w)
+    eng = dev.engine
+    dec = dev.decodes[-1]
+    q = dev.q_dev[dec.q_index][torch.tensor(dec.seqs, device="cuda")].contiguous()
+    tab = torch.from_numpy(np.ascontiguousarray(dec.tables)).to("cuda")
+    ctx = torch.from_numpy(np.asarray(dec.ctx, np.int32)).to("cuda")
+    n, hq, d = q.shape
+    out32 = torch.empty((n, hq, d), dtype=torch.float32, device="cuda")
+    out16 = torch.empty((n, hq, d), dtype=torch.float16, device="cuda")
+    for out in (out32, out16):
+        ws = eng.workspace(n, hq, int(max(dec.ctx)))
+        pa.pa_decode(out, q, eng.k_cache, eng.v_cache, tab, ctx, int(max(dec.ctx)), 1.0 / d ** 0.5,
+                     workspace=ws if ws.numel() else None)
+    torch.cuda.synchronize()
+    diff = int((out32.to(torch.float16).view(torch.int16) != out16.view(torch.int16)).sum())
+    say("fp16 output elements off the rounded fp32 one:", diff)
+    assert diff == 0
+    del dev
+    torch.cuda.empty_cache()
+
 @pytest.mark.timeout(600)
 def test_half_precision_output_is_rounded_fp32():
     """The bf16 output is the fp32 output rounded to nearest even (torch's

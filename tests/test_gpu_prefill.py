@@ -390,6 +390,58 @@ def test_prefill_context_split_matches_oracle(case):
     assert torch.equal(out_h, out.to(tdt))
 
 
+
+# every chunk within one query block of its (sequence, kv head) (4 CB (16 /
+# group) tokens with one column block): the launches whose tiles are each
+# read by one workgroup, with streaming loads, in one piece and split
+# (these batches have fewer than 512 workgroups):
+# dtype, head_dim, block size, q heads, kv heads, context lengths, chunk lengths
+ONE_BLOCK = {
+    "gqa8_bf16_bs32": ("bf16", 128, 32, 64, 8, [3000, 40, 8, 700], [8, 3, 8, 1]),
+    "gqa4_bf16_bs8": ("bf16", 128, 8, 32, 8, [2500, 16, 900], [16, 16, 7]),
+    "mha_f16_bs16": ("f16", 128, 16, 16, 16, [2100, 64, 333], [64, 50, 1]),
+    "gqa16_bf16_d64": ("bf16", 64, 16, 16, 1, [5000, 4, 77], [4, 4, 2]),
+}
+
+
+@pytest.mark.parametrize("case", list(ONE_BLOCK))
+def test_prefill_one_query_block_matches_oracle(case):
+    """Chunks that fit one query block, over block sizes 8, 16 and 32 and
+    groups 1, 4, 8 and 16: in one piece and split, within 2e-3 of the
+    oracle, and the 16-bit output is the fp32 one rounded."""
+    import paged_kv_cache_332_amd as pa
+    from paged_kv_cache_332_amd import runner
+    dtype, d, bs, hq, hkv, ctx, chunk = ONE_BLOCK[case]
+    g = hq // hkv
+    assert max(chunk) <= 4 * (16 // g) and pa.pa_prefill_column_blocks(hq, hkv, max(chunk), len(ctx)) == 1
+    say("prefill one query block", case)
+    w = W.tiny(num_seqs=len(ctx), dtype=dtype, seed=43, ctx=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+               block_size=bs)
+    dev = runner.run_script(w, decode=False)
+    eng = dev.engine
+    tab, _ = eng.bm.export(list(range(len(ctx))), eng.stride)
+    rng = np.random.default_rng([43, len(ctx)])
+    T = int(sum(chunk))
+    q = W.round_to_dtype(rng.standard_normal((T, hq, d), dtype=np.float32), dtype)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    tdt = runner.TORCH_DTYPE[dtype]
+    q_dev = torch.from_numpy(q).to("cuda").to(tdt)
+    scale = 1.0 / d ** 0.5
+    for split in (False, True):
+        out = _prefill_run(pa, eng, q_dev, tab, qs, ctx, chunk, scale, split)
+        out_h = _prefill_run(pa, eng, q_dev, tab, qs, ctx, chunk, scale, split, out_dtype=tdt)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got))
+        err = 0.0
+        for i, n in enumerate(ctx):
+            rows = w.row_of(i, np.arange(n))
+            ref = oracle.prefill_attention(q[qs[i]: qs[i + 1]], w.k_rows[rows], w.v_rows[rows], scale)
+            err = max(err, float(np.max(np.abs(got[qs[i]: qs[i + 1]] - ref))))
+        say(case, "split" if split else "one piece", "max abs error", err)
+        assert err <= 2e-3
+        assert torch.equal(out_h, out.to(tdt))
+
 # contexts, chunks, q heads, kv heads, head dim, block size, dtype
 SPLIT_CODED = {
     # chunks of at most 16 tokens: one query block per (sequence, kv head),
