@@ -237,10 +237,11 @@ __device__ __forceinline__ void dma16_once(const void* src, void* dst) {
 }
 
 // x as an opaque fp32 value: converting the result to 16 bits rounds this
-// fp32 value, as converting a stored fp32 output would (left visible, the
+// fp32 value, as converting a stored fp32 output would.  Left visible, the
 // multiply that produced x can be fused with the conversion into one
-// mixed-precision fma that rounds the exact product once, which lands on the
-// other side of a tie).  The empty asm emits no instruction.
+// mixed-precision fma that rounds the exact product once; where the fp32
+// product is a tie between two 16-bit values, that can pick the other one.
+// The empty asm emits no instruction.
 __device__ __forceinline__ float opaque_f32(float x) {
   asm volatile("" : "+v"(x));
   return x;
